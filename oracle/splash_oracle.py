@@ -1,0 +1,317 @@
+"""Plain fp64 definitions of block-sparse masked attention (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the library.
+
+Everything here is written from the pages' definitions, in float64, with no
+blocking, fusion or reordering beyond what a definition states:
+
+* Element mask: "hstu_ops.py" (RecML), ``pointwise_splash_attention`` builds
+  a CausalMask or FullMask, optionally ANDed with LocalMask((w, w), offset=0);
+  ``_apply_mask`` ANDs that with segment equality ``q_ids == kv_ids``.
+* Block metadata: "hstu_ops.py", ``_next_nonzero`` (a block runs when its
+  ``block_mask`` entry is > 0, needs no element mask when it is not 1, and the
+  kv block fetched at grid step j is ``data_next[h, i, j]``); page 3
+  "JAX 到 VLIW ... 复习笔记", section 21 (sparse indirection: a fully masked kv
+  block is skipped by pointing at the next valid block).
+* Softmax attention: page 3, section 12 (naive attention: scores, max, exp,
+  sum, divide, times V) and section 15 (Out = sum_t e^{a_t - M} v_t /
+  sum_t e^{a_t - M}).
+* Online softmax: page 3, sections 15.1-15.3 (m, L, O per kv block and the
+  correction alpha = e^{m_A - m_AB}).
+* Pointwise attention: "hstu_ops.py", ``_pointwise_splash_attention_fwd_kernel_impl``
+  (scores times scale, times logistic(scores), divided by the query sequence
+  length, masked entries set to 0, then times V), with the contributions of
+  all kv blocks summed (page 3, section 14: kv tiles add, they do not
+  concatenate).
+
+Where the pages are silent, the reading taken is stated at the function that
+relies on it.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# masks
+# ---------------------------------------------------------------------------
+
+
+def _allowed(qpos: np.ndarray, kpos: np.ndarray, head) -> np.ndarray:
+    """Boolean [len(qpos), len(kpos)] base mask of one head.
+
+    ``head = (causal, window_left, window_right)``. causal: key <= query
+    (top-left aligned). Window bounds of -1 are unbounded; otherwise a key is
+    allowed when q - window_left <= k <= q + window_right (the symmetric
+    LocalMask((w, w)) of "hstu_ops.py" is (w, w), read as inclusive bounds).
+    """
+    causal, wl, wr = (int(x) for x in head)
+    q = np.asarray(qpos, dtype=np.int64)[:, None]
+    k = np.asarray(kpos, dtype=np.int64)[None, :]
+    m = np.ones((q.shape[0], k.shape[1]), dtype=bool)
+    if causal:
+        m &= k <= q
+    if wl >= 0:
+        m &= k >= q - wl
+    if wr >= 0:
+        m &= k <= q + wr
+    return m
+
+
+def element_mask(q_len: int, kv_len: int, head, q_seg=None, kv_seg=None,
+                 rows=None) -> np.ndarray:
+    """Boolean element mask [len(rows), kv_len] of one (batch, head).
+
+    ``q_seg`` / ``kv_seg`` are the segment ids of this batch row ([q_len],
+    [kv_len]) or None; with ids, a pair is allowed only when they are equal
+    ("hstu_ops.py", ``_apply_mask``: the masks are combined with logical AND).
+    ``rows`` selects query positions (default: all).
+    """
+    qpos = np.arange(q_len) if rows is None else np.asarray(rows, dtype=np.int64)
+    kpos = np.arange(kv_len)
+    m = _allowed(qpos, kpos, head)
+    if (q_seg is None) != (kv_seg is None):
+        raise ValueError("q and kv segment ids must be given together or not at all")
+    if q_seg is not None:
+        qs = np.asarray(q_seg)[qpos]
+        ks = np.asarray(kv_seg)
+        m &= qs[:, None] == ks[None, :]
+    return m
+
+
+def padded_element_mask(q_len: int, kv_len: int, bq: int, bkv: int, head,
+                        q_seg=None, kv_seg=None, q_block=None) -> np.ndarray:
+    """Element mask over whole blocks: [nq*bq, nk*bkv], or [bq, nk*bkv] for the
+    single query block ``q_block``. Positions past the sequence ends are not
+    allowed (reading for lengths that are not a multiple of the block size)."""
+    nq = -(-q_len // bq)
+    nk = -(-kv_len // bkv)
+    blocks = range(nq) if q_block is None else [int(q_block)]
+    out = np.zeros((len(blocks) * bq, nk * bkv), dtype=bool)
+    for n, i in enumerate(blocks):
+        rows = np.arange(i * bq, min(q_len, (i + 1) * bq))
+        if rows.size:
+            out[n * bq:n * bq + rows.size, :kv_len] = element_mask(
+                q_len, kv_len, head, q_seg, kv_seg, rows=rows)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# block metadata
+# ---------------------------------------------------------------------------
+
+
+def next_nonempty(block_mask_row) -> np.ndarray:
+    """data_next for one row of block classes.
+
+    For each j: the smallest j' >= j whose block is not empty, or nk when
+    there is none (page 3, section 21: a fully masked kv block points at the
+    next valid block; the sentinel nk is the reading for "no next block").
+    """
+    row = np.asarray(block_mask_row)
+    nk = row.shape[0]
+    out = np.empty(nk, dtype=np.int32)
+    for j in range(nk):
+        later = [jj for jj in range(j, nk) if row[jj] != 0]
+        out[j] = later[0] if later else nk
+    return out
+
+
+def mask_info_row(q_len: int, kv_len: int, bq: int, bkv: int, head, i: int,
+                  q_seg=None, kv_seg=None):
+    """(block_mask [nk] int8, data_next [nk] int32) of query block ``i`` of one
+    (batch, head).
+
+    For block (i, j), c counts the allowed (q, k) pairs of the padded element
+    mask; block_mask is 0 when c == 0, 2 when c == bq*bkv (no element mask
+    needed) and 1 otherwise ("hstu_ops.py" ``_next_nonzero``: > 0 runs, != 1
+    skips the element mask; the value 2 for "full" is the reading taken).
+    """
+    nk = -(-kv_len // bkv)
+    m = padded_element_mask(q_len, kv_len, bq, bkv, head, q_seg, kv_seg, q_block=i)
+    counts = m.reshape(bq, nk, bkv).sum(axis=(0, 2), dtype=np.int64)
+    cls = np.where(counts == 0, 0, np.where(counts == bq * bkv, 2, 1)).astype(np.int8)
+    return cls, next_nonempty(cls)
+
+
+def mask_info(B: int, H: int, q_len: int, kv_len: int, bq: int, bkv: int, heads,
+              q_seg=None, kv_seg=None):
+    """Block metadata (block_mask int8, data_next int32), [Bm, Hm, nq, nk].
+
+    Hm = len(heads) (1 broadcasts over all H heads, "hstu_ops.py"
+    ``_next_nonzero`` forces the head index to 0 for one-head metadata);
+    Bm = B with segment ids, else 1. Each row is ``mask_info_row``.
+    """
+    heads = [tuple(h) for h in heads]
+    if len(heads) not in (1, H):
+        raise ValueError("need one head mask or one per head")
+    if (q_seg is None) != (kv_seg is None):
+        raise ValueError("q and kv segment ids must be given together or not at all")
+    Bm = B if q_seg is not None else 1
+    Hm = len(heads)
+    nq = -(-q_len // bq)
+    nk = -(-kv_len // bkv)
+    bmask = np.zeros((Bm, Hm, nq, nk), dtype=np.int8)
+    dnext = np.zeros((Bm, Hm, nq, nk), dtype=np.int32)
+    for b in range(Bm):
+        qs = None if q_seg is None else np.asarray(q_seg)[b]
+        ks = None if kv_seg is None else np.asarray(kv_seg)[b]
+        for hm in range(Hm):
+            for i in range(nq):
+                bmask[b, hm, i], dnext[b, hm, i] = mask_info_row(
+                    q_len, kv_len, bq, bkv, heads[hm], i, qs, ks)
+    return bmask, dnext
+
+
+def block_flops(block_mask: np.ndarray, B: int, H: int, bq: int, bkv: int, D: int) -> int:
+    """4*bq*bkv*D per non-empty block, summed over every (batch, head).
+
+    Metadata with one head or one batch row is broadcast (counted H or B
+    times)."""
+    Bm, Hm = block_mask.shape[:2]
+    per = np.count_nonzero(np.asarray(block_mask), axis=(2, 3))  # [Bm, Hm]
+    per = np.broadcast_to(per, (B if Bm == 1 else Bm, H if Hm == 1 else Hm))
+    return int(per.sum()) * 4 * bq * bkv * D
+
+
+def element_flops(B: int, H: int, q_len: int, kv_len: int, D: int, heads,
+                  q_seg=None, kv_seg=None) -> int:
+    """4*D per allowed (q, k) pair, summed over every (batch, head)."""
+    heads = [tuple(h) for h in heads]
+    total = 0
+    for b in range(B):
+        for h in range(H):
+            hd = heads[0] if len(heads) == 1 else heads[h]
+            qs = None if q_seg is None else np.asarray(q_seg)[b]
+            ks = None if kv_seg is None else np.asarray(kv_seg)[b]
+            total += int(element_mask(q_len, kv_len, hd, qs, ks).sum())
+    return 4 * D * total
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+
+def softmax_attention_rows(q_rows, k, v, scale: float, mask_rows) -> np.ndarray:
+    """Masked softmax attention of some query rows, fp64.
+
+    q_rows [R, D], k [Skv, D], v [Skv, Dv], mask_rows bool [R, Skv].
+    Page 3, section 12 (naive attention) and section 15: scores = scale*q.k,
+    masked scores are excluded (set to -inf, weight exactly 0), M = row max,
+    Out = sum e^{a-M} v / sum e^{a-M}. A row with no allowed key returns 0
+    (reading: nothing to average).
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    s = (q_rows @ k.T) * float(scale)
+    s = np.where(mask_rows, s, -np.inf)
+    out = np.zeros((q_rows.shape[0], v.shape[1]), dtype=np.float64)
+    has = np.asarray(mask_rows).any(axis=1)
+    if has.any():
+        sh = s[has]
+        m = sh.max(axis=1, keepdims=True)
+        w = np.exp(sh - m)
+        out[has] = (w @ v) / w.sum(axis=1, keepdims=True)
+    return out
+
+
+def pointwise_attention_rows(q_rows, k, v, scale: float, mask_rows, seq_len: int) -> np.ndarray:
+    """Pointwise (SiLU) attention of some query rows, fp64.
+
+    "hstu_ops.py" ``_pointwise_splash_attention_fwd_kernel_impl``:
+    x = scale*q.k; p = x * logistic(x) / seq_len with seq_len the query
+    sequence length; masked entries -> 0; out = sum_k p v_k, summed over all kv
+    blocks (the printed per-slice overwrite of the output is read as an
+    accumulation, as the backward on the same page and page 3 section 14
+    imply).
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    x = (q_rows @ k.T) * float(scale)
+    with np.errstate(over="ignore"):
+        p = x / (1.0 + np.exp(-x)) / float(seq_len)
+    p = np.where(mask_rows, p, 0.0)
+    return p @ v
+
+
+def online_softmax_rows(q_rows, k, v, scale: float, mask_rows, block_kv: int) -> np.ndarray:
+    """The same result as ``softmax_attention_rows`` by the blockwise recurrence.
+
+    Page 3, sections 15.1-15.3: for each kv block B after blocks A,
+    m_AB = max(m_A, m_B), alpha = e^{m_A - m_AB}, L_B = sum e^{a - m_AB},
+    O_B = sum e^{a - m_AB} v, L_AB = alpha L_A + L_B, O_AB = alpha O_A + O_B;
+    finally Out = O / L. Excluded entries carry no weight; a row that has
+    seen no allowed key yet keeps m = -inf, L = 0, O = 0.
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    mask_rows = np.asarray(mask_rows)
+    R, Skv = mask_rows.shape
+    out = np.zeros((R, v.shape[1]), dtype=np.float64)
+    for r in range(R):
+        m_a = -np.inf
+        l_a = 0.0
+        o_a = np.zeros(v.shape[1], dtype=np.float64)
+        for j0 in range(0, Skv, block_kv):
+            sel = np.nonzero(mask_rows[r, j0:j0 + block_kv])[0] + j0
+            if sel.size == 0:
+                continue
+            a = (k[sel] @ q_rows[r]) * float(scale)
+            m_b = a.max()
+            m_ab = max(m_a, m_b)
+            alpha = np.exp(m_a - m_ab)          # 0 when m_a = -inf
+            e = np.exp(a - m_ab)
+            l_a = alpha * l_a + e.sum()
+            o_a = alpha * o_a + e @ v[sel]
+            m_a = m_ab
+        if l_a > 0:
+            out[r] = o_a / l_a
+    return out
+
+
+def _heads_list(heads, H):
+    heads = [tuple(h) for h in heads]
+    if len(heads) not in (1, H):
+        raise ValueError("need one head mask or one per head")
+    return heads
+
+
+def _attention(kind: str, q, k, v, scale, heads, q_seg, kv_seg, row_chunk: int):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, Sq, _ = q.shape
+    Skv = k.shape[2]
+    heads = _heads_list(heads, H)
+    out = np.zeros((B, H, Sq, v.shape[3]), dtype=np.float64)
+    for b in range(B):
+        qs = None if q_seg is None else np.asarray(q_seg)[b]
+        ks = None if kv_seg is None else np.asarray(kv_seg)[b]
+        for h in range(H):
+            hd = heads[0] if len(heads) == 1 else heads[h]
+            for r0 in range(0, Sq, row_chunk):
+                rows = np.arange(r0, min(Sq, r0 + row_chunk))
+                m = element_mask(Sq, Skv, hd, qs, ks, rows=rows)
+                if kind == "softmax":
+                    out[b, h, rows] = softmax_attention_rows(q[b, h, rows], k[b, h], v[b, h], scale, m)
+                else:
+                    out[b, h, rows] = pointwise_attention_rows(q[b, h, rows], k[b, h], v[b, h], scale, m, Sq)
+    return out
+
+
+def softmax_attention(q, k, v, scale: float, heads, q_seg=None, kv_seg=None,
+                      row_chunk: int = 512) -> np.ndarray:
+    """Masked softmax attention [B, H, Sq, Dv] (fp64); rows are independent, so
+    the full-score definition is evaluated ``row_chunk`` rows at a time."""
+    return _attention("softmax", q, k, v, scale, heads, q_seg, kv_seg, row_chunk)
+
+
+def pointwise_attention(q, k, v, scale: float, heads, q_seg=None, kv_seg=None,
+                        row_chunk: int = 512) -> np.ndarray:
+    """Pointwise SiLU attention [B, H, Sq, Dv] (fp64), divided by Sq."""
+    return _attention("pointwise", q, k, v, scale, heads, q_seg, kv_seg, row_chunk)

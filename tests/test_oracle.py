@@ -1,0 +1,411 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Nothing here re-types the oracle's own formulas: every check is a printed
+value, a closed form, a special case reducing to a library routine, an
+independent brute force, or an invariant. Runs on the CPU.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_masked_splash_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+CAUSAL, FULL = (1, -1, -1), (0, -1, -1)
+
+
+def _f64(t):
+    return t.to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------
+# metadata
+# ---------------------------------------------------------------------------
+
+
+def test_page3_worked_data_next_example():
+    """Page 3, section 21: valid = 1 0 0 1 0 1 -> data_next[1] = data_next[2] = 3."""
+    with open(os.path.join(GOLDEN, "page3_sec21_data_next.json")) as f:
+        g = json.load(f)
+    dn = oracle.next_nonempty(g["valid"])
+    for j, want in g["printed_data_next"].items():
+        assert dn[int(j)] == want
+    # a valid block points at itself; past the last valid block there is nothing
+    for j, v in enumerate(g["valid"]):
+        if v:
+            assert dn[j] == j
+    assert list(oracle.next_nonempty([0, 0, 0])) == [3, 3, 3]
+    assert list(oracle.next_nonempty([])) == []
+
+
+@pytest.mark.parametrize("S,b", [(256, 64), (1024, 128), (512, 64)])
+def test_causal_metadata_closed_form(S, b):
+    bm, dn = oracle.mask_info(1, 1, S, S, b, b, [CAUSAL])
+    n = S // b
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    want = np.where(j < i, 2, np.where(j == i, 1, 0))
+    np.testing.assert_array_equal(bm[0, 0], want)
+    np.testing.assert_array_equal(dn[0, 0], np.where(j <= i, j, n))
+    assert np.count_nonzero(bm) == n * (n + 1) // 2
+
+
+def test_workload_block_counts_and_flops():
+    """Non-empty block counts n(n+1)/2 of the causal workloads and the FLOP
+    count of the S=8192 workload (4*128*128*128 per block, 64 (b, h))."""
+    for name, want in [("c1", 10), ("c2", 136), ("c5", 528)]:
+        w = wl.WORKLOADS[name]
+        bm, _ = oracle.mask_info(1, 1, w.S, w.S, w.block_q, w.block_kv, w.head_masks)
+        assert np.count_nonzero(bm) == want
+    n = 64
+    bm = np.tril(np.ones((n, n), dtype=np.int8))[None, None]
+    assert oracle.block_flops(bm, 2, 32, 128, 128, 128) == 133120 * 4 * 128 ** 3
+    assert abs(oracle.block_flops(bm, 2, 32, 128, 128, 128) - 1.1167e12) < 1e8
+
+
+def test_local_window_metadata_closed_form():
+    """Causal AND window 1024 at 128x128 blocks: rows i >= 8 have partial
+    blocks {i-8, i} and full blocks i-7..i-1; rows i < 8 have i+1 blocks. At
+    nq = 256 that is 36 + 9*248 = 2268 non-empty blocks per head."""
+    S, b, w = 4096, 128, 1024
+    bm, dn = oracle.mask_info(1, 1, S, S, b, b, [wl.local_causal(w)])
+    n = S // b
+    for i in range(n):
+        row = bm[0, 0, i]
+        if i >= 8:
+            assert row[i - 8] == 1 and row[i] == 1
+            assert (row[i - 7:i] == 2).all()
+            assert (row[:i - 8] == 0).all() and (row[i + 1:] == 0).all()
+            assert dn[0, 0, i, 0] == i - 8
+        else:
+            assert row[i] == 1 and (row[:i] == 2).all() and (row[i + 1:] == 0).all()
+    assert np.count_nonzero(bm) == 36 + 9 * (n - 8)
+    assert 36 + 9 * (256 - 8) == 2268
+
+
+def test_element_counts_closed_form():
+    """Allowed pairs: causal S(S+1)/2; causal window w: sum_q min(q, w) + 1.
+    A window off by one (k > q - w, or k >= q - w + 1) fails the second."""
+    S, w = 300, 37
+    assert oracle.element_mask(S, S, CAUSAL).sum() == S * (S + 1) // 2
+    assert oracle.element_mask(S, S, wl.local_causal(w)).sum() == sum(min(q, w) + 1 for q in range(S))
+    assert oracle.element_mask(S, S, FULL).sum() == S * S
+    # symmetric window without causal: |q - k| <= w
+    m = oracle.element_mask(S, S, (0, w, w))
+    assert m.sum() == sum(min(q, w) + 1 + min(S - 1 - q, w) for q in range(S))
+
+
+def test_head_broadcast_and_per_head_metadata():
+    heads = [CAUSAL, wl.local_causal(64), FULL]
+    bm, dn = oracle.mask_info(1, 3, 512, 512, 64, 64, heads)
+    for h, hd in enumerate(heads):
+        one, one_dn = oracle.mask_info(1, 1, 512, 512, 64, 64, [hd])
+        np.testing.assert_array_equal(bm[:, h], one[:, 0])
+        np.testing.assert_array_equal(dn[:, h], one_dn[:, 0])
+    assert (bm[0, 2] == 2).all()  # FULL: every block full
+
+
+def test_aligned_documents_metadata():
+    """Documents exactly one block long under causal AND segment: only the
+    diagonal blocks run and each is partial; two blocks long: the block below
+    the diagonal inside a document is full."""
+    b, n = 64, 6
+    S = b * n
+    ids = np.repeat(np.arange(n, dtype=np.int32), b)[None]
+    bm, dn = oracle.mask_info(1, 1, S, S, b, b, [CAUSAL], ids, ids)
+    np.testing.assert_array_equal(bm[0, 0], np.eye(n, dtype=np.int8))
+    np.testing.assert_array_equal(dn[0, 0], np.where(np.arange(n)[None] <= np.arange(n)[:, None],
+                                                     np.arange(n)[:, None], n))
+    ids2 = np.repeat(np.arange(n // 2, dtype=np.int32), 2 * b)[None]
+    bm2, _ = oracle.mask_info(1, 1, S, S, b, b, [CAUSAL], ids2, ids2)
+    want = np.eye(n, dtype=np.int8)
+    for d in range(n // 2):
+        want[2 * d + 1, 2 * d] = 2
+    np.testing.assert_array_equal(bm2[0, 0], want)
+
+
+def test_ragged_metadata():
+    """Blocks that extend past the sequence end are never full."""
+    bm, dn = oracle.mask_info(1, 1, 200, 200, 64, 64, [FULL])
+    assert bm.shape == (1, 1, 4, 4)
+    assert (bm[0, 0, :3, :3] == 2).all()
+    assert (bm[0, 0, 3, :] == 1).all() and (bm[0, 0, :, 3] == 1).all()
+    bm, dn = oracle.mask_info(1, 1, 0, 0, 64, 64, [FULL])
+    assert bm.shape == (1, 1, 0, 0)
+    bm, dn = oracle.mask_info(1, 1, 100, 0, 64, 64, [FULL])
+    assert bm.shape == (1, 1, 2, 0)
+
+
+def test_metadata_brute_force_small():
+    """Block classes by scalar loops over every (q, k) pair, random windows,
+    segments and ragged lengths."""
+    rng = np.random.default_rng(7)
+    for trial in range(6):
+        Sq, Skv = int(rng.integers(1, 70)), int(rng.integers(1, 70))
+        bq, bkv = int(rng.choice([4, 8, 16])), int(rng.choice([4, 8, 16]))
+        head = (int(rng.integers(0, 2)), int(rng.integers(-1, 12)), int(rng.integers(-1, 12)))
+        qs = rng.integers(0, 3, size=(1, Sq)).astype(np.int32)
+        ks = rng.integers(0, 3, size=(1, Skv)).astype(np.int32)
+        bm, dn = oracle.mask_info(1, 1, Sq, Skv, bq, bkv, [head], qs, ks)
+        nq, nk = -(-Sq // bq), -(-Skv // bkv)
+        for i in range(nq):
+            for j in range(nk):
+                c = 0
+                for q in range(i * bq, (i + 1) * bq):
+                    for k in range(j * bkv, (j + 1) * bkv):
+                        if q >= Sq or k >= Skv:
+                            continue
+                        ok = (not head[0] or k <= q) and (head[1] < 0 or k >= q - head[1]) \
+                            and (head[2] < 0 or k <= q + head[2]) and qs[0, q] == ks[0, k]
+                        c += bool(ok)
+                want = 0 if c == 0 else (2 if c == bq * bkv else 1)
+                assert bm[0, 0, i, j] == want
+            for j in range(nk):
+                nxt = next((jj for jj in range(j, nk) if bm[0, 0, i, jj]), nk)
+                assert dn[0, 0, i, j] == nxt
+
+
+# ---------------------------------------------------------------------------
+# softmax attention
+# ---------------------------------------------------------------------------
+
+
+def _case(seed, B, H, Sq, Skv, D, sigma=1.0, segments=None):
+    c = wl.random_case(seed, B, H, Sq, Skv, D, "f32", sigma, segments)
+    q, k, v = (_f64(c[n]) for n in ("q", "k", "v"))
+    qs = None if c["q_segment_ids"] is None else c["q_segment_ids"].numpy()
+    ks = None if c["kv_segment_ids"] is None else c["kv_segment_ids"].numpy()
+    return q, k, v, qs, ks
+
+
+@pytest.mark.parametrize("head", [FULL, CAUSAL, (1, 9, 9), (0, 5, 3)])
+@pytest.mark.parametrize("segments", [None, "docs"])
+def test_softmax_matches_torch_sdpa_fp64(head, segments):
+    """torch's scaled_dot_product_attention in float64 with a boolean mask is a
+    library routine of the same definition (rows with no allowed key are
+    avoided here: the library returns NaN for them)."""
+    B, H, S, D = 2, 3, 97, 32
+    q, k, v, qs, ks = _case(11, B, H, S, S, D, segments=segments)
+    scale = 1 / math.sqrt(D)
+    got = oracle.softmax_attention(q, k, v, scale, [head], qs, ks, row_chunk=40)
+    for b in range(B):
+        m = oracle.element_mask(S, S, head, None if qs is None else qs[b], None if ks is None else ks[b])
+        assert m.any(axis=1).all()
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[b]), torch.from_numpy(k[b]), torch.from_numpy(v[b]),
+            attn_mask=torch.from_numpy(m), scale=scale).numpy()
+        np.testing.assert_allclose(got[b], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_softmax_closed_forms():
+    S, D = 50, 16
+    q, k, v, _, _ = _case(3, 1, 1, S, S, D)
+    q, k, v = q[0, 0], k[0, 0], v[0, 0]
+    mask = oracle.element_mask(S, S, CAUSAL)
+    # constant V returns that row
+    c = np.linspace(-1, 1, D)
+    out = oracle.softmax_attention_rows(q, k, np.tile(c, (S, 1)), 0.3, mask)
+    np.testing.assert_allclose(out, np.tile(c, (S, 1)), rtol=0, atol=1e-14)
+    # identical keys: the mean of the allowed V rows
+    kk = np.tile(k[0], (S, 1))
+    out = oracle.softmax_attention_rows(q, kk, v, 0.3, mask)
+    want = np.cumsum(v, axis=0) / np.arange(1, S + 1)[:, None]
+    np.testing.assert_allclose(out, want, rtol=0, atol=1e-13)
+    # scale 0: uniform average of the allowed rows
+    out = oracle.softmax_attention_rows(q, k, v, 0.0, mask)
+    np.testing.assert_allclose(out, want, rtol=0, atol=1e-13)
+    # causal row 0 returns v_0 exactly (weight e^0 = 1 over a sum of 1)
+    out = oracle.softmax_attention_rows(q, k, v, 0.7, mask)
+    assert np.array_equal(out[0], v[0])
+    # local window, identical keys: mean over [q - w, q]
+    w = 4
+    m = oracle.element_mask(S, S, wl.local_causal(w))
+    out = oracle.softmax_attention_rows(q, kk, v, 0.3, m)
+    want = np.stack([v[max(0, t - w):t + 1].mean(axis=0) for t in range(S)])
+    np.testing.assert_allclose(out, want, rtol=0, atol=1e-13)
+    # a row with no allowed key returns 0
+    m = np.zeros((S, S), dtype=bool)
+    assert (oracle.softmax_attention_rows(q, k, v, 0.3, m) == 0).all()
+
+
+def test_first_token_of_each_document_returns_its_own_value():
+    B, H, S, D = 2, 2, 300, 16
+    q, k, v, qs, ks = _case(5, B, H, S, S, D, segments="docs")
+    out = oracle.softmax_attention(q, k, v, 0.25, [CAUSAL], qs, ks)
+    for b in range(B):
+        starts = [0] + [t for t in range(1, S) if qs[b, t] != qs[b, t - 1]]
+        assert len(starts) > 3
+        for t in starts:
+            assert np.array_equal(out[b, :, t], v[b, :, t])
+
+
+def test_softmax_brute_force_scalar_loops():
+    """Pure-Python scalar loops with math.exp, S <= 16, random masks."""
+    rng = np.random.default_rng(12)
+    for trial in range(5):
+        Sq, Skv, D = int(rng.integers(1, 17)), int(rng.integers(1, 17)), int(rng.integers(1, 9))
+        head = (int(rng.integers(0, 2)), int(rng.integers(-1, 6)), int(rng.integers(-1, 6)))
+        q, k, v, qs, ks = _case(100 + trial, 1, 1, Sq, Skv, D, segments="random")
+        q, k, v, qs, ks = q[0, 0], k[0, 0], v[0, 0], qs[0], ks[0]
+        scale = float(rng.uniform(0.1, 1.0))
+        got = oracle.softmax_attention_rows(q, k, v, scale, oracle.element_mask(Sq, Skv, head, qs, ks))
+        for t in range(Sq):
+            allowed = [j for j in range(Skv)
+                       if (not head[0] or j <= t) and (head[1] < 0 or j >= t - head[1])
+                       and (head[2] < 0 or j <= t + head[2]) and qs[t] == ks[j]]
+            want = [0.0] * D
+            if allowed:
+                sc = {j: scale * sum(q[t, d] * k[j, d] for d in range(D)) for j in allowed}
+                mx = max(sc.values())
+                den = sum(math.exp(sc[j] - mx) for j in allowed)
+                want = [sum(math.exp(sc[j] - mx) * v[j, d] for j in allowed) / den for d in range(D)]
+            np.testing.assert_allclose(got[t], want, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("block_kv", [1, 3, 7, 16, 64])
+def test_online_recurrence_equals_definition(block_kv):
+    """Page 3, section 15: the blockwise m, L, O recurrence is exact; the
+    result does not depend on the kv block size (page 3, section 14)."""
+    S, D = 64, 16
+    q, k, v, qs, ks = _case(9, 1, 1, S, S, D, segments="docs")
+    for head in (CAUSAL, (1, 10, 10), FULL):
+        m = oracle.element_mask(S, S, head, qs[0], ks[0])
+        a = oracle.softmax_attention_rows(q[0, 0], k[0, 0], v[0, 0], 0.4, m)
+        b = oracle.online_softmax_rows(q[0, 0], k[0, 0], v[0, 0], 0.4, m, block_kv)
+        np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-13)
+
+
+def test_softmax_large_scores_stay_finite():
+    """q x 30 gives |scores| ~ 1e3; the max-subtracted form stays finite and
+    agrees with the library routine."""
+    S, D = 40, 64
+    q, k, v, _, _ = _case(4, 1, 1, S, S, D)
+    q = q * 30
+    m = oracle.element_mask(S, S, CAUSAL)
+    out = oracle.softmax_attention_rows(q[0, 0], k[0, 0], v[0, 0], 0.125, m)
+    assert np.isfinite(out).all()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q[0, 0]), torch.from_numpy(k[0, 0]), torch.from_numpy(v[0, 0]),
+        attn_mask=torch.from_numpy(m), scale=0.125).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    b = oracle.online_softmax_rows(q[0, 0], k[0, 0], v[0, 0], 0.125, m, 8)
+    np.testing.assert_allclose(b, out, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# pointwise attention
+# ---------------------------------------------------------------------------
+
+
+def test_pointwise_closed_forms():
+    S, D = 48, 8
+    q, k, v, _, _ = _case(21, 1, 1, S, S, D, sigma=0.5)
+    q, k, v = q[0, 0], k[0, 0], v[0, 0]
+    mask = oracle.element_mask(S, S, CAUSAL)
+    scale = 1 / math.sqrt(D)
+    # q = 0: SiLU(0) = 0
+    assert (oracle.pointwise_attention_rows(np.zeros_like(q), k, v, scale, mask, S) == 0).all()
+    # causal row 0: silu(x) v_0 / S with x = scale <q0, k0>
+    out = oracle.pointwise_attention_rows(q, k, v, scale, mask, S)
+    x = scale * float(np.dot(q[0], k[0]))
+    np.testing.assert_allclose(out[0], x / (1 + math.exp(-x)) * v[0] / S, rtol=1e-14, atol=0)
+    # identical keys, constant v = c: |A_q| silu(x_q) c / S
+    kk = np.tile(k[3], (S, 1))
+    c = np.linspace(-2, 2, D)
+    out = oracle.pointwise_attention_rows(q, kk, np.tile(c, (S, 1)), scale, mask, S)
+    for t in range(S):
+        x = scale * float(np.dot(q[t], k[3]))
+        np.testing.assert_allclose(out[t], (t + 1) * x / (1 + math.exp(-x)) * c / S, rtol=1e-12, atol=1e-15)
+    # linear in V
+    v2 = np.random.default_rng(1).standard_normal(v.shape)
+    a = oracle.pointwise_attention_rows(q, k, 2 * v - 3 * v2, scale, mask, S)
+    b = 2 * oracle.pointwise_attention_rows(q, k, v, scale, mask, S) \
+        - 3 * oracle.pointwise_attention_rows(q, k, v2, scale, mask, S)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+def test_pointwise_brute_force_scalar_loops():
+    rng = np.random.default_rng(31)
+    for trial in range(5):
+        Sq, Skv, D = int(rng.integers(1, 17)), int(rng.integers(1, 17)), int(rng.integers(1, 9))
+        head = (int(rng.integers(0, 2)), int(rng.integers(-1, 6)), int(rng.integers(-1, 6)))
+        q, k, v, qs, ks = _case(200 + trial, 1, 1, Sq, Skv, D, sigma=0.5, segments="random")
+        q, k, v, qs, ks = q[0, 0], k[0, 0], v[0, 0], qs[0], ks[0]
+        scale = float(rng.uniform(0.1, 1.0))
+        got = oracle.pointwise_attention_rows(q, k, v, scale, oracle.element_mask(Sq, Skv, head, qs, ks), Sq)
+        for t in range(Sq):
+            want = [0.0] * D
+            for j in range(Skv):
+                ok = (not head[0] or j <= t) and (head[1] < 0 or j >= t - head[1]) \
+                    and (head[2] < 0 or j <= t + head[2]) and qs[t] == ks[j]
+                if not ok:
+                    continue
+                x = scale * sum(q[t, d] * k[j, d] for d in range(D))
+                p = x / (1.0 + math.exp(-x)) / Sq
+                for d in range(D):
+                    want[d] += p * v[j, d]
+            np.testing.assert_allclose(got[t], want, rtol=1e-12, atol=1e-15)
+
+
+def test_full_attention_wrappers_match_rows():
+    B, H, S, D = 2, 2, 70, 16
+    q, k, v, qs, ks = _case(41, B, H, S, S, D, segments="docs")
+    heads = [CAUSAL, wl.local_causal(9)]
+    a = oracle.softmax_attention(q, k, v, 0.3, heads, qs, ks, row_chunk=16)
+    p = oracle.pointwise_attention(q, k, v, 0.3, heads, qs, ks, row_chunk=16)
+    for b in range(B):
+        for h in range(H):
+            m = oracle.element_mask(S, S, heads[h], qs[b], ks[b])
+            np.testing.assert_array_equal(a[b, h], oracle.softmax_attention_rows(q[b, h], k[b, h], v[b, h], 0.3, m))
+            np.testing.assert_array_equal(p[b, h], oracle.pointwise_attention_rows(q[b, h], k[b, h], v[b, h], 0.3, m, S))
+
+
+# ---------------------------------------------------------------------------
+# the pins catch planted mistakes
+# ---------------------------------------------------------------------------
+
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Plant plausible errors in a copy of the oracle's pieces and check that
+    the closed forms above reject them."""
+    import oracle.splash_oracle as so
+
+    real_allowed = so._allowed
+
+    def off_by_one(qpos, kpos, head):   # window k > q - w instead of k >= q - w
+        m = real_allowed(qpos, kpos, head)
+        if head[1] >= 0:
+            q = np.asarray(qpos)[:, None]
+            k = np.asarray(kpos)[None, :]
+            m &= k != q - head[1]
+        return m
+
+    monkeypatch.setattr(so, "_allowed", off_by_one)
+    S, w = 300, 37
+    assert so.element_mask(S, S, (1, w, w)).sum() != sum(min(q, w) + 1 for q in range(S))
+    monkeypatch.setattr(so, "_allowed", real_allowed)
+
+    # a recurrence without the correction factor alpha disagrees with the definition
+    S, D = 64, 16
+    q, k, v, _, _ = _case(9, 1, 1, S, S, D)
+    m = so.element_mask(S, S, CAUSAL)
+    a = so.softmax_attention_rows(q[0, 0], k[0, 0], v[0, 0], 0.4, m)
+    real_exp = np.exp
+    calls = {"n": 0}
+
+    def exp_without_alpha(x):
+        calls["n"] += 1
+        if np.ndim(x) == 0:          # the scalar alpha = e^{m_A - m_AB}
+            return 1.0
+        return real_exp(x)
+
+    monkeypatch.setattr(so.np, "exp", exp_without_alpha)
+    b = so.online_softmax_rows(q[0, 0], k[0, 0], v[0, 0], 0.4, m, 8)
+    monkeypatch.setattr(so.np, "exp", real_exp)
+    assert calls["n"] > 0
+    assert not np.allclose(a, b, rtol=1e-6, atol=1e-6)
