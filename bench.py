@@ -1,0 +1,203 @@
+"""Benchmark of the block-sparse masked attention forward on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic inputs that
+are already resident in HBM: the block metadata build followed by the
+attention forward. The default workload is causal MHA, B=2, H=32, S=8192,
+D=128, bf16, 128x128 blocks. Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload c3h] [--no-cpu-baseline]
+
+Throughput counts 4*bq*bkv*D FLOPs per non-empty (b, h, i, j) block (the
+QKᵀ and P·V products of every block that is not skipped).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak
+METRIC = "splash fwd TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, causal S=8192"
+KERNEL_SOURCES = ["splash_fwd_bf16.hip", "splash_fwd_f32.hip", "internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_masked_splash_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"splash_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, gen, budget_s: float = 12.0):
+    """The oracle, as it is, on a bounded sample of the same workload: whole
+    query blocks of several (b, h), timed on the host cores."""
+    import numpy as np
+    import torch
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(12345)
+    S, bq, bkv, D = w.S, w.block_q, w.block_kv, w.D
+    nq = -(-S // bq)
+    qs = gen["q_segment_ids"]
+    qs = None if qs is None else qs.numpy()
+    flops = 0
+    done = 0
+    t0 = time.perf_counter()
+    cache = {}
+    while time.perf_counter() - t0 < budget_s or done < 4:
+        b, h, i = int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(nq))
+        if (b, h) not in cache:
+            cache.clear()
+            cache[(b, h)] = (gen["k"][b, h].to(torch.float64).numpy(), gen["v"][b, h].to(torch.float64).numpy())
+        k64, v64 = cache[(b, h)]
+        rows = np.arange(i * bq, min(S, (i + 1) * bq))
+        head = w.head_masks[0] if len(w.head_masks) == 1 else w.head_masks[h]
+        m = oracle.element_mask(S, S, head, None if qs is None else qs[b], None if qs is None else qs[b], rows=rows)
+        q64 = gen["q"][b, h, rows[0]:rows[-1] + 1].to(torch.float64).numpy()
+        if w.pointwise:
+            oracle.pointwise_attention_rows(q64, k64, v64, w.scale, m, S)
+        else:
+            oracle.softmax_attention_rows(q64, k64, v64, w.scale, m)
+        cls, _ = oracle.mask_info_row(S, S, bq, bkv, head, i, None if qs is None else qs[b],
+                                      None if qs is None else qs[b])
+        flops += int(np.count_nonzero(cls)) * 4 * bq * bkv * D
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} query blocks of {bq} rows on random (b, h), fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3h")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run N copies of a 1 GiB buffer (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the work shards by (batch, head) with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_masked_splash_amd as sp
+    from block_sparse_masked_splash_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    gen = wl.generate(w)
+    q, k, v = (gen[n].to(dev) for n in ("q", "k", "v"))
+    seg = None if gen["q_segment_ids"] is None else gen["q_segment_ids"].to(dev)
+    fwd = sp.pointwise_fwd if w.pointwise else sp.splash_fwd
+    out = torch.empty_like(q)
+
+    info = sp.mask_info_build(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg, device=dev)
+    torch.cuda.synchronize()
+    nonempty = (info.block_mask != 0).sum(dim=(2, 3)).to(torch.int64)  # [Bm, Hm]
+    Bm, Hm = info.block_mask.shape[:2]
+    per_bh = nonempty.expand(w.B if Bm == 1 else Bm, w.H if Hm == 1 else Hm)
+    blocks = int(per_bh.sum().item())
+    flops = blocks * 4 * w.block_q * w.block_kv * w.D
+
+    def step():
+        sp.mask_info_build(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg, device=dev, out=info)
+        fwd(q, k, v, info, scale=w.scale, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        sp.mask_info_build(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg, device=dev, out=info)
+        ev[s][0].record(stream)
+        fwd(q, k, v, info, scale=w.scale, out=out)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(args.copy_calibration):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    in_f32 = w.dtype == "f32"
+    peak = PEAK_F32_TFLOPS if in_f32 else PEAK_BF16_TFLOPS
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    desc = {
+        "c1": "tiny causal attention B=1 H=1 S=256 D=64 fp32, block 64x64",
+        "c2": "causal MHA B=4 H=16 S=2048 D=128 bf16, block 128x128",
+        "c3h": "causal MHA B=2 H=32 S=8192 D=128 bf16, block 128x128",
+        "c3": "causal AND same-document MHA B=2 H=32 S=8192 D=128 bf16, documents 256-2048, block 128x128",
+        "c4": "mixed heads B=1 H=16 S=32768 D=128 bf16: 8 causal + 8 causal window 1024, block 128x128",
+        "c5": "pointwise SiLU causal B=8 H=8 S=4096 D=64 bf16, N(0,0.5^2), block 128x128",
+    }[w.name]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if in_f32 else "bf16",
+        "data": "synthetic (seeded N(0, sigma^2) q, k, v)",
+        "config": {"workload": f"{w.name}: {desc}", "batch": w.B, "heads": w.H, "seq_len": w.S,
+                   "head_dim": w.D, "block_q": w.block_q, "block_kv": w.block_kv,
+                   "nonempty_blocks": blocks, "flops_per_step": flops,
+                   "step": "mask_info_build + " + ("pointwise_fwd" if w.pointwise else "splash_fwd")},
+        "fwd_kernel_ms": round(kernel_ms, 5),
+        "pct_of_peak": round(100 * value / peak, 2),
+        "roofline": {"bound": "mfma" if not in_f32 else "alu", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_for(w.name), "kernel_source_sha256_16": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, gen)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,16 @@
-"""Block-sparse masked ("Splash") attention forward for AMD MI355X (gfx950)."""
+"""Block-sparse masked ("Splash") attention forward for AMD MI355X (gfx950).
+
+The computation lives in libsplash.so (hand-written HIP kernels behind a C
+ABI, declared in include/splash.h); ``binding`` marshals torch tensors into
+it. ``workloads`` holds the seeded synthetic inputs.
+"""
+
+from .binding import (  # noqa: F401
+    MaskInfo,
+    SplashError,
+    load_library,
+    mask_info_build,
+    pointwise_fwd,
+    splash_fwd,
+)
+from .workloads import CAUSAL, FULL, local_causal  # noqa: F401

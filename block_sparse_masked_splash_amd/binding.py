@@ -1,0 +1,268 @@
+"""ctypes binding of libsplash.so: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this module
+turns torch tensors into device pointers, strides and the caller's stream,
+and turns status codes into exceptions. It has no fallback: if the library
+is missing or a call fails, it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsplash.so")
+
+SPLASH_OK = 0
+SPLASH_ERR_INVALID_ARGUMENT = 1
+SPLASH_ERR_UNSUPPORTED = 2
+SPLASH_ERR_METADATA_MISMATCH = 3
+SPLASH_ERR_HIP = 4
+SPLASH_F32 = 0
+SPLASH_BF16 = 1
+MAX_MASK_HEADS = 256
+
+# Exported symbols, as declared in include/splash.h.
+SYMBOLS = (
+    "splash_mask_info_entries",
+    "splash_mask_info_build",
+    "splash_fwd",
+    "splash_pointwise_fwd",
+    "splash_status_string",
+    "splash_last_error",
+    "splash_abi_version",
+)
+
+
+class SplashError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class HeadMaskC(ctypes.Structure):
+    _fields_ = [("causal", ctypes.c_int32), ("window_left", ctypes.c_int32),
+                ("window_right", ctypes.c_int32)]
+
+
+class MaskDescC(ctypes.Structure):
+    _fields_ = [("num_mask_heads", ctypes.c_int32), ("heads", ctypes.POINTER(HeadMaskC)),
+                ("q_segment_ids", ctypes.c_void_p), ("kv_segment_ids", ctypes.c_void_p)]
+
+
+class MaskInfoC(ctypes.Structure):
+    _fields_ = [("meta_batch", ctypes.c_int32), ("meta_heads", ctypes.c_int32),
+                ("num_q_blocks", ctypes.c_int32), ("num_kv_blocks", ctypes.c_int32),
+                ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32),
+                ("block_mask", ctypes.c_void_p), ("data_next", ctypes.c_void_p)]
+
+
+_I64x3 = ctypes.c_int64 * 3
+_FWD_ARGS = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+             ctypes.c_int,
+             ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+             ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+             ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+             ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+             ctypes.c_float, ctypes.POINTER(MaskDescC), ctypes.POINTER(MaskInfoC), ctypes.c_void_p]
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsplash.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m block_sparse_masked_splash_amd.build` "
+            "(there is no non-HIP implementation)")
+    lib = ctypes.CDLL(path)
+    lib.splash_mask_info_entries.restype = ctypes.c_size_t
+    lib.splash_mask_info_entries.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(MaskDescC)]
+    lib.splash_mask_info_build.restype = ctypes.c_int
+    lib.splash_mask_info_build.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(MaskDescC),
+                                                                ctypes.POINTER(MaskInfoC), ctypes.c_void_p]
+    for name in ("splash_fwd", "splash_pointwise_fwd"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = _FWD_ARGS
+    lib.splash_status_string.restype = ctypes.c_char_p
+    lib.splash_status_string.argtypes = [ctypes.c_int]
+    lib.splash_last_error.restype = ctypes.c_char_p
+    lib.splash_last_error.argtypes = []
+    lib.splash_abi_version.restype = ctypes.c_int
+    lib.splash_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != SPLASH_OK:
+        msg = load_library().splash_last_error().decode()
+        raise SplashError(status, msg)
+
+
+# ---------------------------------------------------------------------------
+# masks and metadata
+# ---------------------------------------------------------------------------
+
+
+def _head_array(head_masks):
+    hm = [tuple(int(x) for x in m) for m in head_masks]
+    arr = (HeadMaskC * max(1, len(hm)))()
+    for n, (c, wl, wr) in enumerate(hm):
+        arr[n] = HeadMaskC(c, wl, wr)
+    return arr, len(hm)
+
+
+def _seg_ptr(t, B, S, name):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.device.type != "cuda" or tuple(t.shape) != (B, S) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor of shape {(B, S)}")
+    return t.data_ptr()
+
+
+@dataclasses.dataclass
+class MaskInfo:
+    """Block metadata on the GPU plus the mask it was built from."""
+    B: int
+    H: int
+    q_len: int
+    kv_len: int
+    block_q: int
+    block_kv: int
+    head_masks: tuple
+    q_segment_ids: torch.Tensor | None
+    kv_segment_ids: torch.Tensor | None
+    block_mask: torch.Tensor   # int8 [meta_batch, meta_heads, nq, nk]
+    data_next: torch.Tensor    # int32, same shape
+
+    def mask_desc(self):
+        arr, n = _head_array(self.head_masks)
+        desc = MaskDescC(n, ctypes.cast(arr, ctypes.POINTER(HeadMaskC)),
+                         _seg_ptr(self.q_segment_ids, self.B, self.q_len, "q_segment_ids"),
+                         _seg_ptr(self.kv_segment_ids, self.B, self.kv_len, "kv_segment_ids"))
+        return desc, arr
+
+    def info_struct(self):
+        Bm, Hm, nq, nk = self.block_mask.shape
+        return MaskInfoC(Bm, Hm, nq, nk, self.block_q, self.block_kv,
+                         self.block_mask.data_ptr() if self.block_mask.numel() else None,
+                         self.data_next.data_ptr() if self.data_next.numel() else None)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def mask_info_build(B: int, H: int, q_len: int, kv_len: int, head_masks, block_q: int = 128,
+                    block_kv: int = 128, q_segment_ids=None, kv_segment_ids=None,
+                    device="cuda", out: MaskInfo | None = None) -> MaskInfo:
+    """Build block metadata with the library's kernel on the current stream.
+
+    ``head_masks``: one (causal, window_left, window_right) triple for every
+    head, or a single one broadcast to all heads. ``out`` reuses the buffers of
+    an earlier MaskInfo of the same shape."""
+    lib = load_library()
+    device = torch.device(device)
+    head_masks = tuple(tuple(int(x) for x in m) for m in head_masks)
+    if len(head_masks) not in (1, H) or len(head_masks) > MAX_MASK_HEADS:
+        raise ValueError("head_masks must hold 1 or H entries")
+    if (q_segment_ids is None) != (kv_segment_ids is None):
+        raise ValueError("both or neither of q_segment_ids and kv_segment_ids must be given")
+    Bm = B if q_segment_ids is not None else 1
+    nq = -(-q_len // block_q) if block_q > 0 else 0
+    nk = -(-kv_len // block_kv) if block_kv > 0 else 0
+    shape = (Bm, len(head_masks), nq, nk)
+    if out is not None and tuple(out.block_mask.shape) == shape:
+        bmask, dnext = out.block_mask, out.data_next
+    else:
+        bmask = torch.empty(shape, dtype=torch.int8, device=device)
+        dnext = torch.empty(shape, dtype=torch.int32, device=device)
+    info = MaskInfo(B, H, q_len, kv_len, block_q, block_kv, head_masks, q_segment_ids, kv_segment_ids,
+                    bmask, dnext)
+    desc, keep = info.mask_desc()
+    cinfo = info.info_struct()
+    st = lib.splash_mask_info_build(B, H, q_len, kv_len, block_q, block_kv, ctypes.byref(desc),
+                                    ctypes.byref(cinfo), ctypes.c_void_p(_stream(device)))
+    del keep
+    _check(st)
+    return info
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+
+_DT = {torch.float32: SPLASH_F32, torch.bfloat16: SPLASH_BF16}
+
+
+def _strides(t: torch.Tensor, layout: str):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("tensors must be 4-D with a contiguous last (head_dim) axis")
+    if layout == "bhsd":
+        return _I64x3(t.stride(0), t.stride(1), t.stride(2)), (t.shape[0], t.shape[1], t.shape[2], t.shape[3])
+    if layout == "bshd":
+        return _I64x3(t.stride(0), t.stride(2), t.stride(1)), (t.shape[0], t.shape[2], t.shape[1], t.shape[3])
+    raise ValueError(f"layout must be 'bhsd' or 'bshd', not {layout!r}")
+
+
+def _forward(fn_name, q, k, v, info: MaskInfo, scale, out, out_dtype, layout):
+    lib = load_library()
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    qs, (B, H, Sq, D) = _strides(q, layout)
+    ks, (Bk, Hk, Skv, Dk) = _strides(k, layout)
+    vs, vshape = _strides(v, layout)
+    if (Bk, Hk, Dk) != (B, H, D) or vshape != (B, H, Skv, D):
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)} ({layout})")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if out_dtype is None:
+        out_dtype = q.dtype if out is None else out.dtype
+    if out is None:
+        shape = (B, H, Sq, D) if layout == "bhsd" else (B, Sq, H, D)
+        out = torch.empty(shape, dtype=out_dtype, device=q.device)
+    if out.dtype != out_dtype or out.dtype not in _DT:
+        raise ValueError("bad output dtype")
+    os_, oshape = _strides(out, layout)
+    if oshape != (B, H, Sq, D):
+        raise ValueError("output shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if (info.B, info.H, info.q_len, info.kv_len) != (B, H, Sq, Skv):
+        # the library checks the metadata shape; this catches a different
+        # batch/head count that happens to give the same shape
+        raise SplashError(SPLASH_ERR_METADATA_MISMATCH,
+                          f"metadata built for B={info.B} H={info.H} q_len={info.q_len} kv_len={info.kv_len}")
+    desc, keep = info.mask_desc()
+    cinfo = info.info_struct()
+    fn = getattr(lib, fn_name)
+    st = fn(_DT[q.dtype], _DT[out_dtype], B, H, Sq, Skv, D,
+            q.data_ptr(), qs, k.data_ptr(), ks, v.data_ptr(), vs, out.data_ptr(), os_,
+            float(scale), ctypes.byref(desc), ctypes.byref(cinfo), ctypes.c_void_p(_stream(q.device)))
+    del keep
+    _check(st)
+    return out
+
+
+def splash_fwd(q, k, v, info: MaskInfo, scale: float | None = None, out=None, out_dtype=None,
+               layout: str = "bhsd"):
+    """Softmax attention forward under the block-sparse mask of ``info``.
+
+    q [B,H,Sq,D], k/v [B,H,Skv,D] (``layout="bshd"``: [B,S,H,D]); default scale
+    1/sqrt(D). Returns ``out`` (allocated if None)."""
+    return _forward("splash_fwd", q, k, v, info, scale, out, out_dtype, layout)
+
+
+def pointwise_fwd(q, k, v, info: MaskInfo, scale: float | None = None, out=None, out_dtype=None,
+                  layout: str = "bhsd"):
+    """Pointwise SiLU attention forward: (1/Sq) sum_k silu(scale q.k) v_k."""
+    return _forward("splash_pointwise_fwd", q, k, v, info, scale, out, out_dtype, layout)

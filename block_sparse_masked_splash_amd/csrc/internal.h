@@ -1,0 +1,61 @@
+// Internal interface between the C-ABI host layer (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "splash.h"
+
+namespace splash {
+
+// A head mask reduced to a band on d = k - q: allowed iff lo <= d <= hi.
+// causal sets hi <= 0; an unbounded side uses +-kUnbounded.
+constexpr int32_t kUnbounded = 0x3fffffff;
+constexpr int kMaxLen = 1 << 30;
+
+struct HeadBand {
+  int32_t lo;
+  int32_t hi;
+};
+
+struct MaskInfoParams {
+  int B, H, q_len, kv_len, block_q, block_kv;
+  int nq, nk, meta_batch, meta_heads;
+  const int32_t* q_seg;   // [B, q_len] or null
+  const int32_t* kv_seg;  // [B, kv_len] or null
+  int8_t* block_mask;
+  int32_t* data_next;
+  HeadBand band[SPLASH_MAX_MASK_HEADS];
+};
+
+struct FwdParams {
+  int B, H, q_len, kv_len, head_dim;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t o_sb, o_sh, o_ss;
+  float scale_log2;  // softmax: scale * log2(e); pointwise: scale * log2(e)
+  float scale;       // raw score scale
+  float inv_q_len;   // pointwise divisor 1 / q_len
+  int block_q, block_kv, nq, nk;
+  int meta_heads;    // 1 or H
+  int meta_batch;    // 1 or B
+  const int8_t* block_mask;
+  const int32_t* data_next;
+  const int32_t* q_seg;
+  const int32_t* kv_seg;
+  HeadBand band[SPLASH_MAX_MASK_HEADS];
+};
+
+// Launchers; return the launch error (hipSuccess when enqueued).
+hipError_t launch_mask_info(const MaskInfoParams& p, hipStream_t stream);
+// bf16 inputs, matrix-core path. out_f32 selects an fp32 output.
+hipError_t launch_fwd_bf16(const FwdParams& p, bool pointwise, bool out_f32, hipStream_t stream);
+// fp32 inputs and output.
+hipError_t launch_fwd_f32(const FwdParams& p, bool pointwise, hipStream_t stream);
+
+}  // namespace splash

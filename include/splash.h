@@ -1,0 +1,177 @@
+/*
+ * splash.h — C ABI of the block-sparse masked attention forward library
+ * (libsplash.so, AMD Instinct MI355X / gfx950).
+ *
+ * The operation is the forward pass of multi-head attention under a
+ * block-sparse mask, computed block by block with an online softmax so that
+ * the [S_q, S_kv] score matrix never exists:
+ *   - "hstu_ops.py" (RecML recml/core/ops/hstu_ops.py): per-(head, q block,
+ *     kv block) metadata read by `_next_nonzero` (a block runs when its class
+ *     is > 0 and needs no element mask when it is not 1, and the kv block to
+ *     fetch is `data_next`), element masks applied by `_apply_mask` (causal /
+ *     local window / segment ids, ANDed), and the pointwise (SiLU, no softmax)
+ *     forward `_pointwise_splash_attention_fwd_kernel_impl`;
+ *   - "JAX 到 VLIW，以及 Pallas / Splash Attention 复习笔记": section 12
+ *     (attention as softmax(Q Kᵀ) V), sections 15.1-15.3 (online softmax with
+ *     running max m, denominator L and numerator O), section 18 (grid over
+ *     (head, q block, kv block), kv axis sequential), section 21 (empty kv
+ *     blocks are never loaded: indirection through data_next), section 23
+ *     (only O is written back).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers unless marked HOST. Each call only enqueues
+ *     work on `stream` (0 = the null stream) and never synchronizes.
+ *   - All validation happens on the host before anything is enqueued. On any
+ *     error nothing is enqueued, no output is touched, a status code is
+ *     returned and splash_last_error() describes it. There is no fallback path.
+ *   - The library allocates no device memory; the caller owns every buffer.
+ *   - Positions: query q in [0, q_len), key k in [0, kv_len). Lengths need not
+ *     be multiples of the block sizes: the last block of each axis is ragged
+ *     and positions past the end are masked out.
+ */
+#ifndef SPLASH_H_
+#define SPLASH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPLASH_ABI_VERSION 1
+#define SPLASH_MAX_MASK_HEADS 256
+
+typedef enum {
+  SPLASH_OK = 0,
+  SPLASH_ERR_INVALID_ARGUMENT = 1,  /* null pointer, bad size/stride/alignment  */
+  SPLASH_ERR_UNSUPPORTED = 2,       /* valid request without a compiled kernel */
+  SPLASH_ERR_METADATA_MISMATCH = 3, /* metadata not built for this call        */
+  SPLASH_ERR_HIP = 4                /* no device, or a HIP launch error        */
+} splash_status;
+
+typedef enum { SPLASH_F32 = 0, SPLASH_BF16 = 1 } splash_dtype;
+
+/* Mask of one head ("hstu_ops.py", pointwise_splash_attention: CausalMask or
+ * FullMask, optionally ANDed with LocalMask((w, w), offset=0)).
+ * A pair (q, k) is allowed when
+ *   (causal == 0 || k <= q) &&
+ *   (window_left  < 0 || k >= q - window_left) &&
+ *   (window_right < 0 || k <= q + window_right).
+ * FULL = {0,-1,-1}; CAUSAL = {1,-1,-1}; causal AND local window w = {1,w,w}. */
+typedef struct {
+  int32_t causal;
+  int32_t window_left;
+  int32_t window_right;
+} splash_head_mask;
+
+/* Whole mask of a call. When segment ids are given, (q, k) is allowed only if
+ * q_segment_ids[b, q] == kv_segment_ids[b, k] as well ("hstu_ops.py",
+ * _apply_mask: segment equality ANDed with the other masks). */
+typedef struct {
+  int32_t num_mask_heads;          /* 1 (broadcast to every head) or H,
+                                      at most SPLASH_MAX_MASK_HEADS          */
+  const splash_head_mask* heads;   /* HOST array [num_mask_heads]           */
+  const int32_t* q_segment_ids;    /* DEVICE int32 [B, q_len] row-major, or NULL */
+  const int32_t* kv_segment_ids;   /* DEVICE int32 [B, kv_len] row-major, or NULL;
+                                      both or neither                        */
+} splash_mask_desc;
+
+/* Block metadata. Shape [meta_batch, meta_heads, num_q_blocks, num_kv_blocks],
+ * row-major, with meta_batch = B when segment ids are given (else 1),
+ * meta_heads = num_mask_heads, num_q_blocks = ceil(q_len / block_q),
+ * num_kv_blocks = ceil(kv_len / block_kv).
+ *   block_mask[...,i,j]: 0 = no allowed pair in block (i, j) (never loaded),
+ *                        1 = some pairs allowed (element mask applied),
+ *                        2 = every pair of the whole block allowed (no mask).
+ *   data_next[...,i,j]:  smallest j' >= j with block_mask[...,i,j'] != 0, or
+ *                        num_kv_blocks if there is none.
+ * The caller allocates both buffers (see splash_mask_info_entries) and fills
+ * the six integer fields; splash_mask_info_build writes the two arrays. */
+typedef struct {
+  int32_t meta_batch;
+  int32_t meta_heads;
+  int32_t num_q_blocks;
+  int32_t num_kv_blocks;
+  int32_t block_q;
+  int32_t block_kv;
+  int8_t* block_mask;   /* DEVICE int8  [meta_batch*meta_heads*nq*nk] */
+  int32_t* data_next;   /* DEVICE int32 [meta_batch*meta_heads*nq*nk] */
+} splash_mask_info;
+
+/* Number of entries of each metadata array for this call (0 if the arguments
+ * are invalid, or if a dimension is empty). Also usable to size the buffers:
+ * block_mask needs that many bytes, data_next four times as many. Host only. */
+size_t splash_mask_info_entries(int B, int H, int q_len, int kv_len, int block_q,
+                                int block_kv, const splash_mask_desc* mask);
+
+/* Build the block metadata on the GPU ("hstu_ops.py", _next_nonzero semantics;
+ * study notes section 21, data_next).
+ * block_q, block_kv: positive, at most 1024. `info` must describe buffers of
+ * the shape given above; its integer fields are checked against the call.
+ * Segment ids are read on the device. Errors: INVALID_ARGUMENT (bad sizes,
+ * null pointers, one segment array without the other, info shape wrong),
+ * HIP (launch failure / no device). */
+splash_status splash_mask_info_build(int B, int H, int q_len, int kv_len, int block_q,
+                                     int block_kv, const splash_mask_desc* mask,
+                                     const splash_mask_info* info, hipStream_t stream);
+
+/* Softmax attention forward:
+ *   o[b,h,q,:] = sum_{k allowed} e^{s_k - m} v[b,h,k,:] / sum_{k allowed} e^{s_k - m}
+ * with s_k = scale * <q[b,h,q,:], k[b,h,k,:]>, m the row max over allowed keys;
+ * a row with no allowed key is written as 0. Empty blocks (block_mask 0) are
+ * skipped through data_next and never read; the element mask is evaluated only
+ * on blocks of class 1 (study notes sections 15, 18, 21, 23).
+ *
+ * Tensors: q [B, H, q_len, head_dim], k and v [B, H, kv_len, head_dim],
+ * o [B, H, q_len, head_dim]. `*_strides` give the element strides of the
+ * batch, head and sequence axes (int64, HOST arrays of 3); head_dim is
+ * contiguous. This covers both [B,H,S,D] and the [B,S,H,D] layout of
+ * "hstu_ops.py" pointwise_splash_attention without copies. Every row must
+ * start 16-byte aligned (base pointers and strides accordingly).
+ *
+ * Supported: in_dtype/out_dtype F32/F32, BF16/BF16 or BF16/F32; head_dim 64 or
+ * 128; block_q and block_kv in {64, 128}. Arithmetic: F32 inputs are computed
+ * in fp32; BF16 inputs use bf16 matrix cores with fp32 accumulation and fp32
+ * softmax statistics, and the probabilities are rounded to bf16 for P·V.
+ * `info` must have been built for the same B, H, lengths, block sizes, mask
+ * heads and segment-id presence (METADATA_MISMATCH otherwise). */
+splash_status splash_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H,
+                         int q_len, int kv_len, int head_dim,
+                         const void* q, const int64_t q_strides[3],
+                         const void* k, const int64_t k_strides[3],
+                         const void* v, const int64_t v_strides[3],
+                         void* o, const int64_t o_strides[3],
+                         float scale, const splash_mask_desc* mask,
+                         const splash_mask_info* info, hipStream_t stream);
+
+/* Pointwise (HSTU) attention forward, "hstu_ops.py",
+ * _pointwise_splash_attention_fwd_kernel_impl:
+ *   o[b,h,q,:] = (1/q_len) * sum_{k allowed} silu(s_k) v[b,h,k,:],
+ *   silu(x) = x / (1 + e^{-x}), s_k as above.
+ * The contributions of all kv blocks are summed (the page's per-slice
+ * overwrite of the output is read as this accumulation). Same arguments,
+ * layouts, support matrix and errors as splash_fwd. */
+splash_status splash_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B,
+                                   int H, int q_len, int kv_len, int head_dim,
+                                   const void* q, const int64_t q_strides[3],
+                                   const void* k, const int64_t k_strides[3],
+                                   const void* v, const int64_t v_strides[3],
+                                   void* o, const int64_t o_strides[3],
+                                   float scale, const splash_mask_desc* mask,
+                                   const splash_mask_info* info, hipStream_t stream);
+
+/* Static name of a status code. */
+const char* splash_status_string(splash_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* splash_last_error(void);
+/* SPLASH_ABI_VERSION of the loaded library. */
+int splash_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLASH_H_ */

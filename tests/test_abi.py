@@ -1,0 +1,147 @@
+"""C ABI checks that need no GPU: exports, version, and argument validation.
+
+Every call made here fails validation on the host, which by contract happens
+before any HIP call, so nothing touches a device.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_masked_splash_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "splash.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(splash_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    declared = _declared_functions()
+    assert set(declared) == set(bd.SYMBOLS)
+    lib = bd.load_library()
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", bd.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (splash_\w+)", out))
+    assert set(declared) <= exported
+
+
+def test_version_and_status_strings():
+    lib = bd.load_library()
+    assert lib.splash_abi_version() == 1
+    assert lib.splash_status_string(0) == b"SPLASH_OK"
+    assert lib.splash_status_string(3) == b"SPLASH_ERR_METADATA_MISMATCH"
+    assert lib.splash_status_string(99) == b"SPLASH_ERR_UNKNOWN"
+
+
+def _desc(heads=((1, -1, -1),), qseg=None, kvseg=None, n=None):
+    arr, cnt = bd._head_array(heads)
+    d = bd.MaskDescC(cnt if n is None else n, ctypes.cast(arr, ctypes.POINTER(bd.HeadMaskC)), qseg, kvseg)
+    return d, arr
+
+
+def test_mask_info_entries():
+    lib = bd.load_library()
+    d, keep = _desc()
+    assert lib.splash_mask_info_entries(2, 4, 256, 256, 64, 64, ctypes.byref(d)) == 16
+    assert lib.splash_mask_info_entries(2, 4, 200, 130, 64, 64, ctypes.byref(d)) == 4 * 3
+    d2, keep2 = _desc(qseg=0x1000, kvseg=0x2000)
+    assert lib.splash_mask_info_entries(2, 4, 256, 256, 64, 64, ctypes.byref(d2)) == 2 * 16
+    d3, keep3 = _desc(qseg=0x1000)
+    assert lib.splash_mask_info_entries(2, 4, 256, 256, 64, 64, ctypes.byref(d3)) == 0
+    assert lib.splash_mask_info_entries(2, 4, 256, 256, 0, 64, ctypes.byref(d)) == 0
+    assert lib.splash_mask_info_entries(2, 4, -1, 256, 64, 64, ctypes.byref(d)) == 0
+    d4, keep4 = _desc(heads=[(1, -1, -1)] * 3)
+    assert lib.splash_mask_info_entries(2, 4, 256, 256, 64, 64, ctypes.byref(d4)) == 0
+
+
+def _info(Bm=1, Hm=1, nq=4, nk=4, bq=64, bkv=64, bm=0x10000, dn=0x20000):
+    return bd.MaskInfoC(Bm, Hm, nq, nk, bq, bkv, bm, dn)
+
+
+def _fwd(lib, fn="splash_fwd", in_dt=1, out_dt=1, B=1, H=1, Sq=256, Skv=256, D=128, q=0x100000,
+         k=0x200000, v=0x300000, o=0x400000, strides=None, scale=0.1, desc=None, info=None):
+    st = strides or [bd._I64x3(H * Sq * D, Sq * D, D) for _ in range(4)]
+    return getattr(lib, fn)(in_dt, out_dt, B, H, Sq, Skv, D, q, st[0], k, st[1], v, st[2], o, st[3],
+                            scale, None if desc is None else ctypes.byref(desc),
+                            None if info is None else ctypes.byref(info), None)
+
+
+@pytest.mark.parametrize("fn", ["splash_fwd", "splash_pointwise_fwd"])
+def test_forward_validation_errors(fn):
+    lib = bd.load_library()
+    d, keep = _desc()
+    inf = _info()
+    E = bd
+    # unsupported dtype pair and head_dim
+    assert _fwd(lib, fn, in_dt=0, out_dt=1, desc=d, info=inf) == E.SPLASH_ERR_UNSUPPORTED
+    assert _fwd(lib, fn, D=96, desc=d, info=inf) == E.SPLASH_ERR_UNSUPPORTED
+    assert b"head_dim" in lib.splash_last_error()
+    assert _fwd(lib, fn, D=0, desc=d, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
+    # null mask / info / tensors
+    assert _fwd(lib, fn, desc=None, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
+    assert _fwd(lib, fn, desc=d, info=None) == E.SPLASH_ERR_INVALID_ARGUMENT
+    assert _fwd(lib, fn, q=None, desc=d, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
+    # misaligned pointer and stride
+    assert _fwd(lib, fn, k=0x200002, desc=d, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
+    bad = [bd._I64x3(256 * 128, 256 * 128, 130)] * 4
+    assert _fwd(lib, fn, strides=bad, desc=d, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
+    # segment ids: both or neither
+    d1, keep1 = _desc(qseg=0x5000)
+    assert _fwd(lib, fn, desc=d1, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
+    assert b"both or neither" in lib.splash_last_error()
+    # num_mask_heads neither 1 nor H
+    d2, keep2 = _desc(heads=[(1, -1, -1)] * 2)
+    assert _fwd(lib, fn, H=3, desc=d2, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
+    # bad head mask fields
+    d3, keep3 = _desc(heads=[(2, -1, -1)])
+    assert _fwd(lib, fn, desc=d3, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
+    # metadata for another call
+    assert _fwd(lib, fn, desc=d, info=_info(nq=2)) == E.SPLASH_ERR_METADATA_MISMATCH
+    assert _fwd(lib, fn, desc=d, info=_info(Hm=2)) == E.SPLASH_ERR_METADATA_MISMATCH
+    d4, keep4 = _desc(qseg=0x5000, kvseg=0x6000)
+    assert _fwd(lib, fn, B=2, desc=d4, info=inf) == E.SPLASH_ERR_METADATA_MISMATCH  # built without segments
+    # block sizes without a kernel
+    assert _fwd(lib, fn, desc=d, info=_info(nq=8, nk=8, bq=32, bkv=32)) == E.SPLASH_ERR_UNSUPPORTED
+    # non-finite scale
+    assert _fwd(lib, fn, scale=float("nan"), desc=d, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
+
+
+def test_mask_info_build_validation_errors():
+    lib = bd.load_library()
+    d, keep = _desc()
+    inf = _info()
+
+    def call(B=1, H=1, Sq=256, Skv=256, bq=64, bkv=64, desc=d, info=inf):
+        return lib.splash_mask_info_build(B, H, Sq, Skv, bq, bkv, None if desc is None else ctypes.byref(desc),
+                                          None if info is None else ctypes.byref(info), None)
+
+    assert call(desc=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(info=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(bq=0) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(bq=2048) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(Sq=-5) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(info=_info(nq=3)) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(info=_info(bm=None)) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    d1, keep1 = _desc(kvseg=0x5000)
+    assert call(desc=d1) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    # empty metadata: nothing to build, nothing launched
+    assert call(Sq=0, info=_info(nq=0)) == bd.SPLASH_OK
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    saved = bd._lib
+    bd._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="missing"):
+            bd.load_library(str(tmp_path / "libsplash.so"))
+    finally:
+        bd._lib = saved
