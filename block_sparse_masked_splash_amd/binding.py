@@ -184,7 +184,9 @@ def mask_info_build(B: int, H: int, q_len: int, kv_len: int, head_masks, block_q
     if out is not None and tuple(out.block_mask.shape) == shape:
         bmask, dnext = out.block_mask, out.data_next
     else:
-        bmask = torch.empty(shape, dtype=torch.int8, device=device)
+        n = shape[0] * shape[1] * shape[2] * shape[3]
+        # the kernels read block classes as aligned 32-bit words: pad to whole words
+        bmask = torch.empty((n + 3) // 4 * 4, dtype=torch.int8, device=device)[:n].view(shape)
         dnext = torch.empty(shape, dtype=torch.int32, device=device)
     info = MaskInfo(B, H, q_len, kv_len, block_q, block_kv, head_masks, q_segment_ids, kv_segment_ids,
                     bmask, dnext)

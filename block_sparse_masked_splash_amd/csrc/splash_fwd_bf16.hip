@@ -12,18 +12,34 @@
 //       pointwise: P = silu(S) / q_len (masked -> 0), O = O + P V_j
 //     O_i = O / L (softmax; 0 where L = 0) or O (pointwise)
 //
-// Work decomposition: one workgroup of NW wavefronts per (b, h, i); each
-// wavefront owns 32 query rows (block_q = 32 * NW). The kv axis is walked in
-// tiles of 64 keys staged in LDS.
+// Work decomposition: one workgroup per (b, h, q block) with NW = block_q / 64
+// wavefronts; each wavefront owns 64 query rows as two 32-row column blocks,
+// so every K or V operand read from LDS feeds two matrix instructions. The kv
+// axis is walked in tiles of 64 keys: K and V tiles are copied HBM -> LDS by
+// direct (VGPR-free) 16-byte-per-lane loads, double-buffered so the copy of
+// tile t+1 runs under the math of tile t.
 //
 // Matrix-core layout: scores are formed transposed, Sᵀ = K Qᵀ, with
 // v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Qᵀ held in registers for
 // the whole kernel). In the 32x32 accumulator layout lane l holds column
 // l % 32 (its query row) and 16 rows (keys), so row max / row sum are
-// in-lane reductions plus one exchange between the two half-waves, and the
-// probabilities are already in the B-operand layout of Oᵀ += Vᵀ Pᵀ, so P never
-// leaves registers. The contraction index (key) order inside one MFMA is
-// free; A (Vᵀ from LDS) is read in the order the accumulator gives P.
+// in-lane reductions plus one exchange between the half-waves, and the
+// probabilities already sit in the B-operand layout of Oᵀ += Vᵀ Pᵀ: P never
+// leaves registers. Vᵀ is read from the row-major V tile with the gfx950
+// transposing LDS read (ds_read_b64_tr_b16), in the key order the
+// accumulator gives P.
+//
+// LDS tiles are row-major (one key per row, head_dim contiguous) with the
+// 16-byte chunks of row r stored at chunk position (chunk ^ (r & 7)), which
+// keeps the K operand reads and the transposing V reads free of bank
+// conflicts; the direct loads write that layout by choosing which global
+// chunk each lane fetches.
+//
+// Softmax bookkeeping is in the log2 domain with the scale folded into one
+// FMA before exp2. The reference maximum is only raised when a tile's maximum
+// exceeds it by more than 8 (so probabilities stay below 2^8): the rescale of
+// O and L is skipped for most tiles and the result is unchanged, because O and
+// L always share one reference.
 
 #include "internal.h"
 
@@ -32,17 +48,69 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
 
-constexpr int KC = 64;           // keys per LDS tile
+constexpr int KC = 64;                 // keys per LDS tile
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units a tile max may exceed the reference by
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-__device__ inline float wave_xor32(float x) {
-  // exchange with lane ^ 32 (the other half-wave)
-  return __shfl_xor(x, 32, 64);
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Direct global -> LDS copy: every active lane fetches 16 (or 4) bytes from its
+// own global address; lane L's bytes land at LDS byte address lds + 16 L (4 L).
+// Issued through asm so that the compiler does not treat the tile being
+// filled as a pending write to every LDS read that follows; completion is
+// awaited explicitly with wait_vmcnt (the copies count on vmcnt like loads).
+__device__ inline void lds_copy16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+__device__ inline void lds_copy4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+// LDS byte address of a (wave-uniform) shared-memory pointer, as an SGPR value.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p);
+}
+
+// Workgroup barrier without a memory fence: LDS reads are complete once their
+// values have been consumed, and direct-load completion is tracked by vmcnt,
+// so no wait on outstanding global traffic is wanted here.
+__device__ inline void barrier_only() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+}
+
+// Metadata is read-only for the whole launch and its addresses are uniform
+// across the workgroup: read it through the constant address space so the
+// loads go through the scalar cache (SGPRs, lgkmcnt) and never wait behind
+// the tile copies on vmcnt.
+typedef __attribute__((address_space(4))) const uint32_t* const_u32_ptr;
+__device__ inline int scalar_load_i32(const int32_t* p) {
+  return (int)*(const_u32_ptr)(uintptr_t)p;
+}
+// Class of kv block j in a metadata row, read as part of its aligned 32-bit
+// word (block_mask buffers are padded to whole words).
+__device__ inline int block_class(const int8_t* row, int j) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(row + j);
+  const uint32_t w = *(const_u32_ptr)(a & ~(uintptr_t)3);
+  return (int)((w >> (8 * (a & 3))) & 0xffu);
 }
 
 template <typename OutT>
@@ -64,220 +132,308 @@ __device__ inline void store4<float>(float* dst, float a, float b, float c, floa
   *reinterpret_cast<f32x4*>(dst) = v;
 }
 
+template <int D, int NW>
+struct Tiling {
+  static constexpr int NT = NW * 64;            // threads
+  static constexpr int ROWB = D * 2;            // bytes per key row
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;          // rows written by one direct-load instruction
+  static constexpr int TILE = KC * ROWB;        // bytes of one K or V tile
+  static constexpr int LOADS = (KC / RPI) / NW; // direct loads per wave per matrix per tile
+  static constexpr int SEG_KEYS = KC / NW;      // segment ids loaded per wave per tile
+  static constexpr int NS = D / 16;             // k-steps of the QKᵀ contraction
+  static constexpr int ND = D / 32;             // 32-wide output blocks
+  // LDS: [stage][K | V][TILE] then [stage][KC] int32 segment ids
+  static constexpr int SEG_OFF = 2 * 2 * TILE;
+  static constexpr int LDS_BYTES = SEG_OFF + 2 * KC * 4;
+};
+
 template <int D, int NW, bool PW, typename OutT>
-__global__ __launch_bounds__(NW * 64) void splash_fwd_bf16_kernel(FwdParams p) {
-  constexpr int NT = NW * 64;
-  constexpr int BQ = NW * 32;
-  constexpr int LDS_STRIDE = D + 8;      // bf16 elements per LDS row (pad vs bank conflicts)
-  constexpr int NS = D / 16;             // k-steps of the QKᵀ contraction
-  constexpr int ND = D / 32;             // 32-wide output column blocks
-  constexpr int CPR = D / 8;             // 16-byte chunks per row
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
+  using T = Tiling<D, NW>;
+  constexpr int NS = T::NS;
+  constexpr int ND = T::ND;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[KC * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[KC * LDS_STRIDE];
-  __shared__ int32_t sKseg[KC];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  // Heavy-first order: the last query blocks (most kv blocks under causal
-  // masks) of every (b, h) are dispatched first.
-  const int BH = p.B * p.H;
-  const int64_t lin = blockIdx.x;
-  const int bh = (int)(lin % BH);
-  const int i = p.nq - 1 - (int)(lin / BH);
+  // XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
+  // id -> (id % 8, id / 8) gives each XCD a contiguous range of logical work,
+  // which runs query blocks of the same (b, h) next to each other (K and V
+  // of that head stay in the XCD's L2). Within a head the heaviest query
+  // blocks (most kv blocks under causal masks) go first.
+  const int wid = (int)(blockIdx.x & 7) * work_per_xcd + (int)(blockIdx.x >> 3);
+  if (wid >= total_work) return;
+  const int bh = wid / p.nq;
+  const int i = p.nq - 1 - (wid - bh * p.nq);
   const int b = bh / p.H;
-  const int h = bh % p.H;
+  const int h = bh - b * p.H;
   const int hm = p.meta_heads == 1 ? 0 : h;
   const int bm = p.meta_batch == 1 ? 0 : b;
   const HeadBand band = p.band[hm];
 
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
   const __bf16* qg = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
-  const __bf16* kg = reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + h * p.k_sh;
-  const __bf16* vg = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + h * p.v_sh;
+  const char* kg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + h * p.k_sh);
+  const char* vg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + h * p.v_sh);
   OutT* og = reinterpret_cast<OutT*>(p.o) + b * p.o_sb + h * p.o_sh;
-
-  const int qrow = i * BQ + wave * 32 + l32;
-  const bool qvalid = qrow < p.q_len;
-
-  // Qᵀ as the B operand: lane holds Q[qrow][16 s + 8 hh + 0..7].
-  bf16x8 qreg[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (qvalid) {
-      qreg[s] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)qrow * p.q_ss + 16 * s + 8 * hh);
-    } else {
-      for (int e = 0; e < 8; ++e) qreg[s][e] = (__bf16)0.0f;
-    }
-  }
+  const int64_t k_rs = p.k_ss * 2;  // bytes between key rows
+  const int64_t v_rs = p.v_ss * 2;
   const bool has_seg = p.q_seg != nullptr;
-  const int32_t my_qseg = (has_seg && qvalid) ? p.q_seg[(int64_t)b * p.q_len + qrow] : 0;
+  const int32_t* kvseg_g = has_seg ? p.kv_seg + (int64_t)b * p.kv_len : nullptr;
 
-  f32x16 oacc[ND];
+  // ---- Q (B operand of Sᵀ = K Qᵀ), two 32-row column blocks per wave ----
+  // Softmax only depends on scale through scale * scores; a negative scale is
+  // applied as an exact sign flip of Q so the fused exponent uses c >= 0.
+  const bool negate_q = !PW && p.scale < 0.0f;
+  // (a zero scale is taken as the smallest normal float: every allowed score
+  // then gets the same weight, and -inf * c stays -inf for masked ones)
+  const float c = PW ? p.scale : fmaxf(negate_q ? -p.scale_log2 : p.scale_log2, 1.17549435e-38f);
+  int qrow[2];
+  bf16x8 qreg[2][NS];
+  int32_t myseg[2];
 #pragma unroll
-  for (int d = 0; d < ND; ++d)
-    for (int r = 0; r < 16; ++r) oacc[d][r] = 0.0f;
-  float m_run = kNegInf;   // running max of the scaled scores (log2 domain)
-  float l_run = 0.0f;      // this lane's share of the running denominator
+  for (int cb = 0; cb < 2; ++cb) {
+    qrow[cb] = i * (NW * 64) + wave * 64 + cb * 32 + l32;
+    const bool valid = qrow[cb] < p.q_len;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (valid) v = *reinterpret_cast<const i16x8*>(qg + (int64_t)qrow[cb] * p.q_ss + 16 * s + 8 * hh);
+      if (negate_q) v ^= (short)0x8000;
+      qreg[cb][s] = __builtin_bit_cast(bf16x8, v);
+    }
+    myseg[cb] = (has_seg && valid) ? p.q_seg[(int64_t)b * p.q_len + qrow[cb]] : 0;
+  }
+
+  // ---- per-lane LDS offsets (swizzled chunk positions) ----
+  // K operand: row 32 kb + l32, chunk 2 s + hh -> position (2 s + hh) ^ (l32 & 7).
+  int koff[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) koff[s] = l32 * T::ROWB + 16 * ((2 * s + hh) ^ (l32 & 7));
+  // V operand (transposing read): lane L reads 4 values of key
+  // kbase + 8 half + 4 hh + ((L % 16) >> 2) at head-dim 32 db + 16 ((L >> 4) & 1) + 4 (L & 3).
+  const int vkey = 4 * hh + ((lane & 15) >> 2);  // key within an 8-key group, also (key & 7)
+  int voff[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) {
+    const int dcol = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    voff[db] = vkey * T::ROWB + 16 * ((dcol >> 3) ^ vkey) + 2 * (dcol & 7);
+  }
+
+  // ---- direct HBM -> LDS copy of one K/V tile (plus segment ids) ----
+  auto issue_tile = [&](int stage, int key0) {
+    char* kdst = smem + stage * 2 * T::TILE;
+    char* vdst = kdst + T::TILE;
+#pragma unroll
+    for (int n = 0; n < T::LOADS; ++n) {
+      const int rb = (n * NW + wave) * T::RPI;
+      const int r = rb + lane / T::CPR;
+      const int chunk = (lane % T::CPR) ^ (r & 7);
+      int row = key0 + r;
+      row = row < p.kv_len ? row : p.kv_len - 1;  // rows past the end: any in-bounds row (masked)
+      lds_copy16(kg + row * k_rs + chunk * 16, lds_addr(kdst + rb * T::ROWB));
+      lds_copy16(vg + row * v_rs + chunk * 16, lds_addr(vdst + rb * T::ROWB));
+    }
+    if (has_seg) {
+      const uint32_t sdst = lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * KC + wave * T::SEG_KEYS);
+      if (lane < T::SEG_KEYS) {
+        int key = key0 + wave * T::SEG_KEYS + lane;
+        key = key < p.kv_len ? key : p.kv_len - 1;
+        lds_copy4(kvseg_g + key, sdst);
+      }
+    }
+  };
+
+  f32x16 oacc[2][ND];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[cb][db][r] = 0.0f;
+  float mref[2] = {kNegInf, kNegInf};  // reference max (log2 domain), shared by O and L
+  float lsum[2] = {0.0f, 0.0f};        // this lane's share of L
 
   const int64_t mrow = (((int64_t)bm * p.meta_heads + hm) * p.nq + i) * p.nk;
   const int8_t* bmask = p.block_mask + mrow;
   const int32_t* dnext = p.data_next + mrow;
 
-  // data_next is only followed forward and within [0, nk], so any metadata
-  // content ends the walk in bounds.
-  int j = p.nk > 0 ? dnext[0] : p.nk;
-  if (j < 0 || j > p.nk) j = p.nk;
-  while (j < p.nk) {
-    const bool partial = bmask[j] == 1;
-    for (int t = 0; t < p.block_kv; t += KC) {
-      const int k0 = j * p.block_kv + t;
-      if (k0 >= p.kv_len) break;
-      __syncthreads();  // every wave is done with the previous tile
-      for (int c = tid; c < KC * CPR; c += NT) {
-        const int r = c / CPR;
-        const int cc = c % CPR;
-        const int kv = k0 + r;
-        uint4 kval = {0u, 0u, 0u, 0u};
-        uint4 vval = {0u, 0u, 0u, 0u};
-        if (kv < p.kv_len) {
-          kval = *reinterpret_cast<const uint4*>(kg + (int64_t)kv * p.k_ss + cc * 8);
-          vval = *reinterpret_cast<const uint4*>(vg + (int64_t)kv * p.v_ss + cc * 8);
-        }
-        *reinterpret_cast<uint4*>(&sK[r * LDS_STRIDE + cc * 8]) = kval;
-        *reinterpret_cast<uint4*>(&sV[r * LDS_STRIDE + cc * 8]) = vval;
-      }
-      if (partial && has_seg && tid < KC) {
-        const int kv = k0 + tid;
-        sKseg[tid] = kv < p.kv_len ? p.kv_seg[(int64_t)b * p.kv_len + kv] : 0;
-      }
-      __syncthreads();
+  // Walk: tiles of 64 keys inside the non-empty blocks reached through
+  // data_next. data_next is only followed forward and within [0, nk], so any
+  // metadata content ends the walk in bounds.
+  auto next_block = [&](int j) {
+    const int jn = (j + 1 < p.nk) ? scalar_load_i32(dnext + j + 1) : p.nk;
+    return (jn > j && jn <= p.nk) ? jn : p.nk;
+  };
+  int cur_j = p.nk > 0 ? scalar_load_i32(dnext) : p.nk;
+  if (cur_j < 0 || cur_j > p.nk) cur_j = p.nk;
+  int cur_t = 0;
+  int stage = 0;
+  if (cur_j < p.nk) issue_tile(0, cur_j * p.block_kv);
 
-      // Sᵀ tile: 64 keys x 32 queries per wave, two 32x32 accumulators.
+  while (cur_j < p.nk) {
+    int nxt_j = cur_j, nxt_t = cur_t + KC;
+    if (nxt_t >= p.block_kv || cur_j * p.block_kv + nxt_t >= p.kv_len) {
+      nxt_j = next_block(cur_j);
+      nxt_t = 0;
+    }
+    const bool has_next = nxt_j < p.nk;
+    if (has_next) {
+      issue_tile(stage ^ 1, nxt_j * p.block_kv + nxt_t);
+      // this wave's copies of the current tile are done once at most the
+      // copies of the next tile are still in flight
+      if (has_seg) {
+        wait_vmcnt<2 * T::LOADS + 1>();
+      } else {
+        wait_vmcnt<2 * T::LOADS>();
+      }
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_only();  // every wave's copies of the current tile are done
+
+    const int k0 = cur_j * p.block_kv + cur_t;
+    const bool partial = block_class(bmask, cur_j) == 1;
+    const char* kt = smem + stage * 2 * T::TILE;
+    const char* vt = kt + T::TILE;
+
+    const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * KC;
+    // The tile is processed as two halves of 32 keys (kb), each: Sᵀ, softmax, Oᵀ += Vᵀ Pᵀ.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // ---- Sᵀ = K Qᵀ: 32 keys x 64 queries ----
       f32x16 sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+      for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(&sK[(32 * kb + l32) * LDS_STRIDE + 16 * s + 8 * hh]);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[kb], 0, 0, 0);
-        }
+        for (int r = 0; r < 16; ++r) sacc[cb][r] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * T::ROWB + koff[s]);
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0][s], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[1][s], sacc[1], 0, 0, 0);
       }
 
-      // sacc[kb][r] is the score of key k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4.
-      float x[2][16];
-      if constexpr (!PW) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          for (int r = 0; r < 16; ++r) x[kb][r] = sacc[kb][r] * p.scale_log2;
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          for (int r = 0; r < 16; ++r) x[kb][r] = sacc[kb][r] * p.scale;
-      }
+      // sacc[cb][r] is the score of key k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4
+      // against query qrow[cb].
       if (partial) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          for (int r = 0; r < 16; ++r) {
-            const int kl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const int kv = k0 + kl;
-            const int dlt = kv - qrow;
-            bool ok = kv < p.kv_len && dlt >= band.lo && dlt <= band.hi;
-            if (has_seg) ok = ok && (sKseg[kl] == my_qseg);
-            if (!ok) x[kb][r] = PW ? 0.0f : kNegInf;
-          }
-      }
-
-      bf16x8 pb[2][2];
-      if constexpr (!PW) {
-        float mx = kNegInf;
+        for (int r = 0; r < 16; ++r) {
+          const int kl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int key = k0 + kl;
+          const int kseg = has_seg ? sseg[kl] : 0;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kb][r]);
-        mx = fmaxf(mx, wave_xor32(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == kNegInf ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
-        float rs = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          for (int r = 0; r < 16; ++r) {
-            const float e = fast_exp2(x[kb][r] - m_use);
-            rs += e;
-            pb[kb][r >> 3][r & 7] = (__bf16)e;
-          }
-        l_run = l_run * alpha + rs;
-#pragma unroll
-        for (int d = 0; d < ND; ++d)
-          for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-      } else {
-        constexpr float kLog2e = 1.4426950408889634f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          for (int r = 0; r < 16; ++r) {
-            const float xv = x[kb][r];
-            const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-xv * kLog2e));
-            pb[kb][r >> 3][r & 7] = (__bf16)(xv * sg * p.inv_q_len);
-          }
-      }
-
-      // Oᵀ += Vᵀ Pᵀ. Step (kb, g) contracts keys 32 kb + 16 g + 8 (e / 4) + 4 hh + e % 4.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int kbase = 32 * kb + 16 * g + 4 * hh;
-#pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            bf16x8 a;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              a[e] = sV[(kbase + 8 * (e >> 2) + (e & 3)) * LDS_STRIDE + 32 * d + l32];
-            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][g], oacc[d], 0, 0, 0);
+          for (int cb = 0; cb < 2; ++cb) {
+            const int dlt = key - qrow[cb];
+            const bool ok = key < p.kv_len && dlt >= band.lo && dlt <= band.hi && kseg == myseg[cb];
+            if (!ok) sacc[cb][r] = PW ? 0.0f : kNegInf;
           }
         }
+      }
+
+      bf16x8 pb[2][2];  // [g][cb]: B operand of Oᵀ += Vᵀ Pᵀ for keys 32 kb + 16 g + ...
+      if constexpr (!PW) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          float mx = kNegInf;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[cb][r]);
+          mx = fmaxf(mx, xor32(mx)) * c;  // max of these 32 keys, log2 domain (-inf if none allowed)
+          const bool raise = mx > mref[cb] + kRescaleSlack;
+          if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+            const float alpha = raise ? fast_exp2(mref[cb] - mx) : 1.0f;
+            mref[cb] = raise ? mx : mref[cb];
+            lsum[cb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[cb][db][r] *= alpha;
+          }
+          // rows with nothing allowed yet keep mref = -inf; all their entries are -inf here
+          const float mneg = mref[cb] == kNegInf ? 0.0f : -mref[cb];
+          float rs = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(__builtin_fmaf(sacc[cb][r], c, mneg));
+            rs += e;
+            pb[r >> 3][cb][r & 7] = (__bf16)e;
+          }
+          lsum[cb] += rs;
+        }
+      } else {
+        const float cneg = -c * kLog2e;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float sv = sacc[cb][r];
+            const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(sv * cneg));
+            pb[r >> 3][cb][r & 7] = (__bf16)(sv * c * sg * p.inv_q_len);
+          }
+      }
+
+      // ---- Oᵀ += Vᵀ Pᵀ over these 32 keys ----
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int rowbase = (32 * kb + 16 * g) * T::ROWB;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vt + rowbase + voff[db]));
+          const i16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vt + rowbase + 8 * T::ROWB + voff[db]));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g][0], oacc[0][db], 0, 0, 0);
+          oacc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g][1], oacc[1][db], 0, 0, 0);
+        }
+      }
     }
-    const int jn = (j + 1 < p.nk) ? dnext[j + 1] : p.nk;
-    j = (jn > j && jn <= p.nk) ? jn : p.nk;
+
+    barrier_only();  // every wave is done reading this stage before it is refilled
+    stage ^= 1;
+    cur_j = nxt_j;
+    cur_t = nxt_t;
   }
 
-  float inv = 1.0f;
-  if constexpr (!PW) {
-    const float l = l_run + wave_xor32(l_run);
-    inv = l > 0.0f ? 1.0f / l : 0.0f;
-  }
-  if (qvalid) {
-    OutT* orow = og + (int64_t)qrow * p.o_ss;
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
+  for (int cb = 0; cb < 2; ++cb) {
+    float inv = 1.0f;
+    if constexpr (!PW) {
+      const float l = lsum[cb] + xor32(lsum[cb]);
+      inv = l > 0.0f ? 1.0f / l : 0.0f;
+    }
+    if (qrow[cb] < p.q_len) {
+      OutT* orow = og + (int64_t)qrow[cb] * p.o_ss;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * d + 8 * g + 4 * hh;
-        store4<OutT>(orow + col, oacc[d][4 * g] * inv, oacc[d][4 * g + 1] * inv,
-                     oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv);
-      }
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = 32 * db + 8 * g + 4 * hh;
+          store4<OutT>(orow + col, oacc[cb][db][4 * g] * inv, oacc[cb][db][4 * g + 1] * inv,
+                       oacc[cb][db][4 * g + 2] * inv, oacc[cb][db][4 * g + 3] * inv);
+        }
+    }
   }
 }
 
 template <int D, int NW, bool PW, typename OutT>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.nq * p.B * p.H;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((splash_fwd_bf16_kernel<D, NW, PW, OutT>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     stream, p);
+  const int64_t total = (int64_t)p.nq * p.B * p.H;
+  if (total == 0) return hipSuccess;
+  const int64_t per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL((splash_fwd_bf16_kernel<D, NW, PW, OutT>), dim3((unsigned)(per_xcd * 8)), dim3(NW * 64), 0,
+                     stream, p, (int)total, (int)per_xcd);
   return hipGetLastError();
 }
 
 template <int D, bool PW, typename OutT>
 hipError_t launch_bq(const FwdParams& p, hipStream_t stream) {
-  if (p.block_q == 64) return launch_one<D, 2, PW, OutT>(p, stream);
-  return launch_one<D, 4, PW, OutT>(p, stream);
+  if (p.block_q == 64) return launch_one<D, 1, PW, OutT>(p, stream);
+  return launch_one<D, 2, PW, OutT>(p, stream);
 }
 
 template <bool PW, typename OutT>

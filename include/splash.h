@@ -89,7 +89,9 @@ typedef struct {
  *   data_next[...,i,j]:  smallest j' >= j with block_mask[...,i,j'] != 0, or
  *                        num_kv_blocks if there is none.
  * The caller allocates both buffers (see splash_mask_info_entries) and fills
- * the six integer fields; splash_mask_info_build writes the two arrays. */
+ * the six integer fields; splash_mask_info_build writes the two arrays. The
+ * forward kernels read block_mask in aligned 32-bit words, so its allocation
+ * must be 4-byte aligned and extend to a whole number of 32-bit words. */
 typedef struct {
   int32_t meta_batch;
   int32_t meta_heads;
