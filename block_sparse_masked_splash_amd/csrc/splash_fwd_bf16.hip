@@ -37,9 +37,10 @@
 //
 // Softmax bookkeeping is in the log2 domain with the scale folded into one
 // FMA before exp2. The reference maximum is only raised when a tile's maximum
-// exceeds it by more than 8 (so probabilities stay below 2^8): the rescale of
-// O and L is skipped for most tiles and the result is unchanged, because O and
-// L always share one reference.
+// exceeds it by more than 32 (probabilities stay below 2^32, far from the
+// fp32/bf16 range limit): after the first tile of a row the rescale of O and L
+// is practically never needed, and the result is unchanged because O and L
+// always share one reference.
 
 #include "internal.h"
 
@@ -59,10 +60,19 @@ typedef __attribute__((address_space(1))) void* global_void_ptr;
 constexpr int KC = 64;                 // keys per LDS tile
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.0f;  // log2 units a tile max may exceed the reference by
+constexpr float kRescaleSlack = 32.0f;  // log2 units a tile max may exceed the reference by
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// {x, x of lane ^ 32}: the gfx950 half-wave swap returns both halves' values
+// in each lane, in an order that does not matter for max and sum.
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
@@ -71,17 +81,33 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Direct global -> LDS copy: every active lane fetches 16 (or 4) bytes from its
-// own global address; lane L's bytes land at LDS byte address lds + 16 L (4 L).
-// Issued through asm so that the compiler does not treat the tile being
-// filled as a pending write to every LDS read that follows; completion is
-// awaited explicitly with wait_vmcnt (the copies count on vmcnt like loads).
-__device__ inline void lds_copy16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+// Direct HBM -> LDS copies through a buffer resource: every active lane
+// fetches 16 (or 4) bytes at byte offset voff + soff of the buffer, and lane
+// L's bytes land at LDS byte address lds + 16 L (4 L). Offsets at or past the
+// buffer's size read as zero, which clips a tile at the end of the sequence
+// with no per-lane arithmetic. Issued through asm so that the compiler does
+// not treat the tile being filled as a pending write to every LDS read that
+// follows; completion is awaited explicitly with wait_vmcnt.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // 32-bit data format, no swizzle, no stride
+
+__device__ inline u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kRawBufferWord3;
+  return r;
+}
+__device__ inline void lds_copy16(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(soff), "s"(lds)
                : "memory", "m0");
 }
-__device__ inline void lds_copy4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
+__device__ inline void lds_copy4(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(soff), "s"(lds)
                : "memory", "m0");
 }
 // LDS byte address of a (wave-uniform) shared-memory pointer, as an SGPR value.
@@ -111,6 +137,20 @@ __device__ inline int block_class(const int8_t* row, int j) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(row + j);
   const uint32_t w = *(const_u32_ptr)(a & ~(uintptr_t)3);
   return (int)((w >> (8 * (a & 3))) & 0xffu);
+}
+
+// Q stays constant for the whole kernel and is only ever an MFMA operand,
+// which may come straight from the accumulation registers: place it there to
+// leave the ordinary VGPRs to the softmax and the output accumulators.
+__device__ inline bf16x8 to_agpr(bf16x8 x) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  i32x4 v = __builtin_bit_cast(i32x4, x);
+  i32x4 r;
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(r[0]) : "v"(v[0]));
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(r[1]) : "v"(v[1]));
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(r[2]) : "v"(v[2]));
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(r[3]) : "v"(v[3]));
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 template <typename OutT>
@@ -205,7 +245,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
       i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
       if (valid) v = *reinterpret_cast<const i16x8*>(qg + (int64_t)qrow[cb] * p.q_ss + 16 * s + 8 * hh);
       if (negate_q) v ^= (short)0x8000;
-      qreg[cb][s] = __builtin_bit_cast(bf16x8, v);
+      qreg[cb][s] = to_agpr(__builtin_bit_cast(bf16x8, v));
     }
     myseg[cb] = (has_seg && valid) ? p.q_seg[(int64_t)b * p.q_len + qrow[cb]] : 0;
   }
@@ -226,28 +266,44 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
   }
 
   // ---- direct HBM -> LDS copy of one K/V tile (plus segment ids) ----
+  // Load n of this wave fills rows rb .. rb + RPI - 1 (rb = (n NW + wave) RPI):
+  // lane L writes row rb + L / CPR at chunk position L % CPR, so it fetches
+  // logical chunk (L % CPR) ^ (row & 7). The per-lane part of the byte offset
+  // only depends on the parity of n NW + wave (RPI = 4) or on nothing (RPI = 8).
+  uint32_t kvo[2], vvo[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int rr = lane / T::CPR;
+    const int r7 = ((T::RPI == 4 ? 4 * par : 0) + rr) & 7;
+    const int chunk = (lane % T::CPR) ^ r7;
+    kvo[par] = (uint32_t)(rr * k_rs + chunk * 16);
+    vvo[par] = (uint32_t)(rr * v_rs + chunk * 16);
+  }
   auto issue_tile = [&](int stage, int key0) {
     char* kdst = smem + stage * 2 * T::TILE;
     char* vdst = kdst + T::TILE;
+    const int rows = p.kv_len - key0 < KC ? p.kv_len - key0 : KC;  // rows past the end read as 0
+    const u32x4 krs = buffer_rsrc(kg + key0 * k_rs, (uint32_t)(rows * k_rs));
+    const u32x4 vrs = buffer_rsrc(vg + key0 * v_rs, (uint32_t)(rows * v_rs));
 #pragma unroll
     for (int n = 0; n < T::LOADS; ++n) {
-      const int rb = (n * NW + wave) * T::RPI;
-      const int r = rb + lane / T::CPR;
-      const int chunk = (lane % T::CPR) ^ (r & 7);
-      int row = key0 + r;
-      row = row < p.kv_len ? row : p.kv_len - 1;  // rows past the end: any in-bounds row (masked)
-      lds_copy16(kg + row * k_rs + chunk * 16, lds_addr(kdst + rb * T::ROWB));
-      lds_copy16(vg + row * v_rs + chunk * 16, lds_addr(vdst + rb * T::ROWB));
+      const int blk = n * NW + wave;
+      const int rb = blk * T::RPI;
+      lds_copy16(krs, kvo[blk & 1], (uint32_t)(rb * k_rs), lds_addr(kdst + rb * T::ROWB));
+      lds_copy16(vrs, vvo[blk & 1], (uint32_t)(rb * v_rs), lds_addr(vdst + rb * T::ROWB));
     }
     if (has_seg) {
       const uint32_t sdst = lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * KC + wave * T::SEG_KEYS);
-      if (lane < T::SEG_KEYS) {
-        int key = key0 + wave * T::SEG_KEYS + lane;
-        key = key < p.kv_len ? key : p.kv_len - 1;
-        lds_copy4(kvseg_g + key, sdst);
-      }
+      const u32x4 srs = buffer_rsrc(kvseg_g + key0, (uint32_t)(rows * 4));
+      if (lane < T::SEG_KEYS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_KEYS * 4), sdst);
     }
   };
+
+  // The tiles start zeroed, so rows that a clipped copy leaves unwritten can
+  // never hold NaN bit patterns (their probabilities are 0, and 0 * NaN is NaN).
+  for (int o = tid * 16; o < T::SEG_OFF; o += T::NT * 16)
+    *reinterpret_cast<uint4*>(smem + o) = uint4{0u, 0u, 0u, 0u};
+  __syncthreads();
 
   f32x16 oacc[2][ND];
 #pragma unroll
@@ -326,11 +382,11 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
         for (int r = 0; r < 16; ++r) {
           const int kl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
           const int key = k0 + kl;
-          const int kseg = has_seg ? sseg[kl] : 0;
+          const int kseg = sseg[kl];
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) {
             const int dlt = key - qrow[cb];
-            const bool ok = key < p.kv_len && dlt >= band.lo && dlt <= band.hi && kseg == myseg[cb];
+            const bool ok = key < p.kv_len && dlt >= band.lo && dlt <= band.hi && (!has_seg || kseg == myseg[cb]);
             if (!ok) sacc[cb][r] = PW ? 0.0f : kNegInf;
           }
         }
@@ -343,7 +399,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
           float mx = kNegInf;
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[cb][r]);
-          mx = fmaxf(mx, xor32(mx)) * c;  // max of these 32 keys, log2 domain (-inf if none allowed)
+          mx = max_xor32(mx) * c;  // max of these 32 keys, log2 domain (-inf if none allowed)
           const bool raise = mx > mref[cb] + kRescaleSlack;
           if (__builtin_amdgcn_ballot_w64(raise) != 0) {
             const float alpha = raise ? fast_exp2(mref[cb] - mx) : 1.0f;
@@ -403,7 +459,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
   for (int cb = 0; cb < 2; ++cb) {
     float inv = 1.0f;
     if constexpr (!PW) {
-      const float l = lsum[cb] + xor32(lsum[cb]);
+      const float l = sum_xor32(lsum[cb]);
       inv = l > 0.0f ? 1.0f / l : 0.0f;
     }
     if (qrow[cb] < p.q_len) {
