@@ -188,8 +188,8 @@ struct Tiling {
   static constexpr int LDS_BYTES = SEG_OFF + 2 * KC * 4;
 };
 
-template <int D, int NW, bool PW, typename OutT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int NW, int CB, bool PW, typename OutT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CB == 1 ? 2 : 1, CB == 1 ? 2 : 1)))
 void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
   using T = Tiling<D, NW>;
   constexpr int NS = T::NS;
@@ -233,12 +233,12 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
   // (a zero scale is taken as the smallest normal float: every allowed score
   // then gets the same weight, and -inf * c stays -inf for masked ones)
   const float c = PW ? p.scale : fmaxf(negate_q ? -p.scale_log2 : p.scale_log2, 1.17549435e-38f);
-  int qrow[2];
-  bf16x8 qreg[2][NS];
-  int32_t myseg[2];
+  int qrow[CB];
+  bf16x8 qreg[CB][NS];
+  int32_t myseg[CB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    qrow[cb] = i * (NW * 64) + wave * 64 + cb * 32 + l32;
+  for (int cb = 0; cb < CB; ++cb) {
+    qrow[cb] = i * (NW * 32 * CB) + wave * (32 * CB) + cb * 32 + l32;
     const bool valid = qrow[cb] < p.q_len;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -305,15 +305,19 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
     *reinterpret_cast<uint4*>(smem + o) = uint4{0u, 0u, 0u, 0u};
   __syncthreads();
 
-  f32x16 oacc[2][ND];
+  f32x16 oacc[CB][ND];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[cb][db][r] = 0.0f;
-  float mref[2] = {kNegInf, kNegInf};  // reference max (log2 domain), shared by O and L
-  float lsum[2] = {0.0f, 0.0f};        // this lane's share of L
+  float mref[CB], lsum[CB];  // reference max (log2 domain), shared by O and L; this lane's share of L
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    mref[cb] = kNegInf;
+    lsum[cb] = 0.0f;
+  }
 
   const int64_t mrow = (((int64_t)bm * p.meta_heads + hm) * p.nq + i) * p.nk;
   const int8_t* bmask = p.block_mask + mrow;
@@ -363,16 +367,17 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // ---- Sᵀ = K Qᵀ: 32 keys x 64 queries ----
-      f32x16 sacc[2];
+      f32x16 sacc[CB];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[cb][r] = 0.0f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * T::ROWB + koff[s]);
-        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0][s], sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[1][s], sacc[1], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          sacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cb][s], sacc[cb], 0, 0, 0);
       }
 
       // sacc[cb][r] is the score of key k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4
@@ -384,7 +389,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
           const int key = k0 + kl;
           const int kseg = sseg[kl];
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
+          for (int cb = 0; cb < CB; ++cb) {
             const int dlt = key - qrow[cb];
             const bool ok = key < p.kv_len && dlt >= band.lo && dlt <= band.hi && (!has_seg || kseg == myseg[cb]);
             if (!ok) sacc[cb][r] = PW ? 0.0f : kNegInf;
@@ -392,10 +397,10 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
         }
       }
 
-      bf16x8 pb[2][2];  // [g][cb]: B operand of Oᵀ += Vᵀ Pᵀ for keys 32 kb + 16 g + ...
+      bf16x8 pb[2][CB];  // [g][cb]: B operand of Oᵀ += Vᵀ Pᵀ for keys 32 kb + 16 g + ...
       if constexpr (!PW) {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < CB; ++cb) {
           float mx = kNegInf;
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[cb][r]);
@@ -424,7 +429,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
       } else {
         const float cneg = -c * kLog2e;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float sv = sacc[cb][r];
@@ -443,8 +448,9 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
           const i16x4 hi =
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vt + rowbase + 8 * T::ROWB + voff[db]));
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g][0], oacc[0][db], 0, 0, 0);
-          oacc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g][1], oacc[1][db], 0, 0, 0);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            oacc[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g][cb], oacc[cb][db], 0, 0, 0);
         }
       }
     }
@@ -456,7 +462,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
   }
 
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     float inv = 1.0f;
     if constexpr (!PW) {
       const float l = sum_xor32(lsum[cb]);
@@ -476,20 +482,26 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
   }
 }
 
-template <int D, int NW, bool PW, typename OutT>
+template <int D, int NW, int CB, bool PW, typename OutT>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   const int64_t total = (int64_t)p.nq * p.B * p.H;
   if (total == 0) return hipSuccess;
   const int64_t per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((splash_fwd_bf16_kernel<D, NW, PW, OutT>), dim3((unsigned)(per_xcd * 8)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((splash_fwd_bf16_kernel<D, NW, CB, PW, OutT>), dim3((unsigned)(per_xcd * 8)), dim3(NW * 64), 0,
                      stream, p, (int)total, (int)per_xcd);
   return hipGetLastError();
 }
 
+// Each wavefront owns SPLASH_ROW_BLOCKS x 32 query rows of the block.
+#ifndef SPLASH_ROW_BLOCKS
+#define SPLASH_ROW_BLOCKS 1
+#endif
+
 template <int D, bool PW, typename OutT>
 hipError_t launch_bq(const FwdParams& p, hipStream_t stream) {
-  if (p.block_q == 64) return launch_one<D, 1, PW, OutT>(p, stream);
-  return launch_one<D, 2, PW, OutT>(p, stream);
+  constexpr int CB = SPLASH_ROW_BLOCKS;
+  if (p.block_q == 64) return launch_one<D, 2 / CB, CB, PW, OutT>(p, stream);
+  return launch_one<D, 4 / CB, CB, PW, OutT>(p, stream);
 }
 
 template <bool PW, typename OutT>
