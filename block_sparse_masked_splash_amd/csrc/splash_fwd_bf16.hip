@@ -30,10 +30,10 @@
 // accumulator gives P.
 //
 // LDS tiles are row-major (one key per row, head_dim contiguous) with the
-// 16-byte chunks of row r stored at chunk position (chunk ^ (r & 7)), which
-// keeps the K operand reads and the transposing V reads free of bank
-// conflicts; the direct loads write that layout by choosing which global
-// chunk each lane fetches.
+// 16-byte chunks of row r stored at a row-dependent XOR-swizzled position
+// (swz below), which keeps the K operand reads and the transposing V reads
+// free of bank conflicts; the direct loads write that layout by choosing which
+// global chunk each lane fetches.
 //
 // Softmax bookkeeping is in the log2 domain with the scale folded into one
 // FMA before exp2. The reference maximum is only raised when a tile's maximum
@@ -172,6 +172,20 @@ __device__ inline void store4<float>(float* dst, float a, float b, float c, floa
   *reinterpret_cast<f32x4*>(dst) = v;
 }
 
+// LDS chunk position of logical 16-byte chunk c of key row r. The mask mixes
+// row bits so that the 8 keys x 4 chunks touched by one transposing V read
+// land on distinct banks (64 banks of 4 bytes; a 128-dim row spans all of
+// them, a 64-dim row half of them); the K operand reads are conflict-free
+// under any such row-dependent XOR.
+template <int D>
+__device__ constexpr int swz(int c, int r) {
+  if constexpr (D == 128) {
+    return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  } else {
+    return c ^ (((r >> 1) & 1) << 2);
+  }
+}
+
 template <int D, int NW>
 struct Tiling {
   static constexpr int NT = NW * 64;            // threads
@@ -251,33 +265,39 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
   }
 
   // ---- per-lane LDS offsets (swizzled chunk positions) ----
-  // K operand: row 32 kb + l32, chunk 2 s + hh -> position (2 s + hh) ^ (l32 & 7).
+  // K operand: row 32 kb + l32 (32 kb does not change the swizzle), chunk 2 s + hh.
   int koff[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) koff[s] = l32 * T::ROWB + 16 * ((2 * s + hh) ^ (l32 & 7));
+  for (int s = 0; s < NS; ++s) koff[s] = l32 * T::ROWB + 16 * swz<D>(2 * s + hh, l32);
   // V operand (transposing read): lane L reads 4 values of key
-  // kbase + 8 half + 4 hh + ((L % 16) >> 2) at head-dim 32 db + 16 ((L >> 4) & 1) + 4 (L & 3).
-  const int vkey = 4 * hh + ((lane & 15) >> 2);  // key within an 8-key group, also (key & 7)
-  int voff[ND];
+  // 32 kb + 16 g + 8 half + vkey, vkey = 4 hh + ((L % 16) >> 2), at head-dim
+  // 32 db + 16 ((L >> 4) & 1) + 4 (L & 3); 32 kb + 16 g does not change the swizzle.
+  const int vkey = 4 * hh + ((lane & 15) >> 2);
+  int voff[2][ND];
 #pragma unroll
-  for (int db = 0; db < ND; ++db) {
-    const int dcol = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    voff[db] = vkey * T::ROWB + 16 * ((dcol >> 3) ^ vkey) + 2 * (dcol & 7);
-  }
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int dcol = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      const int key = 8 * half + vkey;
+      voff[half][db] = key * T::ROWB + 16 * swz<D>(dcol >> 3, key) + 2 * (dcol & 7);
+    }
 
   // ---- direct HBM -> LDS copy of one K/V tile (plus segment ids) ----
   // Load n of this wave fills rows rb .. rb + RPI - 1 (rb = (n NW + wave) RPI):
-  // lane L writes row rb + L / CPR at chunk position L % CPR, so it fetches
-  // logical chunk (L % CPR) ^ (row & 7). The per-lane part of the byte offset
-  // only depends on the parity of n NW + wave (RPI = 4) or on nothing (RPI = 8).
-  uint32_t kvo[2], vvo[2];
+  // lane L writes row rb + L / CPR at chunk position L % CPR, so it fetches the
+  // logical chunk stored there. The swizzle only sees row & 15, so the per-lane
+  // byte offset only depends on (n NW + wave) & 3.
+  uint32_t kvo[4], vvo[4];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
+  for (int v4 = 0; v4 < 4; ++v4) {
     const int rr = lane / T::CPR;
-    const int r7 = ((T::RPI == 4 ? 4 * par : 0) + rr) & 7;
-    const int chunk = (lane % T::CPR) ^ r7;
-    kvo[par] = (uint32_t)(rr * k_rs + chunk * 16);
-    vvo[par] = (uint32_t)(rr * v_rs + chunk * 16);
+    const int row = v4 * T::RPI + rr;
+    int chunk = 0;
+    for (int cc = 0; cc < T::CPR; ++cc)  // logical chunk at position lane % CPR
+      if (swz<D>(cc, row) == lane % T::CPR) chunk = cc;
+    kvo[v4] = (uint32_t)(rr * k_rs + chunk * 16);
+    vvo[v4] = (uint32_t)(rr * v_rs + chunk * 16);
   }
   auto issue_tile = [&](int stage, int key0) {
     char* kdst = smem + stage * 2 * T::TILE;
@@ -289,8 +309,8 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
     for (int n = 0; n < T::LOADS; ++n) {
       const int blk = n * NW + wave;
       const int rb = blk * T::RPI;
-      lds_copy16(krs, kvo[blk & 1], (uint32_t)(rb * k_rs), lds_addr(kdst + rb * T::ROWB));
-      lds_copy16(vrs, vvo[blk & 1], (uint32_t)(rb * v_rs), lds_addr(vdst + rb * T::ROWB));
+      lds_copy16(krs, kvo[blk & 3], (uint32_t)(rb * k_rs), lds_addr(kdst + rb * T::ROWB));
+      lds_copy16(vrs, vvo[blk & 3], (uint32_t)(rb * v_rs), lds_addr(vdst + rb * T::ROWB));
     }
     if (has_seg) {
       const uint32_t sdst = lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * KC + wave * T::SEG_KEYS);
@@ -444,9 +464,8 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
         const int rowbase = (32 * kb + 16 * g) * T::ROWB;
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vt + rowbase + voff[db]));
-          const i16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vt + rowbase + 8 * T::ROWB + voff[db]));
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vt + rowbase + voff[0][db]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vt + rowbase + voff[1][db]));
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb)
