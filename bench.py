@@ -94,6 +94,27 @@ def cpu_baseline(w, gen, budget_s: float = 12.0):
             "sample": f"{done} query blocks of {bq} rows on random (b, h), fp64 numpy, {dt:.1f} s"}
 
 
+def gemm_reference(dev, n: int = 8192, reps: int = 10) -> float:
+    """TFLOP/s of torch's bf16 GEMM (n x n x n) on N(0, 1) operands on this GPU:
+    what the matrix cores sustain on random data, as context for the roofline
+    fraction (the published peak is not reachable with such operands)."""
+    import torch
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +124,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run N copies of a 1 GiB buffer (counter calibration)")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the dense bf16 GEMM reference measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -194,6 +217,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic_for(w.name), "kernel_source_sha256_16": kernel_source_hash()},
     }
+    if not args.no_gemm_reference and not in_f32:
+        g = gemm_reference(dev)
+        line["bf16_gemm_reference"] = {"tflops": round(g, 1), "what": "torch bf16 GEMM 8192^3 on N(0,1) operands",
+                                       "fwd_fraction_of_it": round(achieved / g, 4)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, gen)
     print(json.dumps(line), flush=True)

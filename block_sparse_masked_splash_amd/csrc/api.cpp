@@ -132,8 +132,9 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
                 "info [%d,%d,%d,%d] but this call needs [%d,%d,%lld,%lld] (segment ids %s)", info->meta_batch,
                 info->meta_heads, info->num_q_blocks, info->num_kv_blocks, seg ? B : 1, mask->num_mask_heads,
                 (long long)nq, (long long)nk, seg ? "given" : "absent");
-  if ((bq != 64 && bq != 128) || (bkv != 64 && bkv != 128))
-    return fail(SPLASH_ERR_UNSUPPORTED, "block sizes %d x %d (supported: 64 or 128 each)", bq, bkv);
+  if ((bq != 64 && bq != 128 && bq != 256) || (bkv != 64 && bkv != 128))
+    return fail(SPLASH_ERR_UNSUPPORTED, "block sizes %d x %d (supported: block_q 64, 128 or 256; block_kv 64 or 128)",
+                bq, bkv);
   if (work && nk > 0 && (info->block_mask == nullptr || info->data_next == nullptr))
     return fail(SPLASH_ERR_INVALID_ARGUMENT, "info arrays are null");
   if (!work) return ok();

@@ -100,16 +100,60 @@ __device__ inline u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
   r[3] = kRawBufferWord3;
   return r;
 }
-__device__ inline void lds_copy16(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
-               "s"(soff), "s"(lds)
-               : "memory", "m0");
-}
 __device__ inline void lds_copy4(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
                "s"(soff), "s"(lds)
                : "memory", "m0");
 }
+// N 16-byte-per-lane copies of row groups: copy n reads at byte offset
+// vo_n + soff0 + n * gstep of the buffer and writes LDS lds0 + n * LSTEP
+// (64 lanes x 16 bytes each). The offsets advance in SGPRs inside one asm
+// block, so no per-copy constant is kept live and no per-copy setup is spent.
+#define SPLASH_COPY1(V)                                         \
+  "s_nop 0\n\t"                                                 \
+  "buffer_load_dwordx4 " V ", %[rs], %[so] offen lds\n\t"       \
+  "s_add_u32 m0, m0, %[ls]\n\t"                                 \
+  "s_add_u32 %[so], %[so], %[gs]\n\t"
+template <int N, int LSTEP>
+__device__ inline void lds_copy_rows(u32x4 rsrc, const uint32_t (&vo)[N], uint32_t soff0, uint32_t gstep,
+                                     uint32_t lds0) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "copy count");
+  uint32_t so = soff0;
+  if constexpr (N == 16) {
+    const uint32_t(&lo)[8] = *reinterpret_cast<const uint32_t(*)[8]>(&vo[0]);
+    const uint32_t(&hi)[8] = *reinterpret_cast<const uint32_t(*)[8]>(&vo[8]);
+    lds_copy_rows<8, LSTEP>(rsrc, lo, soff0, gstep, lds0);
+    lds_copy_rows<8, LSTEP>(rsrc, hi, soff0 + 8 * gstep, gstep, lds0 + 8 * LSTEP);
+  } else if constexpr (N == 1) {
+    asm volatile("s_mov_b32 m0, %[lds]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[v0], %[rs], %[so] offen lds"
+                 : [so] "+s"(so)
+                 : [lds] "s"(lds0), [rs] "s"(rsrc), [v0] "v"(vo[0])
+                 : "memory", "m0");
+  } else if constexpr (N == 2) {
+    asm volatile("s_mov_b32 m0, %[lds]\n\t" SPLASH_COPY1("%[v0]") SPLASH_COPY1("%[v1]")
+                 : [so] "+s"(so)
+                 : [lds] "s"(lds0), [rs] "s"(rsrc), [gs] "s"(gstep), [ls] "i"(LSTEP), [v0] "v"(vo[0]), [v1] "v"(vo[1])
+                 : "memory", "m0", "scc");
+  } else if constexpr (N == 4) {
+    asm volatile("s_mov_b32 m0, %[lds]\n\t" SPLASH_COPY1("%[v0]") SPLASH_COPY1("%[v1]")
+                     SPLASH_COPY1("%[v2]") SPLASH_COPY1("%[v3]")
+                 : [so] "+s"(so)
+                 : [lds] "s"(lds0), [rs] "s"(rsrc), [gs] "s"(gstep), [ls] "i"(LSTEP), [v0] "v"(vo[0]), [v1] "v"(vo[1]), [v2] "v"(vo[2]),
+                   [v3] "v"(vo[3])
+                 : "memory", "m0", "scc");
+  } else {
+    asm volatile("s_mov_b32 m0, %[lds]\n\t" SPLASH_COPY1("%[v0]") SPLASH_COPY1("%[v1]")
+                     SPLASH_COPY1("%[v2]") SPLASH_COPY1("%[v3]")
+                         SPLASH_COPY1("%[v4]") SPLASH_COPY1("%[v5]")
+                             SPLASH_COPY1("%[v6]") SPLASH_COPY1("%[v7]")
+                 : [so] "+s"(so)
+                 : [lds] "s"(lds0), [rs] "s"(rsrc), [gs] "s"(gstep), [ls] "i"(LSTEP), [v0] "v"(vo[0]), [v1] "v"(vo[1]), [v2] "v"(vo[2]),
+                   [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5]), [v6] "v"(vo[6]), [v7] "v"(vo[7])
+                 : "memory", "m0", "scc");
+  }
+}
+#undef SPLASH_COPY1
+
 // LDS byte address of a (wave-uniform) shared-memory pointer, as an SGPR value.
 __device__ inline uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p);
@@ -299,19 +343,23 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
     kvo[v4] = (uint32_t)(rr * k_rs + chunk * 16);
     vvo[v4] = (uint32_t)(rr * v_rs + chunk * 16);
   }
+  // Copy n of this wave covers rows (n NW + wave) RPI .. + RPI - 1.
+  uint32_t kvsel[T::LOADS], vvsel[T::LOADS];
+#pragma unroll
+  for (int n = 0; n < T::LOADS; ++n) {
+    kvsel[n] = kvo[(n * NW + wave) & 3];
+    vvsel[n] = vvo[(n * NW + wave) & 3];
+  }
   auto issue_tile = [&](int stage, int key0) {
     char* kdst = smem + stage * 2 * T::TILE;
     char* vdst = kdst + T::TILE;
     const int rows = p.kv_len - key0 < KC ? p.kv_len - key0 : KC;  // rows past the end read as 0
     const u32x4 krs = buffer_rsrc(kg + key0 * k_rs, (uint32_t)(rows * k_rs));
     const u32x4 vrs = buffer_rsrc(vg + key0 * v_rs, (uint32_t)(rows * v_rs));
-#pragma unroll
-    for (int n = 0; n < T::LOADS; ++n) {
-      const int blk = n * NW + wave;
-      const int rb = blk * T::RPI;
-      lds_copy16(krs, kvo[blk & 3], (uint32_t)(rb * k_rs), lds_addr(kdst + rb * T::ROWB));
-      lds_copy16(vrs, vvo[blk & 3], (uint32_t)(rb * v_rs), lds_addr(vdst + rb * T::ROWB));
-    }
+    lds_copy_rows<T::LOADS, NW * 1024>(krs, kvsel, (uint32_t)(wave * T::RPI * k_rs), (uint32_t)(NW * T::RPI * k_rs),
+                                       lds_addr(kdst + wave * T::RPI * T::ROWB));
+    lds_copy_rows<T::LOADS, NW * 1024>(vrs, vvsel, (uint32_t)(wave * T::RPI * v_rs), (uint32_t)(NW * T::RPI * v_rs),
+                                       lds_addr(vdst + wave * T::RPI * T::ROWB));
     if (has_seg) {
       const uint32_t sdst = lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * KC + wave * T::SEG_KEYS);
       const u32x4 srs = buffer_rsrc(kvseg_g + key0, (uint32_t)(rows * 4));
@@ -362,20 +410,11 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
       nxt_j = next_block(cur_j);
       nxt_t = 0;
     }
-    const bool has_next = nxt_j < p.nk;
-    if (has_next) {
-      issue_tile(stage ^ 1, nxt_j * p.block_kv + nxt_t);
-      // this wave's copies of the current tile are done once at most the
-      // copies of the next tile are still in flight
-      if (has_seg) {
-        wait_vmcnt<2 * T::LOADS + 1>();
-      } else {
-        wait_vmcnt<2 * T::LOADS>();
-      }
-    } else {
-      wait_vmcnt<0>();
-    }
-    barrier_only();  // every wave's copies of the current tile are done
+    wait_vmcnt<0>();  // this wave's copies of the current tile are in LDS
+    // After this barrier every wave's copies of the current tile are in LDS and
+    // every wave is done with the previous tile, whose stage is refilled now.
+    barrier_only();
+    if (nxt_j < p.nk) issue_tile(stage ^ 1, nxt_j * p.block_kv + nxt_t);
 
     const int k0 = cur_j * p.block_kv + cur_t;
     const bool partial = block_class(bmask, cur_j) == 1;
@@ -474,7 +513,6 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
       }
     }
 
-    barrier_only();  // every wave is done reading this stage before it is refilled
     stage ^= 1;
     cur_j = nxt_j;
     cur_t = nxt_t;
@@ -520,6 +558,7 @@ template <int D, bool PW, typename OutT>
 hipError_t launch_bq(const FwdParams& p, hipStream_t stream) {
   constexpr int CB = SPLASH_ROW_BLOCKS;
   if (p.block_q == 64) return launch_one<D, 2 / CB, CB, PW, OutT>(p, stream);
+  if (p.block_q == 256) return launch_one<D, 8 / CB, CB, PW, OutT>(p, stream);
   return launch_one<D, 4 / CB, CB, PW, OutT>(p, stream);
 }
 

@@ -157,8 +157,10 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 template <bool PW>
 hipError_t launch_pw(const FwdParams& p, hipStream_t stream) {
   if (p.head_dim == 64) {
+    if (p.block_q == 256) return launch_one<64, 256, PW>(p, stream);
     return p.block_q == 64 ? launch_one<64, 64, PW>(p, stream) : launch_one<64, 128, PW>(p, stream);
   }
+  if (p.block_q == 256) return launch_one<128, 256, PW>(p, stream);
   return p.block_q == 64 ? launch_one<128, 64, PW>(p, stream) : launch_one<128, 128, PW>(p, stream);
 }
 

@@ -135,7 +135,7 @@ splash_status splash_mask_info_build(int B, int H, int q_len, int kv_len, int bl
  * start 16-byte aligned (base pointers and strides accordingly).
  *
  * Supported: in_dtype/out_dtype F32/F32, BF16/BF16 or BF16/F32; head_dim 64 or
- * 128; block_q and block_kv in {64, 128}. Arithmetic: F32 inputs are computed
+ * 128; block_q in {64, 128, 256} and block_kv in {64, 128}. Arithmetic: F32 inputs are computed
  * in fp32; BF16 inputs use bf16 matrix cores with fp32 accumulation and fp32
  * softmax statistics, and the probabilities are rounded to bf16 for P·V.
  * `info` must have been built for the same B, H, lengths, block sizes, mask

@@ -129,6 +129,9 @@ FWD_CASES = [
     (1, 2, 100, 300, 128, [FULL, CAUSAL], 64, 64, None, "bf16"),
     (2, 2, 190, 190, 128, [CAUSAL, wl.local_causal(33)], 128, 64, "docs", "f32"),
     (1, 3, 130, 257, 64, [FULL, (1, 7, 7), (0, 0, 0)], 64, 128, None, "f32"),
+    (2, 2, 600, 600, 128, [CAUSAL, wl.local_causal(100)], 256, 128, "docs", "bf16"),
+    (1, 2, 300, 333, 64, [FULL, CAUSAL], 256, 64, None, "bf16"),
+    (1, 2, 280, 280, 64, [CAUSAL, (0, 50, 20)], 256, 64, "random", "f32"),
 ]
 
 
@@ -298,7 +301,7 @@ def test_tile_size_invariance(gpu_device):
     c = wl.random_case(9, B, H, S, S, D, "bf16")
     g = _to_dev(c, gpu_device)
     outs = []
-    for bq, bkv in ((64, 64), (128, 128), (64, 128), (128, 64)):
+    for bq, bkv in ((64, 64), (128, 128), (64, 128), (128, 64), (256, 128), (256, 64)):
         info = sp.mask_info_build(B, H, S, S, [CAUSAL], bq, bkv, device=gpu_device)
         outs.append(to64(sp.splash_fwd(g["q"], g["k"], g["v"], info, out_dtype=torch.float32)))
     for o in outs[1:]:
@@ -315,6 +318,26 @@ def test_large_scores_stay_finite(gpu_device):
     torch.cuda.synchronize()
     ref = oracle.softmax_attention(to64(c["q"]), to64(c["k"]), to64(c["v"]), D ** -0.5, [CAUSAL])
     check_close(to64(out), ref, "bf16", "q*30")
+
+
+@pytest.mark.parametrize("bq,bkv", [(128, 128), (64, 64), (256, 128)])
+def test_rising_scores_rescale(gpu_device, bq, bkv):
+    """Scores that grow along the key axis by hundreds of units, so the running
+    maximum of a row keeps rising block after block and the accumulated
+    numerator and denominator must be rescaled many times (page 3, section 15:
+    the correction factor applied to l and O when m increases)."""
+    B, H, S, D = 1, 2, 640, 128
+    c = wl.random_case(11, B, H, S, S, D, "bf16", sigma=0.1)
+    ramp = torch.linspace(0.0, 30.0, S).view(1, 1, S, 1)
+    c["q"] = (c["q"].float() + 1.0).to(torch.bfloat16)
+    c["k"] = (c["k"].float() + ramp).to(torch.bfloat16)
+    c["v"] = wl.random_case(12, B, H, S, S, D, "bf16")["v"]
+    g = _to_dev(c, gpu_device)
+    info = sp.mask_info_build(B, H, S, S, [CAUSAL], bq, bkv, device=gpu_device)
+    out = sp.splash_fwd(g["q"], g["k"], g["v"], info)
+    torch.cuda.synchronize()
+    ref = oracle.softmax_attention(to64(c["q"]), to64(c["k"]), to64(c["v"]), D ** -0.5, [CAUSAL])
+    check_close(to64(out), ref, "bf16", f"rising scores {bq}x{bkv}")
 
 
 def test_metadata_mismatch_raises(gpu_device):
