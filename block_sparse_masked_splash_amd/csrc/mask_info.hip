@@ -10,63 +10,106 @@
 // Classes: 0 = no allowed pair, 2 = every pair of the (bq x bkv) block allowed,
 // 1 otherwise; pairs past the sequence ends count as not allowed.
 //
-// One wavefront per metadata row (bm, hm, i). The row is walked back to front
-// in chunks of 64 kv blocks: each lane classifies one block, a ballot marks
-// the non-empty ones, and each lane's data_next is the lowest marked block at
-// or after it, else the carry from the chunks already done.
+// The causal / window part of a head's mask is a band k - q in [lo, hi] with
+// lo <= 0 <= hi, so its class has a closed form per block. Segment ids are
+// arbitrary integers: where they are given, every block the band leaves
+// non-empty is classified by one workgroup that compares all its pairs.
+// data_next is then a suffix scan of each metadata row, one wavefront per
+// row: the row is walked back to front in chunks of 64 kv blocks, a ballot
+// marks the non-empty ones, and each lane takes the lowest marked block at or
+// after it, else the carry from the chunks already done.
 
 #include "internal.h"
 
 namespace splash {
 namespace {
 
-__device__ inline int64_t clamp_count(int64_t lo, int64_t hi) { return hi >= lo ? hi - lo + 1 : 0; }
+struct BlockSpan {
+  int64_t q0, q1;  // first and last valid query of the block
+  int64_t k0, k1;  // first and last valid key
+  bool ragged;     // the block reaches past a sequence end
+};
 
-// Class of block (i, j) for head band `hb`, batch row b (segments only).
-__device__ int classify(const MaskInfoParams& p, HeadBand hb, int b, int i, int j) {
-  const int64_t q_begin = (int64_t)i * p.block_q;
-  const int64_t k_begin = (int64_t)j * p.block_kv;
-  const int64_t k_end = k_begin + p.block_kv - 1;               // inclusive
-  const int64_t k_last = k_end < p.kv_len - 1 ? k_end : (int64_t)p.kv_len - 1;
-  bool any_in = false;
-  bool any_out = (q_begin + p.block_q > p.q_len) || (k_end >= p.kv_len);
-  for (int r = 0; r < p.block_q; ++r) {
-    const int64_t q = q_begin + r;
-    if (q >= p.q_len) break;
-    int64_t a = q + hb.lo;
-    int64_t z = q + hb.hi;
-    if (a < k_begin) a = k_begin;
-    if (z > k_last) z = k_last;
-    const int64_t n = clamp_count(a, z);
-    if (n < p.block_kv) any_out = true;
-    if (n == 0) {
-      if (any_in && any_out) return 1;
-      continue;
-    }
-    if (p.q_seg == nullptr) {
-      any_in = true;
-    } else {
-      const int32_t qs = p.q_seg[(int64_t)b * p.q_len + q];
-      const int32_t* ks = p.kv_seg + (int64_t)b * p.kv_len;
-      for (int64_t k = a; k <= z; ++k) {
-        if (ks[k] == qs) any_in = true; else any_out = true;
-        if (any_in && any_out) return 1;
-      }
-    }
-    if (any_in && any_out) return 1;
-  }
-  if (!any_in) return 0;
-  return any_out ? 1 : 2;
+__device__ inline BlockSpan block_span(const MaskInfoParams& p, int i, int j) {
+  BlockSpan s;
+  s.q0 = (int64_t)i * p.block_q;
+  s.k0 = (int64_t)j * p.block_kv;
+  const int64_t qe = s.q0 + p.block_q, ke = s.k0 + p.block_kv;
+  s.q1 = (qe < p.q_len ? qe : (int64_t)p.q_len) - 1;
+  s.k1 = (ke < p.kv_len ? ke : (int64_t)p.kv_len) - 1;
+  s.ragged = qe > p.q_len || ke > p.kv_len;
+  return s;
 }
 
-__global__ __launch_bounds__(256) void mask_info_kernel(MaskInfoParams p) {
+// Class of a block under the band alone. Some query q of the block sees a key
+// of the block iff q + lo <= k1 and q + hi >= k0 for a q in [q0, q1]; every
+// pair is allowed iff the band of the last query starts at or before k0 and
+// the band of the first query ends at or after k1 (and nothing is ragged).
+__device__ inline int band_class(const BlockSpan& s, HeadBand hb) {
+  const int64_t qa = s.q0 > s.k0 - hb.hi ? s.q0 : s.k0 - hb.hi;
+  const int64_t qb = s.q1 < s.k1 - hb.lo ? s.q1 : s.k1 - hb.lo;
+  if (qa > qb) return 0;
+  const bool full = !s.ragged && s.q1 + hb.lo <= s.k0 && s.q0 + hb.hi >= s.k1;
+  return full ? 2 : 1;
+}
+
+__device__ inline void decode_row(const MaskInfoParams& p, int64_t row, int& bm, int& hm, int& i) {
+  i = (int)(row % p.nq);
+  hm = (int)((row / p.nq) % p.meta_heads);
+  bm = (int)(row / ((int64_t)p.nq * p.meta_heads));
+}
+
+// Segment path: one workgroup per metadata entry (grid-stride over entries).
+constexpr int kSegThreads = 256;
+
+__global__ __launch_bounds__(kSegThreads) void segment_class_kernel(MaskInfoParams p, int64_t entries) {
+  __shared__ int32_t qs[1024];
+  __shared__ int32_t ks[1024];
+  const int t = threadIdx.x;
+  for (int64_t e = blockIdx.x; e < entries; e += gridDim.x) {
+    const int64_t row = e / p.nk;
+    const int j = (int)(e - row * p.nk);
+    int bm, hm, i;
+    decode_row(p, row, bm, hm, i);
+    const HeadBand hb = p.band[hm];
+    const BlockSpan s = block_span(p, i, j);
+    const int base = band_class(s, hb);
+    if (base == 0) {
+      if (t == 0) p.block_mask[e] = 0;
+      continue;
+    }
+    const int nvq = (int)(s.q1 - s.q0 + 1), nvk = (int)(s.k1 - s.k0 + 1);
+    const int32_t* qrow = p.q_seg + (int64_t)bm * p.q_len + s.q0;
+    const int32_t* krow = p.kv_seg + (int64_t)bm * p.kv_len + s.k0;
+    __syncthreads();  // the previous entry's readers are done with qs / ks
+    for (int r = t; r < nvq; r += kSegThreads) qs[r] = qrow[r];
+    for (int c = t; c < nvk; c += kSegThreads) ks[c] = krow[c];
+    __syncthreads();
+    int any_in = 0, any_out = 0;
+    const int pairs = nvq * nvk;
+    for (int x = t; x < pairs; x += kSegThreads) {
+      const int r = x / nvk, c = x - r * nvk;
+      const int64_t d = (s.k0 + c) - (s.q0 + r);  // k - q
+      const bool allowed = d >= hb.lo && d <= hb.hi && qs[r] == ks[c];
+      any_in |= allowed;
+      any_out |= !allowed;
+    }
+    any_in = __syncthreads_or(any_in);
+    any_out = __syncthreads_or(any_out);
+    if (t == 0) p.block_mask[e] = (int8_t)(!any_in ? 0 : (any_out || base == 1 ? 1 : 2));
+  }
+}
+
+// One wavefront per metadata row: classes (closed form, or read back from the
+// segment pass) and the data_next suffix scan.
+template <bool kFromSegments>
+__global__ __launch_bounds__(256) void row_scan_kernel(MaskInfoParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t rows = (int64_t)p.meta_batch * p.meta_heads * p.nq;
   if (row >= rows) return;
-  const int i = (int)(row % p.nq);
-  const int hm = (int)((row / p.nq) % p.meta_heads);
-  const int bm = (int)(row / ((int64_t)p.nq * p.meta_heads));
+  int bm, hm, i;
+  decode_row(p, row, bm, hm, i);
   const HeadBand hb = p.band[hm];
   int8_t* bmask = p.block_mask + row * p.nk;
   int32_t* dnext = p.data_next + row * p.nk;
@@ -76,8 +119,12 @@ __global__ __launch_bounds__(256) void mask_info_kernel(MaskInfoParams p) {
     const int j = c * 64 + lane;
     int cls = 0;
     if (j < p.nk) {
-      cls = classify(p, hb, bm, i, j);
-      bmask[j] = (int8_t)cls;
+      if constexpr (kFromSegments) {
+        cls = bmask[j];
+      } else {
+        cls = band_class(block_span(p, i, j), hb);
+        bmask[j] = (int8_t)cls;
+      }
     }
     const uint64_t bits = __ballot(cls != 0);
     const uint64_t at_or_after = bits >> lane;
@@ -92,7 +139,16 @@ hipError_t launch_mask_info(const MaskInfoParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.meta_batch * p.meta_heads * p.nq;
   if (rows == 0 || p.nk == 0) return hipSuccess;
   const int64_t blocks = (rows + 3) / 4;
-  hipLaunchKernelGGL(mask_info_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  if (p.q_seg != nullptr) {
+    const int64_t entries = rows * p.nk;
+    const int64_t grid = entries < (1 << 20) ? entries : (1 << 20);
+    hipLaunchKernelGGL(segment_class_kernel, dim3((unsigned)grid), dim3(kSegThreads), 0, stream, p, entries);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(row_scan_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(row_scan_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
