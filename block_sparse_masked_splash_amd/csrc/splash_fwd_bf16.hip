@@ -42,6 +42,8 @@
 // is practically never needed, and the result is unchanged because O and L
 // always share one reference.
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace splash {
@@ -52,6 +54,11 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+struct bf16x2x4 {
+  bf16x2 v[4];
+};
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
@@ -303,7 +310,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
       i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
       if (valid) v = *reinterpret_cast<const i16x8*>(qg + (int64_t)qrow[cb] * p.q_ss + 16 * s + 8 * hh);
       if (negate_q) v ^= (short)0x8000;
-      qreg[cb][s] = to_agpr(__builtin_bit_cast(bf16x8, v));
+      qreg[cb][s] = __builtin_bit_cast(bf16x8, v);
     }
     myseg[cb] = (has_seg && valid) ? p.q_seg[(int64_t)b * p.q_len + qrow[cb]] : 0;
   }
@@ -401,10 +408,13 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
   int cur_j = p.nk > 0 ? scalar_load_i32(dnext) : p.nk;
   if (cur_j < 0 || cur_j > p.nk) cur_j = p.nk;
   int cur_t = 0;
-  int stage = 0;
   if (cur_j < p.nk) issue_tile(0, cur_j * p.block_kv);
 
-  while (cur_j < p.nk) {
+  // One tile in LDS stage STAGE (a compile-time constant, so every tile
+  // address is a per-lane offset plus an immediate). Returns whether another
+  // tile follows.
+  auto step = [&](auto stage_tag) -> bool {
+    constexpr int stage = decltype(stage_tag)::value;
     int nxt_j = cur_j, nxt_t = cur_t + KC;
     if (nxt_t >= p.block_kv || cur_j * p.block_kv + nxt_t >= p.kv_len) {
       nxt_j = next_block(cur_j);
@@ -441,19 +451,30 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
 
       // sacc[cb][r] is the score of key k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4
       // against query qrow[cb].
-      if (partial) {
+      // Element mask, only on blocks of class 1. The tests are combined with
+      // bitwise operators so the whole mask is straight-line code.
+      auto apply_mask = [&](auto seg_tag) {
+        constexpr bool kSeg = decltype(seg_tag)::value;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
           const int key = k0 + kl;
-          const int kseg = sseg[kl];
+          int kseg = 0;
+          if constexpr (kSeg) kseg = sseg[kl];
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
             const int dlt = key - qrow[cb];
-            const bool ok = key < p.kv_len && dlt >= band.lo && dlt <= band.hi && (!has_seg || kseg == myseg[cb]);
-            if (!ok) sacc[cb][r] = PW ? 0.0f : kNegInf;
+            bool ok = (key < p.kv_len) & (dlt >= band.lo) & (dlt <= band.hi);
+            if constexpr (kSeg) ok &= kseg == myseg[cb];
+            sacc[cb][r] = ok ? sacc[cb][r] : (PW ? 0.0f : kNegInf);
           }
         }
+      };
+      if (partial) {
+        if (has_seg)
+          apply_mask(std::true_type{});
+        else
+          apply_mask(std::false_type{});
       }
 
       bf16x8 pb[2][CB];  // [g][cb]: B operand of Oᵀ += Vᵀ Pᵀ for keys 32 kb + 16 g + ...
@@ -476,14 +497,15 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
           }
           // rows with nothing allowed yet keep mref = -inf; all their entries are -inf here
           const float mneg = mref[cb] == kNegInf ? 0.0f : -mref[cb];
-          float rs = 0.0f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = fast_exp2(__builtin_fmaf(sacc[cb][r], c, mneg));
-            rs += e;
-            pb[r >> 3][cb][r & 7] = (__bf16)e;
+          for (int r = 0; r < 16; ++r) pb[r >> 3][cb][r & 7] = (__bf16)fast_exp2(__builtin_fmaf(sacc[cb][r], c, mneg));
+          // L sums the probabilities as rounded for P V, two per dot instruction
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const bf16x2x4 pr = __builtin_bit_cast(bf16x2x4, pb[g][cb]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) lsum[cb] = __builtin_amdgcn_fdot2_f32_bf16(pr.v[u], kOnes2, lsum[cb], false);
           }
-          lsum[cb] += rs;
         }
       } else {
         const float cneg = -c * kLog2e;
@@ -513,9 +535,13 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
       }
     }
 
-    stage ^= 1;
     cur_j = nxt_j;
     cur_t = nxt_t;
+    return cur_j < p.nk;
+  };
+  while (cur_j < p.nk) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
   }
 
 #pragma unroll
