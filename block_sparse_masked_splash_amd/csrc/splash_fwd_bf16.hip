@@ -255,21 +255,33 @@ struct Tiling {
 
 template <int D, int NW, int CB, bool PW, typename OutT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CB == 1 ? 2 : 1, CB == 1 ? 2 : 1)))
-void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd) {
+void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int heads_interleaved) {
   using T = Tiling<D, NW>;
   constexpr int NS = T::NS;
   constexpr int ND = T::ND;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
   // XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
-  // id -> (id % 8, id / 8) gives each XCD a contiguous range of logical work,
-  // which runs query blocks of the same (b, h) next to each other (K and V
-  // of that head stay in the XCD's L2). Within a head the heaviest query
-  // blocks (most kv blocks under causal masks) go first.
-  const int wid = (int)(blockIdx.x & 7) * work_per_xcd + (int)(blockIdx.x >> 3);
-  if (wid >= total_work) return;
-  const int bh = wid / p.nq;
-  const int i = p.nq - 1 - (wid - bh * p.nq);
+  // id -> (x, k) = (id % 8, id / 8) is the k-th workgroup XCD x runs. Each
+  // XCD works through whole (b, h) heads one after the other, so K and V of
+  // the head in flight stay in that XCD's L2, and within a head the heaviest
+  // query blocks (most kv blocks under causal masks) go first. When the
+  // number of heads is a multiple of 8, XCD x takes heads x, x + 8, ...:
+  // heads with different masks (say causal and local ones side by side) are
+  // then spread evenly over the XCDs. Otherwise each XCD takes a contiguous
+  // eighth of the (head, query block) list.
+  const int xcd = (int)(blockIdx.x & 7), k_in_xcd = (int)(blockIdx.x >> 3);
+  int bh, i;
+  if (heads_interleaved) {
+    const int hk = k_in_xcd / p.nq;
+    bh = xcd + 8 * hk;
+    i = p.nq - 1 - (k_in_xcd - hk * p.nq);
+  } else {
+    const int wid = xcd * work_per_xcd + k_in_xcd;
+    if (wid >= total_work) return;
+    bh = wid / p.nq;
+    i = p.nq - 1 - (wid - bh * p.nq);
+  }
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int hm = p.meta_heads == 1 ? 0 : h;
@@ -570,8 +582,9 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   const int64_t total = (int64_t)p.nq * p.B * p.H;
   if (total == 0) return hipSuccess;
   const int64_t per_xcd = (total + 7) / 8;
+  const int interleaved = (p.B * p.H) % 8 == 0 ? 1 : 0;  // then total == 8 * per_xcd
   hipLaunchKernelGGL((splash_fwd_bf16_kernel<D, NW, CB, PW, OutT>), dim3((unsigned)(per_xcd * 8)), dim3(NW * 64), 0,
-                     stream, p, (int)total, (int)per_xcd);
+                     stream, p, (int)total, (int)per_xcd, interleaved);
   return hipGetLastError();
 }
 
