@@ -253,8 +253,16 @@ struct Tiling {
   static constexpr int LDS_BYTES = SEG_OFF + 2 * KC * 4;
 };
 
+// Wavefronts per SIMD: at D = 128 a wavefront needs over 128 VGPRs, so two;
+// at D = 64 four fit, and the extra wavefronts hide the longer vector work
+// (per key, the pointwise variant spends two transcendentals on half as many
+// matrix FLOPs).
+#ifndef SPLASH_WAVES_D64
+#define SPLASH_WAVES_D64 4
+#endif
 template <int D, int NW, int CB, bool PW, typename OutT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CB == 1 ? 2 : 1, CB == 1 ? 2 : 1)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CB == 1 ? (D == 64 ? SPLASH_WAVES_D64 : 2) : 1,
+                                                                      CB == 1 ? (D == 64 ? SPLASH_WAVES_D64 : 2) : 1)))
 void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int heads_interleaved) {
   using T = Tiling<D, NW>;
   constexpr int NS = T::NS;
@@ -525,9 +533,11 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
+            // silu(c s) / q_len = (c / q_len) * s * sigmoid(c s): the constant
+            // factor is applied once to O at the end
             const float sv = sacc[cb][r];
             const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(sv * cneg));
-            pb[r >> 3][cb][r & 7] = (__bf16)(sv * c * sg * p.inv_q_len);
+            pb[r >> 3][cb][r & 7] = (__bf16)(sv * sg);
           }
       }
 
@@ -558,7 +568,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
 
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    float inv = 1.0f;
+    float inv = c * p.inv_q_len;  // pointwise: the factor left out of P
     if constexpr (!PW) {
       const float l = sum_xor32(lsum[cb]);
       inv = l > 0.0f ? 1.0f / l : 0.0f;
