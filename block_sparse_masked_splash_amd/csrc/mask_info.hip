@@ -13,7 +13,8 @@
 // The causal / window part of a head's mask is a band k - q in [lo, hi] with
 // lo <= 0 <= hi, so its class has a closed form per block. Segment ids are
 // arbitrary integers: where they are given, every block the band leaves
-// non-empty is classified by one workgroup that compares all its pairs.
+// non-empty is classified by one workgroup, from the id ranges when they
+// decide it, else by comparing all its pairs.
 // data_next is then a suffix scan of each metadata row, one wavefront per
 // row: the row is walked back to front in chunks of 64 kv blocks, a ballot
 // marks the non-empty ones, and each lane takes the lowest marked block at or
@@ -60,12 +61,34 @@ __device__ inline void decode_row(const MaskInfoParams& p, int64_t row, int& bm,
 }
 
 // Segment path: one workgroup per metadata entry (grid-stride over entries).
+// The id ranges of the block's queries and keys decide most blocks without a
+// pair test: disjoint ranges share no id (class 0), and a single common id
+// leaves the band to decide. Otherwise every pair is tested.
 constexpr int kSegThreads = 256;
+
+__device__ inline int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int w = __shfl_xor(v, o, 64);
+    v = w < v ? w : v;
+  }
+  return v;
+}
+__device__ inline int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
+  }
+  return v;
+}
 
 __global__ __launch_bounds__(kSegThreads) void segment_class_kernel(MaskInfoParams p, int64_t entries) {
   __shared__ int32_t qs[1024];
   __shared__ int32_t ks[1024];
+  __shared__ int32_t red[4][kSegThreads / 64];  // per wave: q min, q max, k min, k max
   const int t = threadIdx.x;
+  const int wv = t >> 6;
   for (int64_t e = blockIdx.x; e < entries; e += gridDim.x) {
     const int64_t row = e / p.nk;
     const int j = (int)(e - row * p.nk);
@@ -81,18 +104,64 @@ __global__ __launch_bounds__(kSegThreads) void segment_class_kernel(MaskInfoPara
     const int nvq = (int)(s.q1 - s.q0 + 1), nvk = (int)(s.k1 - s.k0 + 1);
     const int32_t* qrow = p.q_seg + (int64_t)bm * p.q_len + s.q0;
     const int32_t* krow = p.kv_seg + (int64_t)bm * p.kv_len + s.k0;
-    __syncthreads();  // the previous entry's readers are done with qs / ks
-    for (int r = t; r < nvq; r += kSegThreads) qs[r] = qrow[r];
-    for (int c = t; c < nvk; c += kSegThreads) ks[c] = krow[c];
+    __syncthreads();  // the previous entry's readers are done with qs, ks and red
+    int qmin = 0x7fffffff, qmax = (int)0x80000000, kmin = 0x7fffffff, kmax = (int)0x80000000;
+    for (int r = t; r < nvq; r += kSegThreads) {
+      const int v = qrow[r];
+      qs[r] = v;
+      qmin = v < qmin ? v : qmin;
+      qmax = v > qmax ? v : qmax;
+    }
+    for (int c = t; c < nvk; c += kSegThreads) {
+      const int v = krow[c];
+      ks[c] = v;
+      kmin = v < kmin ? v : kmin;
+      kmax = v > kmax ? v : kmax;
+    }
+    qmin = wave_min(qmin);
+    qmax = wave_max(qmax);
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    if ((t & 63) == 0) {
+      red[0][wv] = qmin;
+      red[1][wv] = qmax;
+      red[2][wv] = kmin;
+      red[3][wv] = kmax;
+    }
     __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kSegThreads / 64; ++w) {
+      qmin = red[0][w] < qmin ? red[0][w] : qmin;
+      qmax = red[1][w] > qmax ? red[1][w] : qmax;
+      kmin = red[2][w] < kmin ? red[2][w] : kmin;
+      kmax = red[3][w] > kmax ? red[3][w] : kmax;
+    }
+    if (qmax < kmin || kmax < qmin) {  // no id in common
+      if (t == 0) p.block_mask[e] = 0;
+      continue;
+    }
+    if (qmin == qmax && kmin == kmax) {  // one id on both sides
+      if (t == 0) p.block_mask[e] = (int8_t)base;
+      continue;
+    }
+    // Pair test, in chunks of up to 256 key columns: thread t takes column
+    // t % span of the chunk and every (256 / span)-th row.
     int any_in = 0, any_out = 0;
-    const int pairs = nvq * nvk;
-    for (int x = t; x < pairs; x += kSegThreads) {
-      const int r = x / nvk, c = x - r * nvk;
-      const int64_t d = (s.k0 + c) - (s.q0 + r);  // k - q
-      const bool allowed = d >= hb.lo && d <= hb.hi && qs[r] == ks[c];
-      any_in |= allowed;
-      any_out |= !allowed;
+    for (int c0 = 0; c0 < nvk; c0 += kSegThreads) {
+      const int span = nvk - c0 < kSegThreads ? nvk - c0 : kSegThreads;
+      const int rstep = kSegThreads / span;
+      const int r0 = t / span;
+      if (r0 < rstep) {
+        const int c = c0 + (t - r0 * span);
+        const int32_t kid = ks[c];
+        const int64_t d0 = (s.k0 + c) - s.q0;  // k - q at row 0
+        for (int r = r0; r < nvq; r += rstep) {
+          const int64_t d = d0 - r;
+          const bool allowed = d >= hb.lo && d <= hb.hi && qs[r] == kid;
+          any_in |= allowed;
+          any_out |= !allowed;
+        }
+      }
     }
     any_in = __syncthreads_or(any_in);
     any_out = __syncthreads_or(any_out);

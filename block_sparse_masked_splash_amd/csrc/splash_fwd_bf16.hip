@@ -473,19 +473,30 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
       // against query qrow[cb].
       // Element mask, only on blocks of class 1. The tests are combined with
       // bitwise operators so the whole mask is straight-line code.
+      // The band and the sequence end leave row q one run of keys [a, b] of
+      // the tile (offsets from k0), tested per score as one unsigned compare.
       auto apply_mask = [&](auto seg_tag) {
         constexpr bool kSeg = decltype(seg_tag)::value;
+        int4 kseg4[4];
+        if constexpr (kSeg) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kl = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const int key = k0 + kl;
-          int kseg = 0;
-          if constexpr (kSeg) kseg = sseg[kl];
+          for (int u = 0; u < 4; ++u) kseg4[u] = *reinterpret_cast<const int4*>(sseg + 32 * kb + 8 * u + 4 * hh);
+        }
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            const int dlt = key - qrow[cb];
-            bool ok = (key < p.kv_len) & (dlt >= band.lo) & (dlt <= band.hi);
-            if constexpr (kSeg) ok &= kseg == myseg[cb];
+        for (int cb = 0; cb < CB; ++cb) {
+          int a = qrow[cb] + band.lo - k0;
+          int e = qrow[cb] + band.hi - k0;
+          a = a > 0 ? a : 0;
+          e = e < p.kv_len - 1 - k0 ? e : p.kv_len - 1 - k0;
+          e = e < KC - 1 ? e : KC - 1;
+          if (e < a) a = e = KC;  // no key of the tile
+          const uint32_t width = (uint32_t)(e - a);
+          const int base = 4 * hh - a;  // offset of element r minus a, up to a constant of r
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kc = 32 * kb + 8 * (r >> 2) + (r & 3);
+            bool ok = (uint32_t)(base + kc) <= width;
+            if constexpr (kSeg) ok &= kseg4[r >> 2][r & 3] == myseg[cb];
             sacc[cb][r] = ok ? sacc[cb][r] : (PW ? 0.0f : kNegInf);
           }
         }
