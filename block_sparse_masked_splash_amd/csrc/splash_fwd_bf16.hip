@@ -68,6 +68,9 @@ constexpr int KC = 64;                 // keys per LDS tile
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 32.0f;  // log2 units a tile max may exceed the reference by
+// A lane's sum of 16 probabilities above this means some score rose over 40
+// log2 units above the reference (and a NaN or inf sum fails the test too).
+constexpr float kFastLimit = 1099511627776.0f;  // 2^40
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // {x, x of lane ^ 32}: the gfx950 half-wave swap returns both halves' values
@@ -510,33 +513,46 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
 
       bf16x8 pb[2][CB];  // [g][cb]: B operand of Oᵀ += Vᵀ Pᵀ for keys 32 kb + 16 g + ...
       if constexpr (!PW) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          float mx = kNegInf;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[cb][r]);
-          mx = max_xor32(mx) * c;  // max of these 32 keys, log2 domain (-inf if none allowed)
-          const bool raise = mx > mref[cb] + kRescaleSlack;
-          if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-            const float alpha = raise ? fast_exp2(mref[cb] - mx) : 1.0f;
-            mref[cb] = raise ? mx : mref[cb];
-            lsum[cb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < ND; ++db)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) oacc[cb][db][r] *= alpha;
-          }
-          // rows with nothing allowed yet keep mref = -inf; all their entries are -inf here
-          const float mneg = mref[cb] == kNegInf ? 0.0f : -mref[cb];
+        // Probabilities on the row's current reference, with no max: the sum
+        // of the lane's 16 rounded probabilities (needed for L anyway, two per
+        // dot instruction) shows whether some score rose more than
+        // kFastLimitLog2 above the reference. Only then, or while a row has
+        // no reference yet, does the wavefront take the reference-raising path.
+        auto probs = [&](int cb, float mneg) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) pb[r >> 3][cb][r & 7] = (__bf16)fast_exp2(__builtin_fmaf(sacc[cb][r], c, mneg));
-          // L sums the probabilities as rounded for P V, two per dot instruction
+          float rs = 0.0f;
 #pragma unroll
           for (int g = 0; g < 2; ++g) {
             const bf16x2x4 pr = __builtin_bit_cast(bf16x2x4, pb[g][cb]);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) lsum[cb] = __builtin_amdgcn_fdot2_f32_bf16(pr.v[u], kOnes2, lsum[cb], false);
+            for (int u = 0; u < 4; ++u) rs = __builtin_amdgcn_fdot2_f32_bf16(pr.v[u], kOnes2, rs, false);
           }
+          return rs;
+        };
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          float rs = probs(cb, -mref[cb]);
+          const bool fast = (mref[cb] != kNegInf) & (rs <= kFastLimit);  // false for NaN / inf too
+          if (__builtin_amdgcn_ballot_w64(!fast) != 0) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[cb][r]);
+            mx = max_xor32(mx) * c;  // max of these 32 keys, log2 domain (-inf if none allowed)
+            const bool raise = mx > mref[cb] + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+              const float alpha = raise ? fast_exp2(mref[cb] - mx) : 1.0f;
+              mref[cb] = raise ? mx : mref[cb];
+              lsum[cb] *= alpha;
+#pragma unroll
+              for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[cb][db][r] *= alpha;
+            }
+            // rows with nothing allowed yet keep mref = -inf; all their entries are -inf here
+            rs = probs(cb, mref[cb] == kNegInf ? 0.0f : -mref[cb]);
+          }
+          lsum[cb] += rs;
         }
       } else {
         const float cneg = -c * kLog2e;
