@@ -12,12 +12,11 @@
 //       pointwise: P = silu(S) / q_len (masked -> 0), O = O + P V_j
 //     O_i = O / L (softmax; 0 where L = 0) or O (pointwise)
 //
-// Work decomposition: one workgroup per (b, h, q block) with NW = block_q / 64
-// wavefronts; each wavefront owns 64 query rows as two 32-row column blocks,
-// so every K or V operand read from LDS feeds two matrix instructions. The kv
-// axis is walked in tiles of 64 keys: K and V tiles are copied HBM -> LDS by
-// direct (VGPR-free) 16-byte-per-lane loads, double-buffered so the copy of
-// tile t+1 runs under the math of tile t.
+// Work decomposition: one workgroup per (b, h, q block) with NW = block_q / 32
+// wavefronts; each wavefront owns 32 query rows. The kv axis is walked in
+// tiles of KC keys (32 or 64): K and V tiles are copied HBM -> LDS by direct (VGPR-free)
+// 16-byte-per-lane loads, double-buffered so the copy of tile t+1 runs under
+// the math of tile t.
 //
 // Matrix-core layout: scores are formed transposed, Sᵀ = K Qᵀ, with
 // v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Qᵀ held in registers for
@@ -36,11 +35,16 @@
 // global chunk each lane fetches.
 //
 // Softmax bookkeeping is in the log2 domain with the scale folded into one
-// FMA before exp2. The reference maximum is only raised when a tile's maximum
-// exceeds it by more than 32 (probabilities stay below 2^32, far from the
-// fp32/bf16 range limit): after the first tile of a row the rescale of O and L
-// is practically never needed, and the result is unchanged because O and L
-// always share one reference.
+// FMA before exp2, against a per-row reference m that O and L always share
+// (so the result is the plain softmax whatever m is). Probabilities are first
+// formed on the current m without computing a max; only when their sum shows
+// a score more than 40 log2 units above m (or the row has no m yet) is the
+// 32-key max taken and m raised, if that max exceeds m by more than 32, with
+// O and L rescaled. Probabilities thus stay below 2^40, far from the
+// fp32/bf16 range limit, and the max is computed about once per row.
+//
+// Pointwise: P = s sigmoid(c s) with the constant c / q_len applied to O once
+// at the end.
 
 #include <type_traits>
 
@@ -64,7 +68,6 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
 typedef __attribute__((address_space(1))) void* global_void_ptr;
 
-constexpr int KC = 64;                 // keys per LDS tile
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 32.0f;  // log2 units a tile max may exceed the reference by
@@ -127,14 +130,9 @@ __device__ inline void lds_copy4(u32x4 rsrc, uint32_t voff, uint32_t soff, uint3
 template <int N, int LSTEP>
 __device__ inline void lds_copy_rows(u32x4 rsrc, const uint32_t (&vo)[N], uint32_t soff0, uint32_t gstep,
                                      uint32_t lds0) {
-  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "copy count");
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "copy count");
   uint32_t so = soff0;
-  if constexpr (N == 16) {
-    const uint32_t(&lo)[8] = *reinterpret_cast<const uint32_t(*)[8]>(&vo[0]);
-    const uint32_t(&hi)[8] = *reinterpret_cast<const uint32_t(*)[8]>(&vo[8]);
-    lds_copy_rows<8, LSTEP>(rsrc, lo, soff0, gstep, lds0);
-    lds_copy_rows<8, LSTEP>(rsrc, hi, soff0 + 8 * gstep, gstep, lds0 + 8 * LSTEP);
-  } else if constexpr (N == 1) {
+  if constexpr (N == 1) {
     asm volatile("s_mov_b32 m0, %[lds]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[v0], %[rs], %[so] offen lds"
                  : [so] "+s"(so)
                  : [lds] "s"(lds0), [rs] "s"(rsrc), [v0] "v"(vo[0])
@@ -240,8 +238,22 @@ __device__ constexpr int swz(int c, int r) {
   }
 }
 
+// Keys per LDS tile: 32 at D = 128 for up to four wavefronts (the smaller
+// tiles let three workgroups share a CU's LDS, so three wavefronts share each
+// SIMD), else 64.
+template <int D, int NW>
+constexpr int tile_keys() {
+  return (D == 128 && NW <= 4) ? 32 : 64;
+}
+// Wavefronts per SIMD the register budget is set for.
+template <int D, int NW>
+constexpr int waves_per_simd() {
+  return D == 64 ? 4 : (NW <= 4 ? 3 : 2);
+}
+
 template <int D, int NW>
 struct Tiling {
+  static constexpr int KC = tile_keys<D, NW>();
   static constexpr int NT = NW * 64;            // threads
   static constexpr int ROWB = D * 2;            // bytes per key row
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
@@ -256,18 +268,17 @@ struct Tiling {
   static constexpr int LDS_BYTES = SEG_OFF + 2 * KC * 4;
 };
 
-// Wavefronts per SIMD: at D = 128 a wavefront needs over 128 VGPRs, so two;
+// Wavefronts per SIMD: at D = 128 a wavefront needs up to 168 VGPRs, so
+// three (two for 8-wavefront workgroups, whose LDS allows only one per CU);
 // at D = 64 four fit, and the extra wavefronts hide the longer vector work
 // (per key, the pointwise variant spends two transcendentals on half as many
 // matrix FLOPs).
-#ifndef SPLASH_WAVES_D64
-#define SPLASH_WAVES_D64 4
-#endif
-template <int D, int NW, int CB, bool PW, typename OutT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CB == 1 ? (D == 64 ? SPLASH_WAVES_D64 : 2) : 1,
-                                                                      CB == 1 ? (D == 64 ? SPLASH_WAVES_D64 : 2) : 1)))
+template <int D, int NW, bool PW, typename OutT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW>(),
+                                                                      waves_per_simd<D, NW>())))
 void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int heads_interleaved) {
   using T = Tiling<D, NW>;
+  constexpr int KC = T::KC;
   constexpr int NS = T::NS;
   constexpr int ND = T::ND;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
@@ -321,21 +332,19 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
   // (a zero scale is taken as the smallest normal float: every allowed score
   // then gets the same weight, and -inf * c stays -inf for masked ones)
   const float c = PW ? p.scale : fmaxf(negate_q ? -p.scale_log2 : p.scale_log2, 1.17549435e-38f);
-  int qrow[CB];
-  bf16x8 qreg[CB][NS];
-  int32_t myseg[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    qrow[cb] = i * (NW * 32 * CB) + wave * (32 * CB) + cb * 32 + l32;
-    const bool valid = qrow[cb] < p.q_len;
+  const int qrow = i * (NW * 32) + wave * 32 + l32;
+  bf16x8 qreg[NS];
+  int32_t myseg = 0;
+  {
+    const bool valid = qrow < p.q_len;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (valid) v = *reinterpret_cast<const i16x8*>(qg + (int64_t)qrow[cb] * p.q_ss + 16 * s + 8 * hh);
+      if (valid) v = *reinterpret_cast<const i16x8*>(qg + (int64_t)qrow * p.q_ss + 16 * s + 8 * hh);
       if (negate_q) v ^= (short)0x8000;
-      qreg[cb][s] = __builtin_bit_cast(bf16x8, v);
+      qreg[s] = __builtin_bit_cast(bf16x8, v);
     }
-    myseg[cb] = (has_seg && valid) ? p.q_seg[(int64_t)b * p.q_len + qrow[cb]] : 0;
+    if (has_seg && valid) myseg = p.q_seg[(int64_t)b * p.q_len + qrow];
   }
 
   // ---- per-lane LDS offsets (swizzled chunk positions) ----
@@ -403,25 +412,19 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
     *reinterpret_cast<uint4*>(smem + o) = uint4{0u, 0u, 0u, 0u};
   __syncthreads();
 
-  f32x16 oacc[CB][ND];
+  f32x16 oacc[ND];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
+  for (int db = 0; db < ND; ++db)
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[cb][db][r] = 0.0f;
-  float mref[CB], lsum[CB];  // reference max (log2 domain), shared by O and L; this lane's share of L
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    mref[cb] = kNegInf;
-    lsum[cb] = 0.0f;
-  }
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+  float mref = kNegInf;  // reference max (log2 domain), shared by O and L
+  float lsum = 0.0f;     // this lane's share of L
 
   const int64_t mrow = (((int64_t)bm * p.meta_heads + hm) * p.nq + i) * p.nk;
   const int8_t* bmask = p.block_mask + mrow;
   const int32_t* dnext = p.data_next + mrow;
 
-  // Walk: tiles of 64 keys inside the non-empty blocks reached through
+  // Walk: tiles of KC keys inside the non-empty blocks reached through
   // data_next. data_next is only followed forward and within [0, nk], so any
   // metadata content ends the walk in bounds.
   auto next_block = [&](int j) {
@@ -455,29 +458,24 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
     const char* vt = kt + T::TILE;
 
     const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * KC;
-    // The tile is processed as two halves of 32 keys (kb), each: Sᵀ, softmax, Oᵀ += Vᵀ Pᵀ.
+    // The tile is processed in parts of 32 keys (kb), each: Sᵀ, softmax, Oᵀ += Vᵀ Pᵀ.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // ---- Sᵀ = K Qᵀ: 32 keys x 64 queries ----
-      f32x16 sacc[CB];
+    for (int kb = 0; kb < KC / 32; ++kb) {
+      // ---- Sᵀ = K Qᵀ: 32 keys x 32 queries ----
+      f32x16 sacc;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[cb][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * T::ROWB + koff[s]);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          sacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[cb][s], sacc[cb], 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc, 0, 0, 0);
       }
 
-      // sacc[cb][r] is the score of key k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4
-      // against query qrow[cb].
-      // Element mask, only on blocks of class 1. The tests are combined with
-      // bitwise operators so the whole mask is straight-line code.
-      // The band and the sequence end leave row q one run of keys [a, b] of
-      // the tile (offsets from k0), tested per score as one unsigned compare.
+      // sacc[r] is the score of key k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4
+      // against query qrow.
+      // Element mask, only on blocks of class 1: the band and the sequence end
+      // leave row q one run of keys [a, e] of the tile (offsets from k0),
+      // tested per score as one unsigned compare; straight-line code.
       auto apply_mask = [&](auto seg_tag) {
         constexpr bool kSeg = decltype(seg_tag)::value;
         int4 kseg4[4];
@@ -485,23 +483,20 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
 #pragma unroll
           for (int u = 0; u < 4; ++u) kseg4[u] = *reinterpret_cast<const int4*>(sseg + 32 * kb + 8 * u + 4 * hh);
         }
+        int a = qrow + band.lo - k0;
+        int e = qrow + band.hi - k0;
+        a = a > 0 ? a : 0;
+        e = e < p.kv_len - 1 - k0 ? e : p.kv_len - 1 - k0;
+        e = e < KC - 1 ? e : KC - 1;
+        if (e < a) a = e = KC;  // no key of the tile
+        const uint32_t width = (uint32_t)(e - a);
+        const int base = 4 * hh - a;  // offset of element r minus a, up to a constant of r
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          int a = qrow[cb] + band.lo - k0;
-          int e = qrow[cb] + band.hi - k0;
-          a = a > 0 ? a : 0;
-          e = e < p.kv_len - 1 - k0 ? e : p.kv_len - 1 - k0;
-          e = e < KC - 1 ? e : KC - 1;
-          if (e < a) a = e = KC;  // no key of the tile
-          const uint32_t width = (uint32_t)(e - a);
-          const int base = 4 * hh - a;  // offset of element r minus a, up to a constant of r
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kc = 32 * kb + 8 * (r >> 2) + (r & 3);
-            bool ok = (uint32_t)(base + kc) <= width;
-            if constexpr (kSeg) ok &= kseg4[r >> 2][r & 3] == myseg[cb];
-            sacc[cb][r] = ok ? sacc[cb][r] : (PW ? 0.0f : kNegInf);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int kc = 32 * kb + 8 * (r >> 2) + (r & 3);
+          bool ok = (uint32_t)(base + kc) <= width;
+          if constexpr (kSeg) ok &= kseg4[r >> 2][r & 3] == myseg;
+          sacc[r] = ok ? sacc[r] : (PW ? 0.0f : kNegInf);
         }
       };
       if (partial) {
@@ -511,61 +506,56 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
           apply_mask(std::false_type{});
       }
 
-      bf16x8 pb[2][CB];  // [g][cb]: B operand of Oᵀ += Vᵀ Pᵀ for keys 32 kb + 16 g + ...
+      bf16x8 pb[2];  // [g]: B operand of Oᵀ += Vᵀ Pᵀ for keys 32 kb + 16 g + ...
       if constexpr (!PW) {
         // Probabilities on the row's current reference, with no max: the sum
         // of the lane's 16 rounded probabilities (needed for L anyway, two per
-        // dot instruction) shows whether some score rose more than
-        // kFastLimitLog2 above the reference. Only then, or while a row has
-        // no reference yet, does the wavefront take the reference-raising path.
-        auto probs = [&](int cb, float mneg) {
+        // dot instruction) shows whether some score rose more than 40 log2
+        // units above the reference. Only then, or while a row has no
+        // reference yet, does the wavefront take the reference-raising path.
+        auto probs = [&](float mneg) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) pb[r >> 3][cb][r & 7] = (__bf16)fast_exp2(__builtin_fmaf(sacc[cb][r], c, mneg));
+          for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (__bf16)fast_exp2(__builtin_fmaf(sacc[r], c, mneg));
           float rs = 0.0f;
 #pragma unroll
           for (int g = 0; g < 2; ++g) {
-            const bf16x2x4 pr = __builtin_bit_cast(bf16x2x4, pb[g][cb]);
+            const bf16x2x4 pr = __builtin_bit_cast(bf16x2x4, pb[g]);
 #pragma unroll
             for (int u = 0; u < 4; ++u) rs = __builtin_amdgcn_fdot2_f32_bf16(pr.v[u], kOnes2, rs, false);
           }
           return rs;
         };
+        float rs = probs(-mref);
+        const bool fast = (mref != kNegInf) & (rs <= kFastLimit);  // false for NaN / inf too
+        if (__builtin_amdgcn_ballot_w64(!fast) != 0) {
+          float mx = kNegInf;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          float rs = probs(cb, -mref[cb]);
-          const bool fast = (mref[cb] != kNegInf) & (rs <= kFastLimit);  // false for NaN / inf too
-          if (__builtin_amdgcn_ballot_w64(!fast) != 0) {
-            float mx = kNegInf;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+          mx = max_xor32(mx) * c;  // max of these 32 keys, log2 domain (-inf if none allowed)
+          const bool raise = mx > mref + kRescaleSlack;
+          if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+            const float alpha = raise ? fast_exp2(mref - mx) : 1.0f;
+            mref = raise ? mx : mref;
+            lsum *= alpha;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[cb][r]);
-            mx = max_xor32(mx) * c;  // max of these 32 keys, log2 domain (-inf if none allowed)
-            const bool raise = mx > mref[cb] + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-              const float alpha = raise ? fast_exp2(mref[cb] - mx) : 1.0f;
-              mref[cb] = raise ? mx : mref[cb];
-              lsum[cb] *= alpha;
+            for (int db = 0; db < ND; ++db)
 #pragma unroll
-              for (int db = 0; db < ND; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[cb][db][r] *= alpha;
-            }
-            // rows with nothing allowed yet keep mref = -inf; all their entries are -inf here
-            rs = probs(cb, mref[cb] == kNegInf ? 0.0f : -mref[cb]);
+              for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
           }
-          lsum[cb] += rs;
+          // rows with nothing allowed yet keep mref = -inf; all their entries are -inf here
+          rs = probs(mref == kNegInf ? 0.0f : -mref);
         }
+        lsum += rs;
       } else {
         const float cneg = -c * kLog2e;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // silu(c s) / q_len = (c / q_len) * s * sigmoid(c s): the constant
-            // factor is applied once to O at the end
-            const float sv = sacc[cb][r];
-            const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(sv * cneg));
-            pb[r >> 3][cb][r & 7] = (__bf16)(sv * sg);
-          }
+        for (int r = 0; r < 16; ++r) {
+          // silu(c s) / q_len = (c / q_len) * s * sigmoid(c s): the constant
+          // factor is applied once to O at the end
+          const float sv = sacc[r];
+          const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp2(sv * cneg));
+          pb[r >> 3][r & 7] = (__bf16)(sv * sg);
+        }
       }
 
       // ---- Oᵀ += Vᵀ Pᵀ over these 32 keys ----
@@ -577,9 +567,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vt + rowbase + voff[0][db]));
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vt + rowbase + voff[1][db]));
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-            oacc[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g][cb], oacc[cb][db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[db], 0, 0, 0);
         }
       }
     }
@@ -593,49 +581,42 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
     if (!step(std::integral_constant<int, 1>{})) break;
   }
 
+  // ---- O = O / L (softmax) or O c / q_len (pointwise), strided store ----
+  float inv = c * p.inv_q_len;  // pointwise: the factor left out of P
+  if constexpr (!PW) {
+    const float l = sum_xor32(lsum);
+    inv = l > 0.0f ? 1.0f / l : 0.0f;
+  }
+  if (qrow < p.q_len) {
+    OutT* orow = og + (int64_t)qrow * p.o_ss;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    float inv = c * p.inv_q_len;  // pointwise: the factor left out of P
-    if constexpr (!PW) {
-      const float l = sum_xor32(lsum[cb]);
-      inv = l > 0.0f ? 1.0f / l : 0.0f;
-    }
-    if (qrow[cb] < p.q_len) {
-      OutT* orow = og + (int64_t)qrow[cb] * p.o_ss;
+    for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = 32 * db + 8 * g + 4 * hh;
-          store4<OutT>(orow + col, oacc[cb][db][4 * g] * inv, oacc[cb][db][4 * g + 1] * inv,
-                       oacc[cb][db][4 * g + 2] * inv, oacc[cb][db][4 * g + 3] * inv);
-        }
-    }
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * hh;
+        store4<OutT>(orow + col, oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                     oacc[db][4 * g + 3] * inv);
+      }
   }
 }
 
-template <int D, int NW, int CB, bool PW, typename OutT>
+template <int D, int NW, bool PW, typename OutT>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   const int64_t total = (int64_t)p.nq * p.B * p.H;
   if (total == 0) return hipSuccess;
   const int64_t per_xcd = (total + 7) / 8;
   const int interleaved = (p.B * p.H) % 8 == 0 ? 1 : 0;  // then total == 8 * per_xcd
-  hipLaunchKernelGGL((splash_fwd_bf16_kernel<D, NW, CB, PW, OutT>), dim3((unsigned)(per_xcd * 8)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((splash_fwd_bf16_kernel<D, NW, PW, OutT>), dim3((unsigned)(per_xcd * 8)), dim3(NW * 64), 0,
                      stream, p, (int)total, (int)per_xcd, interleaved);
   return hipGetLastError();
 }
 
-// Each wavefront owns SPLASH_ROW_BLOCKS x 32 query rows of the block.
-#ifndef SPLASH_ROW_BLOCKS
-#define SPLASH_ROW_BLOCKS 1
-#endif
-
+// Each wavefront owns 32 query rows: block_q / 32 wavefronts per workgroup.
 template <int D, bool PW, typename OutT>
 hipError_t launch_bq(const FwdParams& p, hipStream_t stream) {
-  constexpr int CB = SPLASH_ROW_BLOCKS;
-  if (p.block_q == 64) return launch_one<D, 2 / CB, CB, PW, OutT>(p, stream);
-  if (p.block_q == 256) return launch_one<D, 8 / CB, CB, PW, OutT>(p, stream);
-  return launch_one<D, 4 / CB, CB, PW, OutT>(p, stream);
+  if (p.block_q == 64) return launch_one<D, 2, PW, OutT>(p, stream);
+  if (p.block_q == 256) return launch_one<D, 8, PW, OutT>(p, stream);
+  return launch_one<D, 4, PW, OutT>(p, stream);
 }
 
 template <bool PW, typename OutT>
