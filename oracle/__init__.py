@@ -27,4 +27,5 @@ from .splash_oracle import (  # noqa: F401
     pointwise_attention_rows,
     block_flops,
     element_flops,
+    kv_head_of,
 )

@@ -19,6 +19,8 @@ blocking, fusion or reordering beyond what a definition states:
   sum_t e^{a_t - M}).
 * Online softmax: page 3, sections 15.1-15.3 (m, L, O per kv block and the
   correction alpha = e^{m_A - m_AB}).
+* Grouped-query attention: page 3, section 21 (query head h reads K/V head
+  h // q_heads_per_kv_head).
 * Pointwise attention: "hstu_ops.py", ``_pointwise_splash_attention_fwd_kernel_impl``
   (scores times scale, times logistic(scores), divided by the query sequence
   length, masked entries set to 0, then times V), with the contributions of
@@ -274,6 +276,16 @@ def online_softmax_rows(q_rows, k, v, scale: float, mask_rows, block_kv: int) ->
     return out
 
 
+def kv_head_of(h: int, H: int, kv_heads: int) -> int:
+    """KV head read by query head ``h`` when ``H`` query heads share
+    ``kv_heads`` K/V heads (page 3, section 21, GQA/MQA: the K/V index map
+    takes head h // q_heads_per_kv_head, with q_heads_per_kv_head = H /
+    kv_heads, so consecutive query heads share a K/V head)."""
+    if kv_heads < 1 or H % kv_heads:
+        raise ValueError("the query heads must split evenly over the kv heads")
+    return h // (H // kv_heads)
+
+
 def _heads_list(heads, H):
     heads = [tuple(h) for h in heads]
     if len(heads) not in (1, H):
@@ -287,6 +299,7 @@ def _attention(kind: str, q, k, v, scale, heads, q_seg, kv_seg, row_chunk: int):
     v = np.asarray(v, dtype=np.float64)
     B, H, Sq, _ = q.shape
     Skv = k.shape[2]
+    kv_heads = k.shape[1]
     heads = _heads_list(heads, H)
     out = np.zeros((B, H, Sq, v.shape[3]), dtype=np.float64)
     for b in range(B):
@@ -294,24 +307,27 @@ def _attention(kind: str, q, k, v, scale, heads, q_seg, kv_seg, row_chunk: int):
         ks = None if kv_seg is None else np.asarray(kv_seg)[b]
         for h in range(H):
             hd = heads[0] if len(heads) == 1 else heads[h]
+            hk = kv_head_of(h, H, kv_heads)
             for r0 in range(0, Sq, row_chunk):
                 rows = np.arange(r0, min(Sq, r0 + row_chunk))
                 m = element_mask(Sq, Skv, hd, qs, ks, rows=rows)
                 if kind == "softmax":
-                    out[b, h, rows] = softmax_attention_rows(q[b, h, rows], k[b, h], v[b, h], scale, m)
+                    out[b, h, rows] = softmax_attention_rows(q[b, h, rows], k[b, hk], v[b, hk], scale, m)
                 else:
-                    out[b, h, rows] = pointwise_attention_rows(q[b, h, rows], k[b, h], v[b, h], scale, m, Sq)
+                    out[b, h, rows] = pointwise_attention_rows(q[b, h, rows], k[b, hk], v[b, hk], scale, m, Sq)
     return out
 
 
 def softmax_attention(q, k, v, scale: float, heads, q_seg=None, kv_seg=None,
                       row_chunk: int = 512) -> np.ndarray:
     """Masked softmax attention [B, H, Sq, Dv] (fp64); rows are independent, so
-    the full-score definition is evaluated ``row_chunk`` rows at a time."""
+    the full-score definition is evaluated ``row_chunk`` rows at a time. k and
+    v may have fewer heads than q (grouped-query attention, ``kv_head_of``)."""
     return _attention("softmax", q, k, v, scale, heads, q_seg, kv_seg, row_chunk)
 
 
 def pointwise_attention(q, k, v, scale: float, heads, q_seg=None, kv_seg=None,
                         row_chunk: int = 512) -> np.ndarray:
-    """Pointwise SiLU attention [B, H, Sq, Dv] (fp64), divided by Sq."""
+    """Pointwise SiLU attention [B, H, Sq, Dv] (fp64), divided by Sq; k and v
+    may have fewer heads than q (``kv_head_of``)."""
     return _attention("pointwise", q, k, v, scale, heads, q_seg, kv_seg, row_chunk)

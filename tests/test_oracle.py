@@ -202,6 +202,49 @@ def test_softmax_matches_torch_sdpa_fp64(head, segments):
         np.testing.assert_allclose(got[b], ref, rtol=1e-12, atol=1e-12)
 
 
+def test_gqa_head_map_page3_example():
+    """Page 3, section 21: 8 query heads over 2 K/V heads, 4 per K/V head."""
+    with open(os.path.join(GOLDEN, "page3_sec21_gqa_heads.json")) as f:
+        g = json.load(f)
+    got = {str(h): oracle.kv_head_of(h, g["q_heads"], g["kv_heads"]) for h in range(g["q_heads"])}
+    assert got == g["kv_head_of_q_head"]
+    assert g["q_heads"] // g["kv_heads"] == g["q_heads_per_kv_head"]
+    with pytest.raises(ValueError):
+        oracle.kv_head_of(0, 6, 4)
+
+
+@pytest.mark.parametrize("kv_heads", [1, 2, 3])
+def test_gqa_matches_torch_sdpa_enable_gqa(kv_heads):
+    """torch's scaled_dot_product_attention with enable_gqa (K/V heads shared
+    by consecutive groups of query heads) is a library routine of the same
+    definition."""
+    B, H, S, D = 2, 6, 70, 16
+    q, _, _, qs, ks = _case(13, B, H, S, S, D, segments="docs")
+    rng = np.random.default_rng(7)
+    k = rng.standard_normal((B, kv_heads, S, D))
+    v = rng.standard_normal((B, kv_heads, S, D))
+    scale = 0.3
+    got = oracle.softmax_attention(q, k, v, scale, [CAUSAL], qs, ks, row_chunk=32)
+    for b in range(B):
+        m = oracle.element_mask(S, S, CAUSAL, qs[b], ks[b])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[b]), torch.from_numpy(k[b]), torch.from_numpy(v[b]),
+            attn_mask=torch.from_numpy(m), scale=scale, enable_gqa=True).numpy()
+        np.testing.assert_allclose(got[b], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_mqa_identical_query_heads_give_identical_outputs():
+    """One K/V head shared by every query head: equal query heads must give
+    equal outputs, for softmax and pointwise attention."""
+    B, H, S, D = 1, 4, 40, 8
+    q, k, v, _, _ = _case(17, B, 1, S, S, D)
+    q4 = np.repeat(q, H, axis=1)
+    for fn in (oracle.softmax_attention, oracle.pointwise_attention):
+        out = fn(q4, k, v, 0.4, [CAUSAL])
+        for h in range(1, H):
+            assert np.array_equal(out[:, h], out[:, 0])
+
+
 def test_softmax_closed_forms():
     S, D = 50, 16
     q, k, v, _, _ = _case(3, 1, 1, S, S, D)
