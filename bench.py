@@ -73,10 +73,11 @@ def cpu_baseline(w, gen, budget_s: float = 12.0):
     cache = {}
     while time.perf_counter() - t0 < budget_s or done < 4:
         b, h, i = int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(nq))
-        if (b, h) not in cache:
+        hk = oracle.kv_head_of(h, w.H, w.n_kv_heads)
+        if (b, hk) not in cache:
             cache.clear()
-            cache[(b, h)] = (gen["k"][b, h].to(torch.float64).numpy(), gen["v"][b, h].to(torch.float64).numpy())
-        k64, v64 = cache[(b, h)]
+            cache[(b, hk)] = (gen["k"][b, hk].to(torch.float64).numpy(), gen["v"][b, hk].to(torch.float64).numpy())
+        k64, v64 = cache[(b, hk)]
         rows = np.arange(i * bq, min(S, (i + 1) * bq))
         head = w.head_masks[0] if len(w.head_masks) == 1 else w.head_masks[h]
         m = oracle.element_mask(S, S, head, None if qs is None else qs[b], None if qs is None else qs[b], rows=rows)
@@ -193,6 +194,7 @@ def main():
         "c3": "causal AND same-document MHA B=2 H=32 S=8192 D=128 bf16, documents 256-2048, block 128x128",
         "c4": "mixed heads B=1 H=16 S=32768 D=128 bf16: 8 causal + 8 causal window 1024, block 128x128",
         "c5": "pointwise SiLU causal B=8 H=8 S=4096 D=64 bf16, N(0,0.5^2), block 128x128",
+        "g3h": "grouped-query causal B=2 H=32 (8 K/V heads) S=8192 D=128 bf16, block 128x128",
     }[w.name]
     line = {
         "metric": METRIC,
@@ -207,7 +209,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if in_f32 else "bf16",
         "data": "synthetic (seeded N(0, sigma^2) q, k, v)",
-        "config": {"workload": f"{w.name}: {desc}", "batch": w.B, "heads": w.H, "seq_len": w.S,
+        "config": {"workload": f"{w.name}: {desc}", "batch": w.B, "heads": w.H, "kv_heads": w.n_kv_heads,
+                   "seq_len": w.S,
                    "head_dim": w.D, "block_q": w.block_q, "block_kv": w.block_kv,
                    "nonempty_blocks": blocks, "flops_per_step": flops,
                    "step": "mask_info_build + " + ("pointwise_fwd" if w.pointwise else "splash_fwd")},

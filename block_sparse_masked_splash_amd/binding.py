@@ -32,6 +32,8 @@ SYMBOLS = (
     "splash_mask_info_build",
     "splash_fwd",
     "splash_pointwise_fwd",
+    "splash_gqa_fwd",
+    "splash_gqa_pointwise_fwd",
     "splash_status_string",
     "splash_last_error",
     "splash_abi_version",
@@ -69,6 +71,8 @@ _FWD_ARGS = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_in
              ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
              ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
              ctypes.c_float, ctypes.POINTER(MaskDescC), ctypes.POINTER(MaskInfoC), ctypes.c_void_p]
+# grouped-query forms: kv_heads follows H
+_GQA_ARGS = _FWD_ARGS[:4] + [ctypes.c_int] + _FWD_ARGS[4:]
 
 _lib = None
 
@@ -92,6 +96,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = _FWD_ARGS
+    for name in ("splash_gqa_fwd", "splash_gqa_pointwise_fwd"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = _GQA_ARGS
     lib.splash_status_string.restype = ctypes.c_char_p
     lib.splash_status_string.argtypes = [ctypes.c_int]
     lib.splash_last_error.restype = ctypes.c_char_p
@@ -216,14 +224,14 @@ def _strides(t: torch.Tensor, layout: str):
     raise ValueError(f"layout must be 'bhsd' or 'bshd', not {layout!r}")
 
 
-def _forward(fn_name, q, k, v, info: MaskInfo, scale, out, out_dtype, layout):
+def _forward(pointwise: bool, q, k, v, info: MaskInfo, scale, out, out_dtype, layout):
     lib = load_library()
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float32 or bfloat16")
     qs, (B, H, Sq, D) = _strides(q, layout)
     ks, (Bk, Hk, Skv, Dk) = _strides(k, layout)
     vs, vshape = _strides(v, layout)
-    if (Bk, Hk, Dk) != (B, H, D) or vshape != (B, H, Skv, D):
+    if (Bk, Dk) != (B, D) or vshape != (B, Hk, Skv, D) or Hk < 1 or H % Hk:
         raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)} ({layout})")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
@@ -246,10 +254,14 @@ def _forward(fn_name, q, k, v, info: MaskInfo, scale, out, out_dtype, layout):
                           f"metadata built for B={info.B} H={info.H} q_len={info.q_len} kv_len={info.kv_len}")
     desc, keep = info.mask_desc()
     cinfo = info.info_struct()
-    fn = getattr(lib, fn_name)
-    st = fn(_DT[q.dtype], _DT[out_dtype], B, H, Sq, Skv, D,
-            q.data_ptr(), qs, k.data_ptr(), ks, v.data_ptr(), vs, out.data_ptr(), os_,
+    tail = (q.data_ptr(), qs, k.data_ptr(), ks, v.data_ptr(), vs, out.data_ptr(), os_,
             float(scale), ctypes.byref(desc), ctypes.byref(cinfo), ctypes.c_void_p(_stream(q.device)))
+    if Hk == H:
+        fn = lib.splash_pointwise_fwd if pointwise else lib.splash_fwd
+        st = fn(_DT[q.dtype], _DT[out_dtype], B, H, Sq, Skv, D, *tail)
+    else:
+        fn = lib.splash_gqa_pointwise_fwd if pointwise else lib.splash_gqa_fwd
+        st = fn(_DT[q.dtype], _DT[out_dtype], B, H, Hk, Sq, Skv, D, *tail)
     del keep
     _check(st)
     return out
@@ -259,12 +271,15 @@ def splash_fwd(q, k, v, info: MaskInfo, scale: float | None = None, out=None, ou
                layout: str = "bhsd"):
     """Softmax attention forward under the block-sparse mask of ``info``.
 
-    q [B,H,Sq,D], k/v [B,H,Skv,D] (``layout="bshd"``: [B,S,H,D]); default scale
-    1/sqrt(D). Returns ``out`` (allocated if None)."""
-    return _forward("splash_fwd", q, k, v, info, scale, out, out_dtype, layout)
+    q [B,H,Sq,D], k/v [B,Hkv,Skv,D] (``layout="bshd"``: [B,S,H,D]); Hkv = H
+    is multi-head attention, a divisor of H grouped-query attention (query
+    head h reads K/V head h // (H / Hkv)). Default scale 1/sqrt(D). Returns
+    ``out`` (allocated if None)."""
+    return _forward(False, q, k, v, info, scale, out, out_dtype, layout)
 
 
 def pointwise_fwd(q, k, v, info: MaskInfo, scale: float | None = None, out=None, out_dtype=None,
                   layout: str = "bhsd"):
-    """Pointwise SiLU attention forward: (1/Sq) sum_k silu(scale q.k) v_k."""
-    return _forward("splash_pointwise_fwd", q, k, v, info, scale, out, out_dtype, layout)
+    """Pointwise SiLU attention forward: (1/Sq) sum_k silu(scale q.k) v_k;
+    k/v may have fewer heads than q, as for ``splash_fwd``."""
+    return _forward(True, q, k, v, info, scale, out, out_dtype, layout)

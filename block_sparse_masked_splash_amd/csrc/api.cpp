@@ -92,13 +92,15 @@ splash_status check_tensor(const char* name, const void* ptr, const int64_t* str
   return SPLASH_OK;
 }
 
-splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int q_len,
-                         int kv_len, int head_dim, const void* q, const int64_t q_strides[3], const void* k,
+splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
+                         int q_len, int kv_len, int head_dim, const void* q, const int64_t q_strides[3], const void* k,
                          const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* o,
                          const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
                          const splash_mask_info* info, hipStream_t stream) {
   splash_status s = check_sizes(B, H, q_len, kv_len);
   if (s != SPLASH_OK) return s;
+  if (kv_heads < 1 || kv_heads > H || H % kv_heads != 0)
+    return fail(SPLASH_ERR_INVALID_ARGUMENT, "kv_heads=%d must divide H=%d", kv_heads, H);
   const bool f32 = in_dtype == SPLASH_F32 && out_dtype == SPLASH_F32;
   const bool bf16 = in_dtype == SPLASH_BF16 && (out_dtype == SPLASH_BF16 || out_dtype == SPLASH_F32);
   if (!f32 && !bf16)
@@ -143,6 +145,8 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
 
   p.B = B;
   p.H = H;
+  p.kv_heads = kv_heads;
+  p.kv_group = H / kv_heads;
   p.q_len = q_len;
   p.kv_len = kv_len;
   p.head_dim = head_dim;
@@ -170,7 +174,7 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
 
   hipError_t e = f32 ? splash::launch_fwd_f32(p, pointwise, stream)
                      : splash::launch_fwd_bf16(p, pointwise, out_dtype == SPLASH_F32, stream);
-  return hip_status(e, pointwise ? "splash_pointwise_fwd launch" : "splash_fwd launch");
+  return hip_status(e, pointwise ? "pointwise forward launch" : "softmax forward launch");
 }
 
 }  // namespace
@@ -249,7 +253,7 @@ splash_status splash_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, i
                          const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* o,
                          const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
                          const splash_mask_info* info, hipStream_t stream) {
-  return fwd_common(false, in_dtype, out_dtype, B, H, q_len, kv_len, head_dim, q, q_strides, k, k_strides, v,
+  return fwd_common(false, in_dtype, out_dtype, B, H, H, q_len, kv_len, head_dim, q, q_strides, k, k_strides, v,
                     v_strides, o, o_strides, scale, mask, info, stream);
 }
 
@@ -259,8 +263,27 @@ splash_status splash_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_dtype
                                    const int64_t v_strides[3], void* o, const int64_t o_strides[3], float scale,
                                    const splash_mask_desc* mask, const splash_mask_info* info,
                                    hipStream_t stream) {
-  return fwd_common(true, in_dtype, out_dtype, B, H, q_len, kv_len, head_dim, q, q_strides, k, k_strides, v,
+  return fwd_common(true, in_dtype, out_dtype, B, H, H, q_len, kv_len, head_dim, q, q_strides, k, k_strides, v,
                     v_strides, o, o_strides, scale, mask, info, stream);
+}
+
+splash_status splash_gqa_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads, int q_len,
+                             int kv_len, int head_dim, const void* q, const int64_t q_strides[3], const void* k,
+                             const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* o,
+                             const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
+                             const splash_mask_info* info, hipStream_t stream) {
+  return fwd_common(false, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides,
+                    v, v_strides, o, o_strides, scale, mask, info, stream);
+}
+
+splash_status splash_gqa_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
+                                       int q_len, int kv_len, int head_dim, const void* q,
+                                       const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
+                                       const void* v, const int64_t v_strides[3], void* o,
+                                       const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
+                                       const splash_mask_info* info, hipStream_t stream) {
+  return fwd_common(true, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides,
+                    v, v_strides, o, o_strides, scale, mask, info, stream);
 }
 
 }  // extern "C"

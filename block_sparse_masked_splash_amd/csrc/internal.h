@@ -30,6 +30,8 @@ struct MaskInfoParams {
 
 struct FwdParams {
   int B, H, q_len, kv_len, head_dim;
+  int kv_heads;      // K/V heads; query head h reads kv head h / kv_group
+  int kv_group;      // H / kv_heads
   const void* q;
   const void* k;
   const void* v;

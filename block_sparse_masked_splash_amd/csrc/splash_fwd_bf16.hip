@@ -276,7 +276,7 @@ struct Tiling {
 template <int D, int NW, bool PW, typename OutT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW>(),
                                                                       waves_per_simd<D, NW>())))
-void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int heads_interleaved) {
+void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
   using T = Tiling<D, NW>;
   constexpr int KC = T::KC;
   constexpr int NS = T::NS;
@@ -284,28 +284,33 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
   // XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
-  // id -> (x, k) = (id % 8, id / 8) is the k-th workgroup XCD x runs. Each
-  // XCD works through whole (b, h) heads one after the other, so K and V of
-  // the head in flight stay in that XCD's L2, and within a head the heaviest
-  // query blocks (most kv blocks under causal masks) go first. When the
-  // number of heads is a multiple of 8, XCD x takes heads x, x + 8, ...:
-  // heads with different masks (say causal and local ones side by side) are
-  // then spread evenly over the XCDs. Otherwise each XCD takes a contiguous
-  // eighth of the (head, query block) list.
+  // id -> (x, k) = (id % 8, id / 8) is the k-th workgroup XCD x runs. The
+  // unit an XCD works through in one go is a K/V head together with the
+  // kv_group query heads that read it (one head without grouping), so that
+  // K/V head stays in the XCD's L2; within a unit the heaviest query blocks
+  // (most kv blocks under causal masks) go first, the unit's heads side by
+  // side. When the number of units is a multiple of 8, XCD x takes units
+  // x, x + 8, ...: units with different masks (say causal and local heads)
+  // are then spread evenly over the XCDs. Otherwise each XCD takes a
+  // contiguous eighth of the work list.
   const int xcd = (int)(blockIdx.x & 7), k_in_xcd = (int)(blockIdx.x >> 3);
-  int bh, i;
-  if (heads_interleaved) {
-    const int hk = k_in_xcd / p.nq;
-    bh = xcd + 8 * hk;
-    i = p.nq - 1 - (k_in_xcd - hk * p.nq);
+  const int per_unit = p.nq * p.kv_group;
+  int unit, rest;
+  if (units_interleaved) {
+    const int uk = k_in_xcd / per_unit;
+    unit = xcd + 8 * uk;
+    rest = k_in_xcd - uk * per_unit;
   } else {
     const int wid = xcd * work_per_xcd + k_in_xcd;
     if (wid >= total_work) return;
-    bh = wid / p.nq;
-    i = p.nq - 1 - (wid - bh * p.nq);
+    unit = wid / per_unit;
+    rest = wid - unit * per_unit;
   }
-  const int b = bh / p.H;
-  const int h = bh - b * p.H;
+  const int ri = rest / p.kv_group;
+  const int i = p.nq - 1 - ri;
+  const int b = unit / p.kv_heads;
+  const int hk = unit - b * p.kv_heads;  // K/V head
+  const int h = hk * p.kv_group + (rest - ri * p.kv_group);
   const int hm = p.meta_heads == 1 ? 0 : h;
   const int bm = p.meta_batch == 1 ? 0 : b;
   const HeadBand band = p.band[hm];
@@ -317,8 +322,8 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int h
   const int hh = lane >> 5;
 
   const __bf16* qg = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
-  const char* kg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + h * p.k_sh);
-  const char* vg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + h * p.v_sh);
+  const char* kg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh);
+  const char* vg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh);
   OutT* og = reinterpret_cast<OutT*>(p.o) + b * p.o_sb + h * p.o_sh;
   const int64_t k_rs = p.k_ss * 2;  // bytes between key rows
   const int64_t v_rs = p.v_ss * 2;
@@ -605,7 +610,7 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   const int64_t total = (int64_t)p.nq * p.B * p.H;
   if (total == 0) return hipSuccess;
   const int64_t per_xcd = (total + 7) / 8;
-  const int interleaved = (p.B * p.H) % 8 == 0 ? 1 : 0;  // then total == 8 * per_xcd
+  const int interleaved = (p.B * p.kv_heads) % 8 == 0 ? 1 : 0;  // then total == 8 * per_xcd
   hipLaunchKernelGGL((splash_fwd_bf16_kernel<D, NW, PW, OutT>), dim3((unsigned)(per_xcd * 8)), dim3(NW * 64), 0,
                      stream, p, (int)total, (int)per_xcd, interleaved);
   return hipGetLastError();

@@ -47,8 +47,9 @@ __global__ __launch_bounds__(BQ*(D / 32)) void splash_fwd_f32_kernel(FwdParams p
   const HeadBand band = p.band[hm];
 
   const float* qg = reinterpret_cast<const float*>(p.q) + b * p.q_sb + h * p.q_sh;
-  const float* kg = reinterpret_cast<const float*>(p.k) + b * p.k_sb + h * p.k_sh;
-  const float* vg = reinterpret_cast<const float*>(p.v) + b * p.v_sb + h * p.v_sh;
+  const int hk = h / p.kv_group;  // K/V head read by query head h
+  const float* kg = reinterpret_cast<const float*>(p.k) + b * p.k_sb + hk * p.k_sh;
+  const float* vg = reinterpret_cast<const float*>(p.v) + b * p.v_sb + hk * p.v_sh;
   float* og = reinterpret_cast<float*>(p.o) + b * p.o_sb + h * p.o_sh;
 
   const int qrow = i * BQ + rl;

@@ -7,7 +7,8 @@ here.
 
 Recipe (shared by every test and by the benchmark):
   * ``numpy.random.default_rng(seed)`` (PCG64); q, k, v are drawn in that order
-    as float32 ``standard_normal`` of shape [B, H, S, D], multiplied by sigma.
+    as float32 ``standard_normal`` of shape [B, H, S, D] (k and v with
+    kv_heads instead of H heads for grouped-query workloads), times sigma.
   * bf16 workloads round those float32 values to bfloat16 with
     round-to-nearest-even (``torch.Tensor.to(torch.bfloat16)``); the oracle
     receives the rounded values upcast exactly to float64.
@@ -55,6 +56,11 @@ class Workload:
     segments: bool          # packed documents (causal AND same segment)
     pointwise: bool         # SiLU pointwise attention instead of softmax
     seed: int
+    kv_heads: int = 0       # K/V heads (0: H, plain multi-head attention)
+
+    @property
+    def n_kv_heads(self) -> int:
+        return self.kv_heads or self.H
 
     @property
     def scale(self) -> float:
@@ -81,15 +87,19 @@ WORKLOADS = {
     "c4": Workload("c4", 1, 16, 32768, 128, "bf16", 1.0, _LOCAL_MIX, 128, 128, False, False, 4),
     # pointwise SiLU attention, causal, N(0, 0.5^2)
     "c5": Workload("c5", 8, 8, 4096, 64, "bf16", 0.5, (CAUSAL,), 128, 128, False, True, 5),
+    # grouped-query form of c3h: 32 query heads over 8 K/V heads
+    "g3h": Workload("g3h", 2, 32, 8192, 128, "bf16", 1.0, (CAUSAL,), 128, 128, False, False, 6, kv_heads=8),
 }
 
 
 def draw_qkv_f32(rng: np.random.Generator, B: int, H: int, Sq: int, Skv: int, D: int,
-                 sigma: float):
-    """float32 q [B,H,Sq,D], k [B,H,Skv,D], v [B,H,Skv,D], drawn in that order."""
+                 sigma: float, kv_heads: int | None = None):
+    """float32 q [B,H,Sq,D], k [B,Hk,Skv,D], v [B,Hk,Skv,D] (Hk = kv_heads or
+    H), drawn in that order."""
+    Hk = H if kv_heads is None else kv_heads
     q = rng.standard_normal((B, H, Sq, D), dtype=np.float32) * np.float32(sigma)
-    k = rng.standard_normal((B, H, Skv, D), dtype=np.float32) * np.float32(sigma)
-    v = rng.standard_normal((B, H, Skv, D), dtype=np.float32) * np.float32(sigma)
+    k = rng.standard_normal((B, Hk, Skv, D), dtype=np.float32) * np.float32(sigma)
+    v = rng.standard_normal((B, Hk, Skv, D), dtype=np.float32) * np.float32(sigma)
     return q, k, v
 
 
@@ -125,10 +135,11 @@ def generate(w: Workload, *, B: int | None = None, H: int | None = None,
     are int32 torch tensors [B, S] or None.
     """
     B = w.B if B is None else B
+    Hk = w.n_kv_heads if H is None else max(1, H // (w.H // w.n_kv_heads))
     H = w.H if H is None else H
     S = w.S if S is None else S
     rng = np.random.default_rng(w.seed if seed is None else seed)
-    q, k, v = draw_qkv_f32(rng, B, H, S, S, w.D, w.sigma)
+    q, k, v = draw_qkv_f32(rng, B, H, S, S, w.D, w.sigma, Hk)
     out = dict(q=_store(q, w.dtype), k=_store(k, w.dtype), v=_store(v, w.dtype),
                q_segment_ids=None, kv_segment_ids=None)
     del q, k, v

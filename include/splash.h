@@ -165,6 +165,31 @@ splash_status splash_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_dtype
                                    float scale, const splash_mask_desc* mask,
                                    const splash_mask_info* info, hipStream_t stream);
 
+/* Grouped-query (and multi-query) forms of the two forwards ("JAX 到 VLIW ..."
+ * study notes, section 21: several query heads share one K/V head, and query
+ * head h reads K/V head h / (H / kv_heads)). Same arguments, layouts, support
+ * matrix and errors as splash_fwd / splash_pointwise_fwd, except that k and v
+ * are [B, kv_heads, kv_len, head_dim] (their head stride steps over K/V
+ * heads). kv_heads must divide H (INVALID_ARGUMENT otherwise); kv_heads == H
+ * is plain multi-head attention and kv_heads == 1 multi-query attention. The
+ * mask heads and the metadata stay per query head. */
+splash_status splash_gqa_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
+                             int q_len, int kv_len, int head_dim,
+                             const void* q, const int64_t q_strides[3],
+                             const void* k, const int64_t k_strides[3],
+                             const void* v, const int64_t v_strides[3],
+                             void* o, const int64_t o_strides[3],
+                             float scale, const splash_mask_desc* mask,
+                             const splash_mask_info* info, hipStream_t stream);
+splash_status splash_gqa_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H,
+                                       int kv_heads, int q_len, int kv_len, int head_dim,
+                                       const void* q, const int64_t q_strides[3],
+                                       const void* k, const int64_t k_strides[3],
+                                       const void* v, const int64_t v_strides[3],
+                                       void* o, const int64_t o_strides[3],
+                                       float scale, const splash_mask_desc* mask,
+                                       const splash_mask_info* info, hipStream_t stream);
+
 /* Static name of a status code. */
 const char* splash_status_string(splash_status s);
 /* Detail of the last failure on the calling thread ("" if none). */

@@ -115,6 +115,28 @@ def test_forward_validation_errors(fn):
     assert _fwd(lib, fn, scale=float("nan"), desc=d, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
 
 
+@pytest.mark.parametrize("fn", ["splash_gqa_fwd", "splash_gqa_pointwise_fwd"])
+def test_gqa_forward_validation_errors(fn):
+    """kv_heads must divide H; the rest is checked as for splash_fwd. Every
+    call here fails on the host, so nothing is launched."""
+    lib = bd.load_library()
+    d, keep = _desc()
+    inf = _info()
+
+    def call(H=4, kv_heads=2, desc=d, info=inf, D=128):
+        st = [bd._I64x3(H * 256 * D, 256 * D, D) for _ in range(4)]
+        return getattr(lib, fn)(1, 1, 1, H, kv_heads, 256, 256, D, 0x100000, st[0], 0x200000, st[1],
+                                0x300000, st[2], 0x400000, st[3], 0.1, ctypes.byref(desc) if desc else None,
+                                ctypes.byref(info) if info else None, None)
+
+    assert call(kv_heads=3) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert b"kv_heads" in lib.splash_last_error()
+    assert call(kv_heads=0) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(kv_heads=8) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(D=96) == bd.SPLASH_ERR_UNSUPPORTED
+    assert call(info=_info(nq=2)) == bd.SPLASH_ERR_METADATA_MISMATCH
+
+
 def test_mask_info_build_validation_errors():
     lib = bd.load_library()
     d, keep = _desc()

@@ -184,7 +184,7 @@ def test_workload_c2_full(gpu_device):
 # ---------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("name", ["c3h", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c3h", "c3", "c4", "c5", "g3h"])
 def test_full_workload_sampled_rows(gpu_device, name):
     w = wl.WORKLOADS[name]
     print(f"full workload {name}", flush=True)
@@ -204,10 +204,11 @@ def test_full_workload_sampled_rows(gpu_device, name):
     got, ref = [], []
     cache = {}
     for (b, h, t) in rows:
-        if (b, h) not in cache:
+        hk = oracle.kv_head_of(h, w.H, w.n_kv_heads)
+        if (b, hk) not in cache:
             cache.clear()
-            cache[(b, h)] = (to64(c["k"][b, h]), to64(c["v"][b, h]))
-        k64, v64 = cache[(b, h)]
+            cache[(b, hk)] = (to64(c["k"][b, hk]), to64(c["v"][b, hk]))
+        k64, v64 = cache[(b, hk)]
         head = w.head_masks[0] if len(w.head_masks) == 1 else w.head_masks[h]
         m = oracle.element_mask(w.S, w.S, head, None if qs is None else qs[b], None if qs is None else qs[b], rows=[t])
         q64 = to64(c["q"][b, h, t:t + 1])
@@ -225,7 +226,46 @@ def test_full_workload_sampled_rows(gpu_device, name):
         for (b, h, t) in rows:
             alone = t == 0 or (qs is not None and qs[b, t] != qs[b, t - 1])
             if alone:
-                assert torch.equal(out[b, h, t].cpu(), c["v"][b, h, t]), (b, h, t)
+                hk = oracle.kv_head_of(h, w.H, w.n_kv_heads)
+                assert torch.equal(out[b, h, t].cpu(), c["v"][b, hk, t]), (b, h, t)
+
+
+# ---------------------------------------------------------------------------
+# grouped-query attention (query head h reads K/V head h // (H / kv_heads))
+# ---------------------------------------------------------------------------
+
+GQA_CASES = [
+    # B, H, kv_heads, Sq, Skv, D, heads, bq, bkv, segments, dtype, layout
+    (2, 4, 2, 333, 333, 128, [CAUSAL], 128, 128, None, "bf16", "bhsd"),
+    (2, 4, 1, 300, 420, 64, [FULL, CAUSAL, wl.local_causal(40), (0, 30, 60)], 64, 128, "random", "bf16", "bhsd"),
+    (1, 8, 2, 517, 517, 128, [CAUSAL], 128, 64, "docs", "bf16", "bshd"),
+    (1, 6, 3, 290, 290, 128, [wl.local_causal(70)], 256, 128, None, "bf16", "bhsd"),
+    (2, 4, 2, 200, 200, 64, [CAUSAL], 64, 64, "docs", "f32", "bhsd"),
+]
+
+
+@pytest.mark.parametrize("pointwise", [False, True], ids=["softmax", "pointwise"])
+@pytest.mark.parametrize("case", GQA_CASES, ids=[f"g{n}" for n in range(len(GQA_CASES))])
+def test_gqa_small_matches_oracle(gpu_device, case, pointwise):
+    B, H, Hk, Sq, Skv, D, heads, bq, bkv, seg, dt, layout = case
+    print(f"gqa case {case} pointwise={pointwise}", flush=True)
+    sigma = 0.5 if pointwise else 1.0
+    c = wl.random_case(29, B, H, Sq, Skv, D, dt, sigma=sigma, segments=seg, doc_len=(1, 150))
+    kv = wl.random_case(31, B, Hk, Sq, Skv, D, dt, sigma=sigma)
+    c["k"], c["v"] = kv["k"], kv["v"]
+    g = _to_dev(c, gpu_device)
+    info = _meta(gpu_device, B, H, Sq, Skv, heads, bq, bkv, g)
+    fn = sp.pointwise_fwd if pointwise else sp.splash_fwd
+    if layout == "bshd":
+        q, k, v = (g[n].transpose(1, 2).contiguous() for n in ("q", "k", "v"))
+        out = fn(q, k, v, info, layout="bshd").transpose(1, 2)
+    else:
+        out = fn(g["q"], g["k"], g["v"], info)
+    torch.cuda.synchronize()
+    ofn = oracle.pointwise_attention if pointwise else oracle.softmax_attention
+    ref = ofn(to64(c["q"]), to64(c["k"]), to64(c["v"]), 1 / math.sqrt(D), heads,
+              _seg_np(c["q_segment_ids"]), _seg_np(c["kv_segment_ids"]))
+    print(check_close(to64(out), ref, dt, f"gqa {case}"))
 
 
 # ---------------------------------------------------------------------------
