@@ -28,4 +28,5 @@ from .splash_oracle import (  # noqa: F401
     block_flops,
     element_flops,
     kv_head_of,
+    partial_blocks,
 )

@@ -9,6 +9,9 @@ blocking, fusion or reordering beyond what a definition states:
 * Element mask: "hstu_ops.py" (RecML), ``pointwise_splash_attention`` builds
   a CausalMask or FullMask, optionally ANDed with LocalMask((w, w), offset=0);
   ``_apply_mask`` ANDs that with segment equality ``q_ids == kv_ids``.
+* Dense masks: "hstu_ops.py", ``pointwise_splash_attention`` (a numpy array
+  mask of shape (q_len, kv_len) becomes a NumpyMask) and the forward's mask
+  block index map (partial blocks fetch their mask through ``mask_next``).
 * Block metadata: "hstu_ops.py", ``_next_nonzero`` (a block runs when its
   ``block_mask`` entry is > 0, needs no element mask when it is not 1, and the
   kv block fetched at grid step j is ``data_next[h, i, j]``); page 3
@@ -62,17 +65,25 @@ def _allowed(qpos: np.ndarray, kpos: np.ndarray, head) -> np.ndarray:
 
 
 def element_mask(q_len: int, kv_len: int, head, q_seg=None, kv_seg=None,
-                 rows=None) -> np.ndarray:
+                 rows=None, dense=None) -> np.ndarray:
     """Boolean element mask [len(rows), kv_len] of one (batch, head).
 
     ``q_seg`` / ``kv_seg`` are the segment ids of this batch row ([q_len],
-    [kv_len]) or None; with ids, a pair is allowed only when they are equal
-    ("hstu_ops.py", ``_apply_mask``: the masks are combined with logical AND).
-    ``rows`` selects query positions (default: all).
+    [kv_len]) or None; with ids, a pair is allowed only when they are equal.
+    ``dense`` is an arbitrary boolean [q_len, kv_len] mask of this head or
+    None ("hstu_ops.py", ``pointwise_splash_attention``: a numpy array mask
+    becomes a NumpyMask, which the local window is ANDed onto). All parts are
+    combined with logical AND ("hstu_ops.py", ``_apply_mask``). ``rows``
+    selects query positions (default: all).
     """
     qpos = np.arange(q_len) if rows is None else np.asarray(rows, dtype=np.int64)
     kpos = np.arange(kv_len)
     m = _allowed(qpos, kpos, head)
+    if dense is not None:
+        d = np.asarray(dense, dtype=bool)
+        if d.shape != (q_len, kv_len):
+            raise ValueError(f"dense mask shape {d.shape} is not ({q_len}, {kv_len})")
+        m &= d[qpos]
     if (q_seg is None) != (kv_seg is None):
         raise ValueError("q and kv segment ids must be given together or not at all")
     if q_seg is not None:
@@ -83,7 +94,7 @@ def element_mask(q_len: int, kv_len: int, head, q_seg=None, kv_seg=None,
 
 
 def padded_element_mask(q_len: int, kv_len: int, bq: int, bkv: int, head,
-                        q_seg=None, kv_seg=None, q_block=None) -> np.ndarray:
+                        q_seg=None, kv_seg=None, q_block=None, dense=None) -> np.ndarray:
     """Element mask over whole blocks: [nq*bq, nk*bkv], or [bq, nk*bkv] for the
     single query block ``q_block``. Positions past the sequence ends are not
     allowed (reading for lengths that are not a multiple of the block size)."""
@@ -95,7 +106,7 @@ def padded_element_mask(q_len: int, kv_len: int, bq: int, bkv: int, head,
         rows = np.arange(i * bq, min(q_len, (i + 1) * bq))
         if rows.size:
             out[n * bq:n * bq + rows.size, :kv_len] = element_mask(
-                q_len, kv_len, head, q_seg, kv_seg, rows=rows)
+                q_len, kv_len, head, q_seg, kv_seg, rows=rows, dense=dense)
     return out
 
 
@@ -121,7 +132,7 @@ def next_nonempty(block_mask_row) -> np.ndarray:
 
 
 def mask_info_row(q_len: int, kv_len: int, bq: int, bkv: int, head, i: int,
-                  q_seg=None, kv_seg=None):
+                  q_seg=None, kv_seg=None, dense=None):
     """(block_mask [nk] int8, data_next [nk] int32) of query block ``i`` of one
     (batch, head).
 
@@ -131,27 +142,41 @@ def mask_info_row(q_len: int, kv_len: int, bq: int, bkv: int, head, i: int,
     skips the element mask; the value 2 for "full" is the reading taken).
     """
     nk = -(-kv_len // bkv)
-    m = padded_element_mask(q_len, kv_len, bq, bkv, head, q_seg, kv_seg, q_block=i)
+    m = padded_element_mask(q_len, kv_len, bq, bkv, head, q_seg, kv_seg, q_block=i, dense=dense)
     counts = m.reshape(bq, nk, bkv).sum(axis=(0, 2), dtype=np.int64)
     cls = np.where(counts == 0, 0, np.where(counts == bq * bkv, 2, 1)).astype(np.int8)
     return cls, next_nonempty(cls)
 
 
+def _dense_heads(dense, H):
+    """None, or a list of per-head boolean masks (1 broadcast, or H)."""
+    if dense is None:
+        return None
+    d = np.asarray(dense, dtype=bool)
+    if d.ndim == 2:
+        d = d[None]
+    if d.shape[0] not in (1, H):
+        raise ValueError("need one dense mask or one per head")
+    return [d[n] for n in range(d.shape[0])]
+
+
 def mask_info(B: int, H: int, q_len: int, kv_len: int, bq: int, bkv: int, heads,
-              q_seg=None, kv_seg=None):
+              q_seg=None, kv_seg=None, dense=None):
     """Block metadata (block_mask int8, data_next int32), [Bm, Hm, nq, nk].
 
-    Hm = len(heads) (1 broadcasts over all H heads, "hstu_ops.py"
-    ``_next_nonzero`` forces the head index to 0 for one-head metadata);
-    Bm = B with segment ids, else 1. Each row is ``mask_info_row``.
+    Hm = max(len(heads), number of dense masks) (1 broadcasts over all H
+    heads, "hstu_ops.py" ``_next_nonzero`` forces the head index to 0 for
+    one-head metadata); Bm = B with segment ids, else 1. Each row is
+    ``mask_info_row``.
     """
     heads = [tuple(h) for h in heads]
     if len(heads) not in (1, H):
         raise ValueError("need one head mask or one per head")
     if (q_seg is None) != (kv_seg is None):
         raise ValueError("q and kv segment ids must be given together or not at all")
+    dh = _dense_heads(dense, H)
     Bm = B if q_seg is not None else 1
-    Hm = len(heads)
+    Hm = max(len(heads), 1 if dh is None else len(dh))
     nq = -(-q_len // bq)
     nk = -(-kv_len // bkv)
     bmask = np.zeros((Bm, Hm, nq, nk), dtype=np.int8)
@@ -160,10 +185,42 @@ def mask_info(B: int, H: int, q_len: int, kv_len: int, bq: int, bkv: int, heads,
         qs = None if q_seg is None else np.asarray(q_seg)[b]
         ks = None if kv_seg is None else np.asarray(kv_seg)[b]
         for hm in range(Hm):
+            head = heads[0] if len(heads) == 1 else heads[hm]
+            dm = None if dh is None else (dh[0] if len(dh) == 1 else dh[hm])
             for i in range(nq):
                 bmask[b, hm, i], dnext[b, hm, i] = mask_info_row(
-                    q_len, kv_len, bq, bkv, heads[hm], i, qs, ks)
+                    q_len, kv_len, bq, bkv, head, i, qs, ks, dense=dm)
     return bmask, dnext
+
+
+def partial_blocks(H: int, q_len: int, kv_len: int, bq: int, bkv: int, heads, dense):
+    """Element masks of the partial blocks under a dense mask, and how many
+    distinct ones there are.
+
+    Returns (blocks, distinct): ``blocks`` maps (hm, i, j) of every class-1
+    block to its padded element mask [bq, bkv]; ``distinct`` is the number of
+    different such masks. "hstu_ops.py" fetches the mask of a partial block
+    through an index (``mask_next``, the m index map of the forward) into a
+    store of [bq, bkv] mask blocks, so equal blocks can share one entry.
+    """
+    heads = [tuple(h) for h in heads]
+    dh = _dense_heads(dense, H)
+    Hm = max(len(heads), len(dh))
+    nq = -(-q_len // bq)
+    nk = -(-kv_len // bkv)
+    blocks, seen = {}, set()
+    for hm in range(Hm):
+        head = heads[0] if len(heads) == 1 else heads[hm]
+        dm = dh[0] if len(dh) == 1 else dh[hm]
+        for i in range(nq):
+            m = padded_element_mask(q_len, kv_len, bq, bkv, head, q_block=i, dense=dm)
+            for j in range(nk):
+                blk = m[:, j * bkv:(j + 1) * bkv]
+                c = int(blk.sum())
+                if 0 < c < bq * bkv:
+                    blocks[(hm, i, j)] = blk.copy()
+                    seen.add(blk.tobytes())
+    return blocks, len(seen)
 
 
 def block_flops(block_mask: np.ndarray, B: int, H: int, bq: int, bkv: int, D: int) -> int:
@@ -293,7 +350,7 @@ def _heads_list(heads, H):
     return heads
 
 
-def _attention(kind: str, q, k, v, scale, heads, q_seg, kv_seg, row_chunk: int):
+def _attention(kind: str, q, k, v, scale, heads, q_seg, kv_seg, row_chunk: int, dense=None):
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -301,6 +358,7 @@ def _attention(kind: str, q, k, v, scale, heads, q_seg, kv_seg, row_chunk: int):
     Skv = k.shape[2]
     kv_heads = k.shape[1]
     heads = _heads_list(heads, H)
+    dh = _dense_heads(dense, H)
     out = np.zeros((B, H, Sq, v.shape[3]), dtype=np.float64)
     for b in range(B):
         qs = None if q_seg is None else np.asarray(q_seg)[b]
@@ -308,9 +366,10 @@ def _attention(kind: str, q, k, v, scale, heads, q_seg, kv_seg, row_chunk: int):
         for h in range(H):
             hd = heads[0] if len(heads) == 1 else heads[h]
             hk = kv_head_of(h, H, kv_heads)
+            dm = None if dh is None else (dh[0] if len(dh) == 1 else dh[h])
             for r0 in range(0, Sq, row_chunk):
                 rows = np.arange(r0, min(Sq, r0 + row_chunk))
-                m = element_mask(Sq, Skv, hd, qs, ks, rows=rows)
+                m = element_mask(Sq, Skv, hd, qs, ks, rows=rows, dense=dm)
                 if kind == "softmax":
                     out[b, h, rows] = softmax_attention_rows(q[b, h, rows], k[b, hk], v[b, hk], scale, m)
                 else:
@@ -319,15 +378,15 @@ def _attention(kind: str, q, k, v, scale, heads, q_seg, kv_seg, row_chunk: int):
 
 
 def softmax_attention(q, k, v, scale: float, heads, q_seg=None, kv_seg=None,
-                      row_chunk: int = 512) -> np.ndarray:
+                      row_chunk: int = 512, dense=None) -> np.ndarray:
     """Masked softmax attention [B, H, Sq, Dv] (fp64); rows are independent, so
     the full-score definition is evaluated ``row_chunk`` rows at a time. k and
     v may have fewer heads than q (grouped-query attention, ``kv_head_of``)."""
-    return _attention("softmax", q, k, v, scale, heads, q_seg, kv_seg, row_chunk)
+    return _attention("softmax", q, k, v, scale, heads, q_seg, kv_seg, row_chunk, dense)
 
 
 def pointwise_attention(q, k, v, scale: float, heads, q_seg=None, kv_seg=None,
-                        row_chunk: int = 512) -> np.ndarray:
+                        row_chunk: int = 512, dense=None) -> np.ndarray:
     """Pointwise SiLU attention [B, H, Sq, Dv] (fp64), divided by Sq; k and v
     may have fewer heads than q (``kv_head_of``)."""
-    return _attention("pointwise", q, k, v, scale, heads, q_seg, kv_seg, row_chunk)
+    return _attention("pointwise", q, k, v, scale, heads, q_seg, kv_seg, row_chunk, dense)

@@ -171,6 +171,81 @@ def test_metadata_brute_force_small():
 
 
 # ---------------------------------------------------------------------------
+# dense masks
+# ---------------------------------------------------------------------------
+
+
+def test_dense_lower_triangle_is_the_causal_mask():
+    """A dense mask holding the lower triangle reduces to the causal head mask:
+    same element mask, same metadata."""
+    Sq, Skv, bq, bkv = 200, 230, 32, 64
+    tril = np.tri(Sq, Skv, dtype=bool)
+    np.testing.assert_array_equal(oracle.element_mask(Sq, Skv, FULL, dense=tril),
+                                  oracle.element_mask(Sq, Skv, CAUSAL))
+    a = oracle.mask_info(1, 1, Sq, Skv, bq, bkv, [FULL], dense=tril)
+    c = oracle.mask_info(1, 1, Sq, Skv, bq, bkv, [CAUSAL])
+    np.testing.assert_array_equal(a[0], c[0])
+    np.testing.assert_array_equal(a[1], c[1])
+
+
+def test_dense_metadata_brute_force_small():
+    """Block classes of dense masks ANDed with head bands, by scalar loops."""
+    rng = np.random.default_rng(19)
+    for trial in range(6):
+        Sq, Skv = int(rng.integers(1, 60)), int(rng.integers(1, 60))
+        bq, bkv = int(rng.choice([4, 8, 16])), int(rng.choice([4, 8, 16]))
+        head = (int(rng.integers(0, 2)), int(rng.integers(-1, 12)), int(rng.integers(-1, 12)))
+        dense = rng.random((Sq, Skv)) < rng.choice([0.05, 0.5, 0.95])
+        bm, dn = oracle.mask_info(1, 1, Sq, Skv, bq, bkv, [head], dense=dense)
+        nq, nk = -(-Sq // bq), -(-Skv // bkv)
+        for i in range(nq):
+            for j in range(nk):
+                c = 0
+                for q in range(i * bq, min(Sq, (i + 1) * bq)):
+                    for k in range(j * bkv, min(Skv, (j + 1) * bkv)):
+                        ok = (not head[0] or k <= q) and (head[1] < 0 or k >= q - head[1]) \
+                            and (head[2] < 0 or k <= q + head[2]) and dense[q, k]
+                        c += bool(ok)
+                want = 0 if c == 0 else (2 if c == bq * bkv else 1)
+                assert bm[0, 0, i, j] == want
+
+
+def test_dense_partial_blocks_closed_forms():
+    """Lower-triangular dense mask with square blocks of 32. At S = 256 the
+    partial blocks are the 8 diagonal ones, all equal: one distinct mask. At
+    S = 250 the last block row is ragged (26 of 32 rows), so its blocks left of
+    the diagonal are partial too: 8 diagonal + 7 ragged blocks, with three
+    distinct masks (full triangle, ragged triangle, 26 full rows)."""
+    blocks, n = oracle.partial_blocks(1, 256, 256, 32, 32, [FULL], np.tri(256, 256, dtype=bool))
+    assert sorted(blocks) == [(0, i, i) for i in range(8)] and n == 1
+    blocks, n = oracle.partial_blocks(1, 250, 250, 32, 32, [FULL], np.tri(250, 250, dtype=bool))
+    assert sorted(blocks) == sorted([(0, i, i) for i in range(8)] + [(0, 7, j) for j in range(7)])
+    assert n == 3
+    # a per-head stack: head 1 empty, head 0 full -> no partial blocks at all
+    d = np.stack([np.ones((64, 64), bool), np.zeros((64, 64), bool)])
+    blocks, n = oracle.partial_blocks(2, 64, 64, 16, 16, [FULL], d)
+    assert blocks == {} and n == 0
+
+
+def test_dense_attention_matches_torch_sdpa_fp64():
+    """torch's scaled_dot_product_attention with the boolean mask (dense AND
+    local window) is a library routine of the same definition."""
+    B, H, S, D = 1, 2, 90, 16
+    q, k, v, _, _ = _case(23, B, H, S, S, D)
+    rng = np.random.default_rng(29)
+    dense = rng.random((H, S, S)) < 0.4
+    dense[:, np.arange(S), np.arange(S)] = True  # every row keeps a key
+    head = (0, 30, 30)
+    got = oracle.softmax_attention(q, k, v, 0.25, [head], dense=dense, row_chunk=40)
+    for h in range(H):
+        m = oracle.element_mask(S, S, head) & dense[h]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[0, h]), torch.from_numpy(k[0, h]), torch.from_numpy(v[0, h]),
+            attn_mask=torch.from_numpy(m), scale=0.25).numpy()
+        np.testing.assert_allclose(got[0, h], ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # softmax attention
 # ---------------------------------------------------------------------------
 
