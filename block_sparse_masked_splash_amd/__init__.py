@@ -8,6 +8,7 @@ it. ``workloads`` holds the seeded synthetic inputs.
 from .binding import (  # noqa: F401
     MaskInfo,
     SplashError,
+    dense_mask_info_build,
     load_library,
     mask_info_build,
     pointwise_fwd,

@@ -34,6 +34,8 @@ SYMBOLS = (
     "splash_pointwise_fwd",
     "splash_gqa_fwd",
     "splash_gqa_pointwise_fwd",
+    "splash_dense_mask_info_host",
+    "splash_masked_fwd",
     "splash_status_string",
     "splash_last_error",
     "splash_abi_version",
@@ -63,6 +65,10 @@ class MaskInfoC(ctypes.Structure):
                 ("block_mask", ctypes.c_void_p), ("data_next", ctypes.c_void_p)]
 
 
+class PartialMasksC(ctypes.Structure):
+    _fields_ = [("mask_next", ctypes.c_void_p), ("mask_blocks", ctypes.c_void_p), ("num_blocks", ctypes.c_int64)]
+
+
 _I64x3 = ctypes.c_int64 * 3
 _FWD_ARGS = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
              ctypes.c_int,
@@ -73,6 +79,8 @@ _FWD_ARGS = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_in
              ctypes.c_float, ctypes.POINTER(MaskDescC), ctypes.POINTER(MaskInfoC), ctypes.c_void_p]
 # grouped-query forms: kv_heads follows H
 _GQA_ARGS = _FWD_ARGS[:4] + [ctypes.c_int] + _FWD_ARGS[4:]
+# general form: pointwise flag first, partial masks before the stream
+_MASKED_ARGS = [ctypes.c_int] + _GQA_ARGS[:-1] + [ctypes.POINTER(PartialMasksC), ctypes.c_void_p]
 
 _lib = None
 
@@ -100,6 +108,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = _GQA_ARGS
+    lib.splash_masked_fwd.restype = ctypes.c_int
+    lib.splash_masked_fwd.argtypes = _MASKED_ARGS
+    lib.splash_dense_mask_info_host.restype = ctypes.c_int
+    lib.splash_dense_mask_info_host.argtypes = (
+        [ctypes.c_int] * 5 + [ctypes.POINTER(HeadMaskC), ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+        + [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)])
     lib.splash_status_string.restype = ctypes.c_char_p
     lib.splash_status_string.argtypes = [ctypes.c_int]
     lib.splash_last_error.restype = ctypes.c_char_p
@@ -151,6 +165,19 @@ class MaskInfo:
     kv_segment_ids: torch.Tensor | None
     block_mask: torch.Tensor   # int8 [meta_batch, meta_heads, nq, nk]
     data_next: torch.Tensor    # int32, same shape
+    # dense masks only: mask_next int32 (same shape) and the store of partial
+    # blocks, int32 [num_blocks, block_q, block_kv // 32] (bits, see splash.h)
+    mask_next: torch.Tensor | None = None
+    mask_blocks: torch.Tensor | None = None
+
+    @property
+    def dense(self) -> bool:
+        return self.mask_next is not None
+
+    def partial_struct(self):
+        n = 0 if self.mask_blocks is None else self.mask_blocks.shape[0]
+        return PartialMasksC(self.mask_next.data_ptr() if self.mask_next.numel() else None,
+                             self.mask_blocks.data_ptr() if n else None, n)
 
     def mask_desc(self):
         arr, n = _head_array(self.head_masks)
@@ -168,6 +195,52 @@ class MaskInfo:
 
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def dense_mask_info_build(B: int, H: int, dense, head_masks=((0, -1, -1),), block_q: int = 128,
+                          block_kv: int = 128, device="cuda") -> MaskInfo:
+    """Metadata of an arbitrary dense mask ANDed with head masks, built on the
+    host by the library and copied to ``device``.
+
+    ``dense``: boolean [q_len, kv_len] (shared by all heads) or [H, q_len,
+    kv_len]; ``head_masks``: 1 or H (causal, window_left, window_right)
+    triples. No segment ids."""
+    lib = load_library()
+    d = torch.as_tensor(dense).to("cpu")
+    if d.dim() == 2:
+        d = d.unsqueeze(0)
+    if d.dim() != 3 or d.shape[0] not in (1, H):
+        raise ValueError("dense must be [q_len, kv_len] or [H, q_len, kv_len]")
+    d = d.to(torch.uint8).contiguous()
+    Hd, q_len, kv_len = d.shape
+    head_masks = tuple(tuple(int(x) for x in m) for m in head_masks)
+    if len(head_masks) not in (1, H) or len(head_masks) > MAX_MASK_HEADS:
+        raise ValueError("head_masks must hold 1 or H entries")
+    Hm = max(Hd, len(head_masks))
+    nq = -(-q_len // block_q) if block_q > 0 else 0
+    nk = -(-kv_len // block_kv) if block_kv > 0 else 0
+    arr, nmh = _head_array(head_masks)
+    heads_p = ctypes.cast(arr, ctypes.POINTER(HeadMaskC))
+    count = ctypes.c_int64(0)
+    st = lib.splash_dense_mask_info_host(q_len, kv_len, block_q, block_kv, nmh, heads_p, Hd, d.data_ptr(), Hm,
+                                         None, None, None, None, 0, ctypes.byref(count))
+    _check(st)
+    n = count.value
+    shape = (1, Hm, nq, nk)
+    entries = Hm * nq * nk
+    bmask = torch.empty((entries + 3) // 4 * 4, dtype=torch.int8)
+    dnext = torch.empty(shape, dtype=torch.int32)
+    mnext = torch.empty(shape, dtype=torch.int32)
+    wpr = block_kv // 32
+    blocks = torch.empty((n, block_q, wpr), dtype=torch.int32)
+    st = lib.splash_dense_mask_info_host(q_len, kv_len, block_q, block_kv, nmh, heads_p, Hd, d.data_ptr(), Hm,
+                                         bmask.data_ptr(), dnext.data_ptr(), mnext.data_ptr(),
+                                         blocks.data_ptr() if n else None, n, ctypes.byref(count))
+    _check(st)
+    device = torch.device(device)
+    bmask_dev = bmask.to(device)[:entries].view(shape)
+    return MaskInfo(B, H, q_len, kv_len, block_q, block_kv, head_masks, None, None, bmask_dev,
+                    dnext.to(device), mnext.to(device), blocks.to(device))
 
 
 def mask_info_build(B: int, H: int, q_len: int, kv_len: int, head_masks, block_q: int = 128,
@@ -256,7 +329,11 @@ def _forward(pointwise: bool, q, k, v, info: MaskInfo, scale, out, out_dtype, la
     cinfo = info.info_struct()
     tail = (q.data_ptr(), qs, k.data_ptr(), ks, v.data_ptr(), vs, out.data_ptr(), os_,
             float(scale), ctypes.byref(desc), ctypes.byref(cinfo), ctypes.c_void_p(_stream(q.device)))
-    if Hk == H:
+    if info.dense:
+        part = info.partial_struct()
+        st = lib.splash_masked_fwd(int(pointwise), _DT[q.dtype], _DT[out_dtype], B, H, Hk, Sq, Skv, D,
+                                   *tail[:-1], ctypes.byref(part), tail[-1])
+    elif Hk == H:
         fn = lib.splash_pointwise_fwd if pointwise else lib.splash_fwd
         st = fn(_DT[q.dtype], _DT[out_dtype], B, H, Sq, Skv, D, *tail)
     else:

@@ -16,10 +16,12 @@
 #include "internal.h"
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-splash_status fail(splash_status s, const char* fmt, ...) {
+namespace splash {
+
+splash_status record_error(splash_status s, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -29,10 +31,35 @@ splash_status fail(splash_status s, const char* fmt, ...) {
   return s;
 }
 
-splash_status ok() {
+splash_status record_ok() {
   g_last_error.clear();
   return SPLASH_OK;
 }
+
+bool head_band(const splash_head_mask& m, int index, HeadBand* out) {
+  if (m.causal != 0 && m.causal != 1) {
+    record_error(SPLASH_ERR_INVALID_ARGUMENT, "head %d: causal=%d must be 0 or 1", index, m.causal);
+    return false;
+  }
+  if (m.window_left < -1 || m.window_right < -1) {
+    record_error(SPLASH_ERR_INVALID_ARGUMENT, "head %d: window bounds must be >= -1", index);
+    return false;
+  }
+  int32_t lo = m.window_left >= 0 ? -m.window_left : -kUnbounded;
+  int32_t hi = m.window_right >= 0 ? m.window_right : kUnbounded;
+  if (m.causal && hi > 0) hi = 0;
+  if (lo < -kUnbounded) lo = -kUnbounded;
+  if (hi > kUnbounded) hi = kUnbounded;
+  *out = {lo, hi};
+  return true;
+}
+
+}  // namespace splash
+
+namespace {
+
+using splash::record_error;
+splash_status ok() { return splash::record_ok(); }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -40,53 +67,42 @@ bool len_ok(int x) { return x >= 0 && x <= splash::kMaxLen; }
 
 // Checks the mask description against B and H; fills the head bands.
 splash_status check_mask(int H, const splash_mask_desc* mask, splash::HeadBand* band) {
-  if (mask == nullptr) return fail(SPLASH_ERR_INVALID_ARGUMENT, "mask is null");
+  if (mask == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "mask is null");
   const int nm = mask->num_mask_heads;
   if (nm < 1 || nm > SPLASH_MAX_MASK_HEADS)
-    return fail(nm < 1 ? SPLASH_ERR_INVALID_ARGUMENT : SPLASH_ERR_UNSUPPORTED,
+    return record_error(nm < 1 ? SPLASH_ERR_INVALID_ARGUMENT : SPLASH_ERR_UNSUPPORTED,
                 "num_mask_heads=%d must be 1 or H, at most %d", nm, SPLASH_MAX_MASK_HEADS);
-  if (nm != 1 && nm != H) return fail(SPLASH_ERR_INVALID_ARGUMENT, "num_mask_heads=%d is neither 1 nor H=%d", nm, H);
-  if (mask->heads == nullptr) return fail(SPLASH_ERR_INVALID_ARGUMENT, "mask->heads is null");
+  if (nm != 1 && nm != H) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "num_mask_heads=%d is neither 1 nor H=%d", nm, H);
+  if (mask->heads == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "mask->heads is null");
   if ((mask->q_segment_ids == nullptr) != (mask->kv_segment_ids == nullptr))
-    return fail(SPLASH_ERR_INVALID_ARGUMENT, "both or neither of q_segment_ids and kv_segment_ids must be given");
-  for (int h = 0; h < nm; ++h) {
-    const splash_head_mask m = mask->heads[h];
-    if (m.causal != 0 && m.causal != 1)
-      return fail(SPLASH_ERR_INVALID_ARGUMENT, "head %d: causal=%d must be 0 or 1", h, m.causal);
-    if (m.window_left < -1 || m.window_right < -1)
-      return fail(SPLASH_ERR_INVALID_ARGUMENT, "head %d: window bounds must be >= -1", h);
-    int32_t lo = m.window_left >= 0 ? -m.window_left : -splash::kUnbounded;
-    int32_t hi = m.window_right >= 0 ? m.window_right : splash::kUnbounded;
-    if (m.causal && hi > 0) hi = 0;
-    if (lo < -splash::kUnbounded) lo = -splash::kUnbounded;
-    if (hi > splash::kUnbounded) hi = splash::kUnbounded;
-    band[h] = {lo, hi};
-  }
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "both or neither of q_segment_ids and kv_segment_ids must be given");
+  for (int h = 0; h < nm; ++h)
+    if (!splash::head_band(mask->heads[h], h, &band[h])) return SPLASH_ERR_INVALID_ARGUMENT;
   return SPLASH_OK;
 }
 
 splash_status check_sizes(int B, int H, int q_len, int kv_len) {
   if (B < 0 || H < 0 || !len_ok(q_len) || !len_ok(kv_len) || B > (1 << 24) || H > (1 << 16))
-    return fail(SPLASH_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d q_len=%d kv_len=%d", B, H, q_len, kv_len);
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d q_len=%d kv_len=%d", B, H, q_len, kv_len);
   return SPLASH_OK;
 }
 
 splash_status hip_status(hipError_t e, const char* what) {
-  if (e != hipSuccess) return fail(SPLASH_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  if (e != hipSuccess) return record_error(SPLASH_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
 }
 
 splash_status check_tensor(const char* name, const void* ptr, const int64_t* strides, int elem_bytes,
                            bool needed) {
-  if (strides == nullptr) return fail(SPLASH_ERR_INVALID_ARGUMENT, "%s strides are null", name);
+  if (strides == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s strides are null", name);
   if (!needed) return SPLASH_OK;
-  if (ptr == nullptr) return fail(SPLASH_ERR_INVALID_ARGUMENT, "%s is null", name);
+  if (ptr == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s is null", name);
   if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
-    return fail(SPLASH_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
   for (int a = 0; a < 3; ++a) {
-    if (strides[a] < 0) return fail(SPLASH_ERR_INVALID_ARGUMENT, "%s stride %d is negative", name, a);
+    if (strides[a] < 0) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s stride %d is negative", name, a);
     if ((strides[a] * elem_bytes) % 16 != 0)
-      return fail(SPLASH_ERR_INVALID_ARGUMENT, "%s stride %d (%lld elements) breaks 16-byte row alignment", name, a,
+      return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s stride %d (%lld elements) breaks 16-byte row alignment", name, a,
                   (long long)strides[a]);
   }
   return SPLASH_OK;
@@ -96,25 +112,25 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
                          int q_len, int kv_len, int head_dim, const void* q, const int64_t q_strides[3], const void* k,
                          const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* o,
                          const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
-                         const splash_mask_info* info, hipStream_t stream) {
+                         const splash_mask_info* info, const splash_partial_masks* partial, hipStream_t stream) {
   splash_status s = check_sizes(B, H, q_len, kv_len);
   if (s != SPLASH_OK) return s;
   if (kv_heads < 1 || kv_heads > H || H % kv_heads != 0)
-    return fail(SPLASH_ERR_INVALID_ARGUMENT, "kv_heads=%d must divide H=%d", kv_heads, H);
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "kv_heads=%d must divide H=%d", kv_heads, H);
   const bool f32 = in_dtype == SPLASH_F32 && out_dtype == SPLASH_F32;
   const bool bf16 = in_dtype == SPLASH_BF16 && (out_dtype == SPLASH_BF16 || out_dtype == SPLASH_F32);
   if (!f32 && !bf16)
-    return fail(SPLASH_ERR_UNSUPPORTED, "dtype pair in=%d out=%d (supported: f32->f32, bf16->bf16, bf16->f32)",
+    return record_error(SPLASH_ERR_UNSUPPORTED, "dtype pair in=%d out=%d (supported: f32->f32, bf16->bf16, bf16->f32)",
                 (int)in_dtype, (int)out_dtype);
-  if (head_dim <= 0) return fail(SPLASH_ERR_INVALID_ARGUMENT, "head_dim=%d", head_dim);
+  if (head_dim <= 0) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "head_dim=%d", head_dim);
   if (head_dim != 64 && head_dim != 128)
-    return fail(SPLASH_ERR_UNSUPPORTED, "head_dim=%d (supported: 64, 128)", head_dim);
-  if (!std::isfinite(scale)) return fail(SPLASH_ERR_INVALID_ARGUMENT, "scale is not finite");
+    return record_error(SPLASH_ERR_UNSUPPORTED, "head_dim=%d (supported: 64, 128)", head_dim);
+  if (!std::isfinite(scale)) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "scale is not finite");
 
   splash::FwdParams p{};
   s = check_mask(H, mask, p.band);
   if (s != SPLASH_OK) return s;
-  if (info == nullptr) return fail(SPLASH_ERR_INVALID_ARGUMENT, "info is null");
+  if (info == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "info is null");
 
   const bool work = (int64_t)B * H * q_len > 0;
   const int in_bytes = in_dtype == SPLASH_F32 ? 4 : 2;
@@ -125,26 +141,40 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
   if ((s = check_tensor("o", o, o_strides, out_bytes, work)) != SPLASH_OK) return s;
 
   const bool seg = mask->q_segment_ids != nullptr;
+  if (partial != nullptr && seg)
+    return record_error(SPLASH_ERR_UNSUPPORTED, "dense-mask metadata is built without segment ids");
   const int bq = info->block_q, bkv = info->block_kv;
-  if (bq <= 0 || bkv <= 0) return fail(SPLASH_ERR_METADATA_MISMATCH, "info block sizes %d x %d", bq, bkv);
+  if (bq <= 0 || bkv <= 0) return record_error(SPLASH_ERR_METADATA_MISMATCH, "info block sizes %d x %d", bq, bkv);
   const int64_t nq = ceil_div(q_len, bq), nk = ceil_div(kv_len, bkv);
-  if (info->meta_batch != (seg ? B : 1) || info->meta_heads != mask->num_mask_heads || info->num_q_blocks != nq ||
-      info->num_kv_blocks != nk)
-    return fail(SPLASH_ERR_METADATA_MISMATCH,
-                "info [%d,%d,%d,%d] but this call needs [%d,%d,%lld,%lld] (segment ids %s)", info->meta_batch,
-                info->meta_heads, info->num_q_blocks, info->num_kv_blocks, seg ? B : 1, mask->num_mask_heads,
-                (long long)nq, (long long)nk, seg ? "given" : "absent");
+  // metadata heads: those of the head masks, or (dense masks) 1 or H with the
+  // head masks 1 or as many
+  const int nm = mask->num_mask_heads;
+  const bool heads_ok = partial == nullptr ? info->meta_heads == nm
+                                           : ((info->meta_heads == 1 || info->meta_heads == H) &&
+                                              (nm == 1 || nm == info->meta_heads));
+  if (info->meta_batch != (seg ? B : 1) || !heads_ok || info->num_q_blocks != nq || info->num_kv_blocks != nk)
+    return record_error(SPLASH_ERR_METADATA_MISMATCH,
+                "info [%d,%d,%d,%d] but this call needs [%d,%d,%lld,%lld] (segment ids %s%s)", info->meta_batch,
+                info->meta_heads, info->num_q_blocks, info->num_kv_blocks, seg ? B : 1, nm, (long long)nq,
+                (long long)nk, seg ? "given" : "absent", partial ? ", dense masks" : "");
   if ((bq != 64 && bq != 128 && bq != 256) || (bkv != 64 && bkv != 128))
-    return fail(SPLASH_ERR_UNSUPPORTED, "block sizes %d x %d (supported: block_q 64, 128 or 256; block_kv 64 or 128)",
+    return record_error(SPLASH_ERR_UNSUPPORTED, "block sizes %d x %d (supported: block_q 64, 128 or 256; block_kv 64 or 128)",
                 bq, bkv);
   if (work && nk > 0 && (info->block_mask == nullptr || info->data_next == nullptr))
-    return fail(SPLASH_ERR_INVALID_ARGUMENT, "info arrays are null");
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "info arrays are null");
+  if (partial != nullptr) {
+    if (partial->num_blocks < 0 || partial->num_blocks > ((int64_t)1 << 31))
+      return record_error(SPLASH_ERR_INVALID_ARGUMENT, "num_blocks=%lld", (long long)partial->num_blocks);
+    if (work && nk > 0 && (partial->mask_next == nullptr || (partial->num_blocks > 0 && partial->mask_blocks == nullptr)))
+      return record_error(SPLASH_ERR_INVALID_ARGUMENT, "dense mask arrays are null");
+  }
   if (!work) return ok();
   if (nq * B * H >= (int64_t)1 << 31)
-    return fail(SPLASH_ERR_UNSUPPORTED, "%lld workgroups exceed one launch", (long long)(nq * B * H));
+    return record_error(SPLASH_ERR_UNSUPPORTED, "%lld workgroups exceed one launch", (long long)(nq * B * H));
 
   p.B = B;
   p.H = H;
+  p.band_heads = nm;
   p.kv_heads = kv_heads;
   p.kv_group = H / kv_heads;
   p.q_len = q_len;
@@ -165,12 +195,17 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
   p.block_kv = bkv;
   p.nq = (int)nq;
   p.nk = (int)nk;
-  p.meta_heads = mask->num_mask_heads;
+  p.meta_heads = info->meta_heads;
   p.meta_batch = seg ? B : 1;
   p.block_mask = info->block_mask;
   p.data_next = info->data_next;
   p.q_seg = mask->q_segment_ids;
   p.kv_seg = mask->kv_segment_ids;
+  if (partial != nullptr) {
+    p.mask_next = partial->mask_next;
+    p.mask_blocks = partial->num_blocks > 0 ? partial->mask_blocks : nullptr;
+    p.num_mask_blocks = partial->num_blocks;
+  }
 
   hipError_t e = f32 ? splash::launch_fwd_f32(p, pointwise, stream)
                      : splash::launch_fwd_bf16(p, pointwise, out_dtype == SPLASH_F32, stream);
@@ -213,24 +248,24 @@ splash_status splash_mask_info_build(int B, int H, int q_len, int kv_len, int bl
   splash_status s = check_sizes(B, H, q_len, kv_len);
   if (s != SPLASH_OK) return s;
   if (block_q < 1 || block_q > 1024 || block_kv < 1 || block_kv > 1024)
-    return fail(SPLASH_ERR_INVALID_ARGUMENT, "block sizes %d x %d must be in [1, 1024]", block_q, block_kv);
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "block sizes %d x %d must be in [1, 1024]", block_q, block_kv);
   splash::MaskInfoParams p{};
   s = check_mask(H, mask, p.band);
   if (s != SPLASH_OK) return s;
-  if (info == nullptr) return fail(SPLASH_ERR_INVALID_ARGUMENT, "info is null");
+  if (info == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "info is null");
   const bool seg = mask->q_segment_ids != nullptr;
   const int64_t nq = ceil_div(q_len, block_q), nk = ceil_div(kv_len, block_kv);
   if (info->meta_batch != (seg ? B : 1) || info->meta_heads != mask->num_mask_heads || info->num_q_blocks != nq ||
       info->num_kv_blocks != nk || info->block_q != block_q || info->block_kv != block_kv)
-    return fail(SPLASH_ERR_INVALID_ARGUMENT, "info fields [%d,%d,%d,%d] blocks %dx%d do not describe this call",
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "info fields [%d,%d,%d,%d] blocks %dx%d do not describe this call",
                 info->meta_batch, info->meta_heads, info->num_q_blocks, info->num_kv_blocks, info->block_q,
                 info->block_kv);
   const int64_t entries = (int64_t)info->meta_batch * info->meta_heads * nq * nk;
   if (entries == 0) return ok();
   if ((int64_t)info->meta_batch * info->meta_heads * nq / 4 >= ((int64_t)1 << 31))
-    return fail(SPLASH_ERR_UNSUPPORTED, "too many metadata rows for one launch");
+    return record_error(SPLASH_ERR_UNSUPPORTED, "too many metadata rows for one launch");
   if (info->block_mask == nullptr || info->data_next == nullptr)
-    return fail(SPLASH_ERR_INVALID_ARGUMENT, "info arrays are null");
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "info arrays are null");
   p.B = B;
   p.H = H;
   p.q_len = q_len;
@@ -254,7 +289,7 @@ splash_status splash_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, i
                          const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
                          const splash_mask_info* info, hipStream_t stream) {
   return fwd_common(false, in_dtype, out_dtype, B, H, H, q_len, kv_len, head_dim, q, q_strides, k, k_strides, v,
-                    v_strides, o, o_strides, scale, mask, info, stream);
+                    v_strides, o, o_strides, scale, mask, info, nullptr, stream);
 }
 
 splash_status splash_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int q_len,
@@ -264,7 +299,7 @@ splash_status splash_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_dtype
                                    const splash_mask_desc* mask, const splash_mask_info* info,
                                    hipStream_t stream) {
   return fwd_common(true, in_dtype, out_dtype, B, H, H, q_len, kv_len, head_dim, q, q_strides, k, k_strides, v,
-                    v_strides, o, o_strides, scale, mask, info, stream);
+                    v_strides, o, o_strides, scale, mask, info, nullptr, stream);
 }
 
 splash_status splash_gqa_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads, int q_len,
@@ -273,7 +308,7 @@ splash_status splash_gqa_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int 
                              const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
                              const splash_mask_info* info, hipStream_t stream) {
   return fwd_common(false, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides,
-                    v, v_strides, o, o_strides, scale, mask, info, stream);
+                    v, v_strides, o, o_strides, scale, mask, info, nullptr, stream);
 }
 
 splash_status splash_gqa_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
@@ -283,7 +318,19 @@ splash_status splash_gqa_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_d
                                        const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
                                        const splash_mask_info* info, hipStream_t stream) {
   return fwd_common(true, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides,
-                    v, v_strides, o, o_strides, scale, mask, info, stream);
+                    v, v_strides, o, o_strides, scale, mask, info, nullptr, stream);
+}
+
+splash_status splash_masked_fwd(int pointwise, splash_dtype in_dtype, splash_dtype out_dtype, int B, int H,
+                                int kv_heads, int q_len, int kv_len, int head_dim, const void* q,
+                                const int64_t q_strides[3], const void* k, const int64_t k_strides[3], const void* v,
+                                const int64_t v_strides[3], void* o, const int64_t o_strides[3], float scale,
+                                const splash_mask_desc* mask, const splash_mask_info* info,
+                                const splash_partial_masks* partial, hipStream_t stream) {
+  if (pointwise != 0 && pointwise != 1)
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "pointwise=%d must be 0 or 1", pointwise);
+  return fwd_common(pointwise == 1, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k,
+                    k_strides, v, v_strides, o, o_strides, scale, mask, info, partial, stream);
 }
 
 }  // extern "C"

@@ -18,6 +18,14 @@ struct HeadBand {
   int32_t hi;
 };
 
+// Host side, shared by the C-ABI translation units (defined in api.cpp).
+// Records a failure for splash_last_error() and returns s.
+splash_status record_error(splash_status s, const char* fmt, ...);
+// Clears the last error and returns SPLASH_OK.
+splash_status record_ok();
+// Band of one head mask; false (and a recorded error) for invalid fields.
+bool head_band(const splash_head_mask& m, int index, HeadBand* out);
+
 struct MaskInfoParams {
   int B, H, q_len, kv_len, block_q, block_kv;
   int nq, nk, meta_batch, meta_heads;
@@ -30,6 +38,7 @@ struct MaskInfoParams {
 
 struct FwdParams {
   int B, H, q_len, kv_len, head_dim;
+  int band_heads;    // head masks in band[] (1: shared by every head)
   int kv_heads;      // K/V heads; query head h reads kv head h / kv_group
   int kv_group;      // H / kv_heads
   const void* q;
@@ -50,6 +59,11 @@ struct FwdParams {
   const int32_t* data_next;
   const int32_t* q_seg;
   const int32_t* kv_seg;
+  // dense masks: for a partial block, mask_next names its entry of
+  // mask_blocks ([num_mask_blocks][block_q][block_kv / 32] bits); null if none
+  const int32_t* mask_next;
+  const uint32_t* mask_blocks;
+  int64_t num_mask_blocks;
   HeadBand band[SPLASH_MAX_MASK_HEADS];
 };
 

@@ -263,9 +263,13 @@ struct Tiling {
   static constexpr int SEG_KEYS = KC / NW;      // segment ids loaded per wave per tile
   static constexpr int NS = D / 16;             // k-steps of the QKᵀ contraction
   static constexpr int ND = D / 32;             // 32-wide output blocks
-  // LDS: [stage][K | V][TILE] then [stage][KC] int32 segment ids
+  static constexpr int WPT = KC / 32;           // dense-mask words per query row per tile
+  static constexpr int DM_WORDS = NW * 32 * WPT; // dense-mask words per tile (every row of the block)
+  // LDS: [stage][K | V][TILE], [stage][KC] int32 segment ids, [stage][DM_WORDS]
+  // dense-mask words
   static constexpr int SEG_OFF = 2 * 2 * TILE;
-  static constexpr int LDS_BYTES = SEG_OFF + 2 * KC * 4;
+  static constexpr int DM_OFF = SEG_OFF + 2 * KC * 4;
+  static constexpr int LDS_BYTES = DM_OFF + 2 * DM_WORDS * 4;
 };
 
 // Wavefronts per SIMD: at D = 128 a wavefront needs up to 168 VGPRs, so
@@ -313,7 +317,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
   const int h = hk * p.kv_group + (rest - ri * p.kv_group);
   const int hm = p.meta_heads == 1 ? 0 : h;
   const int bm = p.meta_batch == 1 ? 0 : b;
-  const HeadBand band = p.band[hm];
+  const HeadBand band = p.band[p.band_heads == 1 ? 0 : h];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -394,7 +398,15 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
     kvsel[n] = kvo[(n * NW + wave) & 3];
     vvsel[n] = vvo[(n * NW + wave) & 3];
   }
-  auto issue_tile = [&](int stage, int key0) {
+  const int64_t mrow = (((int64_t)bm * p.meta_heads + hm) * p.nq + i) * p.nk;
+  const int8_t* bmask = p.block_mask + mrow;
+  const int32_t* dnext = p.data_next + mrow;
+  const bool dense = p.mask_blocks != nullptr;
+
+  // Copy of tile (block j, offset t): K and V rows, their segment ids, and for
+  // a partial block of a dense mask the block's bits of this tile's keys.
+  auto issue_tile = [&](int stage, int j, int t) {
+    const int key0 = j * p.block_kv + t;
     char* kdst = smem + stage * 2 * T::TILE;
     char* vdst = kdst + T::TILE;
     const int rows = p.kv_len - key0 < KC ? p.kv_len - key0 : KC;  // rows past the end read as 0
@@ -408,6 +420,19 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
       const uint32_t sdst = lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * KC + wave * T::SEG_KEYS);
       const u32x4 srs = buffer_rsrc(kvseg_g + key0, (uint32_t)(rows * 4));
       if (lane < T::SEG_KEYS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_KEYS * 4), sdst);
+    }
+    if (dense && block_class(bmask, j) == 1) {
+      int m = scalar_load_i32(p.mask_next + mrow + j);
+      m = m < 0 ? 0 : (m >= p.num_mask_blocks ? (int)p.num_mask_blocks - 1 : m);  // any content stays in the store
+      const int wpr = p.block_kv / 32;
+      const u32x4 drs = buffer_rsrc(p.mask_blocks + (int64_t)m * p.block_q * wpr, (uint32_t)(p.block_q * wpr * 4));
+      const uint32_t* ddst = reinterpret_cast<const uint32_t*>(smem + T::DM_OFF) + stage * T::DM_WORDS;
+      // word e of the tile: row e / WPT, word t / 32 + e % WPT of that row
+      for (int e0 = wave * 64; e0 < T::DM_WORDS; e0 += NW * 64) {
+        const int e = e0 + lane;
+        const uint32_t voff = (uint32_t)(((e / T::WPT) * wpr + t / 32 + e % T::WPT) * 4);
+        if (e < T::DM_WORDS) lds_copy4(drs, voff, 0u, lds_addr(ddst + e0));
+      }
     }
   };
 
@@ -425,9 +450,6 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
   float mref = kNegInf;  // reference max (log2 domain), shared by O and L
   float lsum = 0.0f;     // this lane's share of L
 
-  const int64_t mrow = (((int64_t)bm * p.meta_heads + hm) * p.nq + i) * p.nk;
-  const int8_t* bmask = p.block_mask + mrow;
-  const int32_t* dnext = p.data_next + mrow;
 
   // Walk: tiles of KC keys inside the non-empty blocks reached through
   // data_next. data_next is only followed forward and within [0, nk], so any
@@ -439,7 +461,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
   int cur_j = p.nk > 0 ? scalar_load_i32(dnext) : p.nk;
   if (cur_j < 0 || cur_j > p.nk) cur_j = p.nk;
   int cur_t = 0;
-  if (cur_j < p.nk) issue_tile(0, cur_j * p.block_kv);
+  if (cur_j < p.nk) issue_tile(0, cur_j, 0);
 
   // One tile in LDS stage STAGE (a compile-time constant, so every tile
   // address is a per-lane offset plus an immediate). Returns whether another
@@ -455,7 +477,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
     // After this barrier every wave's copies of the current tile are in LDS and
     // every wave is done with the previous tile, whose stage is refilled now.
     barrier_only();
-    if (nxt_j < p.nk) issue_tile(stage ^ 1, nxt_j * p.block_kv + nxt_t);
+    if (nxt_j < p.nk) issue_tile(stage ^ 1, nxt_j, nxt_t);
 
     const int k0 = cur_j * p.block_kv + cur_t;
     const bool partial = block_class(bmask, cur_j) == 1;
@@ -463,6 +485,8 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
     const char* vt = kt + T::TILE;
 
     const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * KC;
+    const uint32_t* dmw = reinterpret_cast<const uint32_t*>(smem + T::DM_OFF) + stage * T::DM_WORDS +
+                          (wave * 32 + l32) * T::WPT;  // this row's dense-mask words of the tile
     // The tile is processed in parts of 32 keys (kb), each: Sᵀ, softmax, Oᵀ += Vᵀ Pᵀ.
 #pragma unroll
     for (int kb = 0; kb < KC / 32; ++kb) {
@@ -488,6 +512,8 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
 #pragma unroll
           for (int u = 0; u < 4; ++u) kseg4[u] = *reinterpret_cast<const int4*>(sseg + 32 * kb + 8 * u + 4 * hh);
         }
+        // dense mask: bit 8 (r / 4) + r % 4 of this word for score r (all ones without one)
+        const uint32_t dbits = dense ? dmw[kb] >> (4 * hh) : 0xffffffffu;
         int a = qrow + band.lo - k0;
         int e = qrow + band.hi - k0;
         a = a > 0 ? a : 0;
@@ -499,7 +525,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kc = 32 * kb + 8 * (r >> 2) + (r & 3);
-          bool ok = (uint32_t)(base + kc) <= width;
+          bool ok = ((uint32_t)(base + kc) <= width) & ((dbits >> (8 * (r >> 2) + (r & 3))) & 1u);
           if constexpr (kSeg) ok &= kseg4[r >> 2][r & 3] == myseg;
           sacc[r] = ok ? sacc[r] : (PW ? 0.0f : kNegInf);
         }

@@ -6,7 +6,9 @@
 // pointwise forward): one workgroup per (b, h, q block), kv blocks reached
 // through data_next, element mask only on class-1 blocks, online softmax
 // per kv tile of 32 keys. Each query row is owned by D/32 adjacent lanes,
-// each holding 32 of the head dimensions of q and of the accumulator.
+// each holding 32 of the head dimensions of q and of the accumulator. With a
+// dense mask, a partial block's bits (its entry of the mask store) are ANDed
+// into the element mask.
 
 #include "internal.h"
 
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(BQ*(D / 32)) void splash_fwd_f32_kernel(FwdParams p
   const int h = bh % p.H;
   const int hm = p.meta_heads == 1 ? 0 : h;
   const int bm = p.meta_batch == 1 ? 0 : b;
-  const HeadBand band = p.band[hm];
+  const HeadBand band = p.band[p.band_heads == 1 ? 0 : h];
 
   const float* qg = reinterpret_cast<const float*>(p.q) + b * p.q_sb + h * p.q_sh;
   const int hk = h / p.kv_group;  // K/V head read by query head h
@@ -71,8 +73,17 @@ __global__ __launch_bounds__(BQ*(D / 32)) void splash_fwd_f32_kernel(FwdParams p
   // content ends the walk in bounds.
   int j = p.nk > 0 ? dnext[0] : p.nk;
   if (j < 0 || j > p.nk) j = p.nk;
+  const bool dense = p.mask_blocks != nullptr;
+  const int wpr = p.block_kv / 32;
   while (j < p.nk) {
     const bool partial = bmask[j] == 1;
+    // dense mask: this row's bits of block j (row i * BQ + rl of the block store entry)
+    const uint32_t* drow = nullptr;
+    if (partial && dense) {
+      int m = p.mask_next[mrow + j];
+      m = m < 0 ? 0 : (m >= p.num_mask_blocks ? (int)p.num_mask_blocks - 1 : m);  // any content stays in the store
+      drow = p.mask_blocks + ((int64_t)m * p.block_q + rl) * wpr;
+    }
     for (int t = 0; t < p.block_kv; t += KT) {
       const int k0 = j * p.block_kv + t;
       if (k0 >= p.kv_len) break;
@@ -108,6 +119,7 @@ __global__ __launch_bounds__(BQ*(D / 32)) void splash_fwd_f32_kernel(FwdParams p
           const int kv = k0 + kk;
           const int dlt = kv - qrow;
           ok[kk] = kv < p.kv_len && dlt >= band.lo && dlt <= band.hi && (!has_seg || sKseg[kk] == my_qseg);
+          if (drow != nullptr) ok[kk] = ok[kk] && ((drow[(t + kk) >> 5] >> ((t + kk) & 31)) & 1u);
         }
       }
       if constexpr (PW) {

@@ -190,6 +190,62 @@ splash_status splash_gqa_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_d
                                        float scale, const splash_mask_desc* mask,
                                        const splash_mask_info* info, hipStream_t stream);
 
+/* Dense masks ("hstu_ops.py", pointwise_splash_attention: a numpy array mask
+ * of shape (q_len, kv_len) becomes a NumpyMask, ANDed with the local window;
+ * the forward fetches the mask of a partial block through a second index map,
+ * mask_next, into a store of mask blocks, so equal partial blocks share one
+ * entry).
+ *
+ * splash_dense_mask_info_host builds, on the host, the metadata of the mask
+ *   allowed(h, q, k) = dense[h', q, k] != 0 AND the band of head mask h'',
+ * with h' = 0 if dense_heads == 1 else h, h'' likewise for num_mask_heads,
+ * for meta_heads = max(dense_heads, num_mask_heads) metadata heads (each count
+ * 1 or meta_heads), meta_batch 1 (no segment ids). ALL POINTERS ARE HOST.
+ *   dense:       [dense_heads, q_len, kv_len] bytes, nonzero = allowed.
+ *   block_mask, data_next: as splash_mask_info, [meta_heads, nq, nk].
+ *   mask_next:   [meta_heads, nq, nk]: for a block of class 1, its entry of
+ *                mask_blocks; 0 for the other blocks.
+ *   mask_blocks: [capacity, block_q, block_kv / 32] uint32: row r of an
+ *                entry is block_kv / 32 words, bit b of word w standing for
+ *                key offset 32 w + b of the block; positions past the
+ *                sequence ends are 0. Equal partial blocks share an entry.
+ *   num_blocks:  out: the number of entries the mask needs.
+ * With block_mask, data_next and mask_next all NULL the call only sets
+ * *num_blocks (size the store with it). Otherwise capacity must be at least
+ * *num_blocks (INVALID_ARGUMENT, and nothing written, if not). block_kv must be
+ * a multiple of 32. The caller copies the arrays to the device for
+ * splash_masked_fwd. This call runs on the calling thread and touches no GPU. */
+splash_status splash_dense_mask_info_host(int q_len, int kv_len, int block_q, int block_kv,
+                                          int num_mask_heads, const splash_head_mask* heads,
+                                          int dense_heads, const uint8_t* dense, int meta_heads,
+                                          int8_t* block_mask, int32_t* data_next, int32_t* mask_next,
+                                          uint32_t* mask_blocks, int64_t capacity, int64_t* num_blocks);
+
+/* Device copies of a dense mask's partial blocks (see above). */
+typedef struct {
+  const int32_t* mask_next;     /* DEVICE [meta_heads, nq, nk]                    */
+  const uint32_t* mask_blocks;  /* DEVICE [num_blocks, block_q, block_kv / 32]    */
+  int64_t num_blocks;
+} splash_partial_masks;
+
+/* General forward: pointwise = 0 is splash_fwd, 1 is splash_pointwise_fwd,
+ * with grouped-query K/V (kv_heads, as splash_gqa_fwd) and optional dense-mask
+ * blocks. With partial == NULL this is exactly those calls. With partial
+ * given, `info` holds the block_mask / data_next of the same dense mask (its
+ * meta_heads 1 or H, the head masks 1 or as many), segment ids are not
+ * accepted (UNSUPPORTED), and on every block of class 1 the block's bits are
+ * ANDed with the head band. mask_next entries outside [0, num_blocks) are
+ * clamped, so no metadata content makes the kernel read outside the store. */
+splash_status splash_masked_fwd(int pointwise, splash_dtype in_dtype, splash_dtype out_dtype, int B, int H,
+                                int kv_heads, int q_len, int kv_len, int head_dim,
+                                const void* q, const int64_t q_strides[3],
+                                const void* k, const int64_t k_strides[3],
+                                const void* v, const int64_t v_strides[3],
+                                void* o, const int64_t o_strides[3],
+                                float scale, const splash_mask_desc* mask,
+                                const splash_mask_info* info, const splash_partial_masks* partial,
+                                hipStream_t stream);
+
 /* Static name of a status code. */
 const char* splash_status_string(splash_status s);
 /* Detail of the last failure on the calling thread ("" if none). */

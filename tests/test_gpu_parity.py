@@ -269,6 +269,98 @@ def test_gqa_small_matches_oracle(gpu_device, case, pointwise):
 
 
 # ---------------------------------------------------------------------------
+# dense masks (partial blocks carry their own mask bits)
+# ---------------------------------------------------------------------------
+
+
+def _dense(kind, rng, H, Sq, Skv):
+    if kind == "tril":
+        return np.tri(Sq, Skv, dtype=bool)
+    if kind == "random":
+        d = rng.random((H, Sq, Skv)) < 0.3
+    elif kind == "strided":  # local band plus every 16th key (a global-token pattern)
+        q = np.arange(Sq)[:, None]
+        k = np.arange(Skv)[None, :]
+        d = ((np.abs(q - k) < 24) | (k % 16 == 0))[None].repeat(H, axis=0)
+    else:
+        raise ValueError(kind)
+    n = min(Sq, Skv)
+    d[:, np.arange(n), np.arange(n)] = True  # every row keeps a key
+    return d
+
+
+DENSE_CASES = [
+    # B, H, kv_heads, Sq, Skv, D, dense, head masks, bq, bkv, dtype
+    (2, 2, 2, 333, 333, 128, "random", [FULL], 128, 128, "bf16"),
+    (1, 2, 2, 300, 300, 128, "tril", [FULL], 64, 64, "bf16"),
+    (1, 4, 2, 517, 400, 128, "strided", [CAUSAL, (0, 100, 100), FULL, CAUSAL], 128, 64, "bf16"),
+    (1, 2, 1, 290, 290, 64, "random", [(1, 80, 80)], 256, 128, "bf16"),
+    (2, 2, 2, 200, 230, 64, "strided", [FULL], 64, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("pointwise", [False, True], ids=["softmax", "pointwise"])
+@pytest.mark.parametrize("case", DENSE_CASES, ids=[f"n{n}" for n in range(len(DENSE_CASES))])
+def test_dense_mask_small_matches_oracle(gpu_device, case, pointwise):
+    B, H, Hk, Sq, Skv, D, kind, heads, bq, bkv, dt = case
+    print(f"dense case {case} pointwise={pointwise}", flush=True)
+    rng = np.random.default_rng(53)
+    dense = _dense(kind, rng, H, Sq, Skv)
+    sigma = 0.5 if pointwise else 1.0
+    c = wl.random_case(47, B, H, Sq, Skv, D, dt, sigma=sigma)
+    kv = wl.random_case(59, B, Hk, Sq, Skv, D, dt, sigma=sigma)
+    q, k, v = c["q"].to(gpu_device), kv["k"].to(gpu_device), kv["v"].to(gpu_device)
+    info = sp.dense_mask_info_build(B, H, torch.from_numpy(dense), heads, bq, bkv, device=gpu_device)
+    ref_meta = oracle.mask_info(B, H, Sq, Skv, bq, bkv, heads, dense=dense)
+    assert np.array_equal(info.block_mask.cpu().numpy(), ref_meta[0])
+    fn = sp.pointwise_fwd if pointwise else sp.splash_fwd
+    out = fn(q, k, v, info)
+    torch.cuda.synchronize()
+    ofn = oracle.pointwise_attention if pointwise else oracle.softmax_attention
+    ref = ofn(to64(c["q"]), to64(kv["k"]), to64(kv["v"]), 1 / math.sqrt(D), heads, dense=dense)
+    print(check_close(to64(out), ref, dt, f"dense {case}"))
+
+
+def test_dense_causal_equals_causal_head_mask(gpu_device):
+    """A lower-triangular dense mask gives the causal result (bit-identical:
+    the same blocks are visited and the same pairs allowed)."""
+    B, H, S, D = 1, 2, 520, 128
+    c = wl.random_case(61, B, H, S, S, D, "bf16")
+    g = _to_dev(c, gpu_device)
+    dinfo = sp.dense_mask_info_build(B, H, torch.from_numpy(np.tri(S, S, dtype=bool)), [FULL], 128, 128,
+                                     device=gpu_device)
+    cinfo = sp.mask_info_build(B, H, S, S, [CAUSAL], 128, 128, device=gpu_device)
+    # the full triangle, the ragged last one (8 rows), and 8 full rows left of it
+    assert dinfo.mask_blocks.shape[0] == 3
+    a = sp.splash_fwd(g["q"], g["k"], g["v"], dinfo)
+    b = sp.splash_fwd(g["q"], g["k"], g["v"], cinfo)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_dense_mask_large_sampled_rows(gpu_device):
+    """Strided dense mask (local band of 24 plus every 16th key) ANDed with
+    causal at S=4096, B=1, H=8, D=128, 128x128 blocks; sampled rows."""
+    B, H, S, D = 1, 8, 4096, 128
+    dense = _dense("strided", None, 1, S, S)[0]
+    c = wl.random_case(67, B, H, S, S, D, "bf16")
+    g = _to_dev(c, gpu_device)
+    info = sp.dense_mask_info_build(B, H, torch.from_numpy(dense), [CAUSAL], 128, 128, device=gpu_device)
+    out = sp.splash_fwd(g["q"], g["k"], g["v"], info)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(71)
+    rows = sample_rows(rng, B, H, S, 40, [127, 128, 2000])
+    got, ref = [], []
+    for (b, h, t) in rows:
+        m = oracle.element_mask(S, S, CAUSAL, rows=[t], dense=dense)
+        r = oracle.softmax_attention_rows(to64(c["q"][b, h, t:t + 1]), to64(c["k"][b, h]), to64(c["v"][b, h]),
+                                          D ** -0.5, m)
+        ref.append(r[0])
+        got.append(to64(out[b, h, t]))
+    print(check_close(np.stack(got), np.stack(ref), "bf16", "dense large"))
+
+
+# ---------------------------------------------------------------------------
 # layouts, dtypes, edge cases, determinism
 # ---------------------------------------------------------------------------
 
