@@ -2,8 +2,9 @@
 
 A step is one pass of the whole path over one batch of synthetic inputs that
 are already resident in HBM: the block metadata build followed by the
-attention forward. The default workload is causal MHA, B=2, H=32, S=8192,
-D=128, bf16, 128x128 blocks. Prints one JSON line.
+attention forward (for a dense-mask workload, whose metadata is built once on
+the host, the forward alone). The default workload is causal MHA, B=2, H=32,
+S=8192, D=128, bf16, 128x128 blocks. Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload c3h] [--no-cpu-baseline]
 
@@ -67,6 +68,7 @@ def cpu_baseline(w, gen, budget_s: float = 12.0):
     nq = -(-S // bq)
     qs = gen["q_segment_ids"]
     qs = None if qs is None else qs.numpy()
+    dense = None if gen["dense"] is None else gen["dense"].numpy()
     flops = 0
     done = 0
     t0 = time.perf_counter()
@@ -80,14 +82,15 @@ def cpu_baseline(w, gen, budget_s: float = 12.0):
         k64, v64 = cache[(b, hk)]
         rows = np.arange(i * bq, min(S, (i + 1) * bq))
         head = w.head_masks[0] if len(w.head_masks) == 1 else w.head_masks[h]
-        m = oracle.element_mask(S, S, head, None if qs is None else qs[b], None if qs is None else qs[b], rows=rows)
+        m = oracle.element_mask(S, S, head, None if qs is None else qs[b], None if qs is None else qs[b], rows=rows,
+                                dense=dense)
         q64 = gen["q"][b, h, rows[0]:rows[-1] + 1].to(torch.float64).numpy()
         if w.pointwise:
             oracle.pointwise_attention_rows(q64, k64, v64, w.scale, m, S)
         else:
             oracle.softmax_attention_rows(q64, k64, v64, w.scale, m)
         cls, _ = oracle.mask_info_row(S, S, bq, bkv, head, i, None if qs is None else qs[b],
-                                      None if qs is None else qs[b])
+                                      None if qs is None else qs[b], dense=dense)
         flops += int(np.count_nonzero(cls)) * 4 * bq * bkv * D
         done += 1
     dt = time.perf_counter() - t0
@@ -145,7 +148,13 @@ def main():
     fwd = sp.pointwise_fwd if w.pointwise else sp.splash_fwd
     out = torch.empty_like(q)
 
-    info = sp.mask_info_build(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg, device=dev)
+    dense = gen["dense"]
+    if dense is not None:
+        # a dense mask's metadata is built once, on the host (as for a mask
+        # fixed ahead of time); the step is then the forward alone
+        info = sp.dense_mask_info_build(w.B, w.H, dense, w.head_masks, w.block_q, w.block_kv, device=dev)
+    else:
+        info = sp.mask_info_build(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg, device=dev)
     torch.cuda.synchronize()
     nonempty = (info.block_mask != 0).sum(dim=(2, 3)).to(torch.int64)  # [Bm, Hm]
     Bm, Hm = info.block_mask.shape[:2]
@@ -153,8 +162,13 @@ def main():
     blocks = int(per_bh.sum().item())
     flops = blocks * 4 * w.block_q * w.block_kv * w.D
 
+    def build_metadata():
+        if dense is None:
+            sp.mask_info_build(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg, device=dev,
+                               out=info)
+
     def step():
-        sp.mask_info_build(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg, device=dev, out=info)
+        build_metadata()
         fwd(q, k, v, info, scale=w.scale, out=out)
 
     for _ in range(args.warmup):
@@ -166,7 +180,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        sp.mask_info_build(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg, device=dev, out=info)
+        build_metadata()
         ev[s][0].record(stream)
         fwd(q, k, v, info, scale=w.scale, out=out)
         ev[s][1].record(stream)
@@ -195,7 +209,11 @@ def main():
         "c4": "mixed heads B=1 H=16 S=32768 D=128 bf16: 8 causal + 8 causal window 1024, block 128x128",
         "c5": "pointwise SiLU causal B=8 H=8 S=4096 D=64 bf16, N(0,0.5^2), block 128x128",
         "g3h": "grouped-query causal B=2 H=32 (8 K/V heads) S=8192 D=128 bf16, block 128x128",
+        "d3h": "dense-mask MHA B=2 H=32 S=8192 D=128 bf16, the causal pattern as an [S, S] array, block 128x128",
+        "d5": "dense-mask pointwise SiLU B=8 H=8 S=4096 D=64 bf16, the causal pattern as an [S, S] array, "
+              "N(0,0.5^2), block 128x128",
     }[w.name]
+    fwd_name = "pointwise_fwd" if w.pointwise else "splash_fwd"
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -213,7 +231,8 @@ def main():
                    "seq_len": w.S,
                    "head_dim": w.D, "block_q": w.block_q, "block_kv": w.block_kv,
                    "nonempty_blocks": blocks, "flops_per_step": flops,
-                   "step": "mask_info_build + " + ("pointwise_fwd" if w.pointwise else "splash_fwd")},
+                   "step": (f"{fwd_name} (dense-mask metadata built once on the host, before timing)"
+                            if dense is not None else "mask_info_build + " + fwd_name)},
         "fwd_kernel_ms": round(kernel_ms, 5),
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma" if not in_f32 else "alu", "achieved": round(achieved, 3), "peak": peak,

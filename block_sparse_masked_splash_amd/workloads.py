@@ -17,6 +17,11 @@ Recipe (shared by every test and by the benchmark):
     running total reaches S, the last document is cut at S, and documents are
     numbered 0, 1, 2, ... along the row; q and kv share the ids.
 
+A dense mask is an explicit boolean [S, S] array shared by all heads; the one
+workload kind here ("tril") is the causal pattern written out as such an
+array, the form in which "hstu_ops.py" (``pointwise_splash_attention``)
+accepts an arbitrary numpy mask.
+
 A head mask is a plain triple ``(causal, window_left, window_right)``: causal
 means key position <= query position; a window bound of -1 is unbounded,
 otherwise keys in [q - window_left, q + window_right] are allowed. This is the
@@ -57,6 +62,7 @@ class Workload:
     pointwise: bool         # SiLU pointwise attention instead of softmax
     seed: int
     kv_heads: int = 0       # K/V heads (0: H, plain multi-head attention)
+    dense: str = ""         # "" (none) or "tril": the causal pattern as a dense [S, S] array
 
     @property
     def n_kv_heads(self) -> int:
@@ -89,7 +95,21 @@ WORKLOADS = {
     "c5": Workload("c5", 8, 8, 4096, 64, "bf16", 0.5, (CAUSAL,), 128, 128, False, True, 5),
     # grouped-query form of c3h: 32 query heads over 8 K/V heads
     "g3h": Workload("g3h", 2, 32, 8192, 128, "bf16", 1.0, (CAUSAL,), 128, 128, False, False, 6, kv_heads=8),
+    # c3h's attention with its causal pattern handed over as a dense mask array
+    "d3h": Workload("d3h", 2, 32, 8192, 128, "bf16", 1.0, (FULL,), 128, 128, False, False, 7, dense="tril"),
+    # c5's pointwise attention with its causal pattern as a dense mask array
+    "d5": Workload("d5", 8, 8, 4096, 64, "bf16", 0.5, (FULL,), 128, 128, False, True, 8, dense="tril"),
 }
+
+
+def dense_mask(w: Workload, S: int):
+    """The workload's dense boolean [S, S] mask as a CPU torch tensor, or None."""
+    if not w.dense:
+        return None
+    if w.dense != "tril":
+        raise ValueError(f"unknown dense mask kind {w.dense!r}")
+    import torch
+    return torch.from_numpy(np.tri(S, S, dtype=bool))
 
 
 def draw_qkv_f32(rng: np.random.Generator, B: int, H: int, Sq: int, Skv: int, D: int,
@@ -131,8 +151,9 @@ def generate(w: Workload, *, B: int | None = None, H: int | None = None,
              S: int | None = None, seed: int | None = None) -> dict:
     """CPU torch tensors for workload ``w`` (sizes overridable for small cases).
 
-    Returns dict(q, k, v, q_segment_ids, kv_segment_ids) where the segment ids
-    are int32 torch tensors [B, S] or None.
+    Returns dict(q, k, v, q_segment_ids, kv_segment_ids, dense) where the
+    segment ids are int32 torch tensors [B, S] or None and ``dense`` is the
+    boolean [S, S] mask or None.
     """
     B = w.B if B is None else B
     Hk = w.n_kv_heads if H is None else max(1, H // (w.H // w.n_kv_heads))
@@ -141,7 +162,7 @@ def generate(w: Workload, *, B: int | None = None, H: int | None = None,
     rng = np.random.default_rng(w.seed if seed is None else seed)
     q, k, v = draw_qkv_f32(rng, B, H, S, S, w.D, w.sigma, Hk)
     out = dict(q=_store(q, w.dtype), k=_store(k, w.dtype), v=_store(v, w.dtype),
-               q_segment_ids=None, kv_segment_ids=None)
+               q_segment_ids=None, kv_segment_ids=None, dense=dense_mask(w, S))
     del q, k, v
     if w.segments:
         import torch

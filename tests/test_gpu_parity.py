@@ -184,13 +184,18 @@ def test_workload_c2_full(gpu_device):
 # ---------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("name", ["c3h", "c3", "c4", "c5", "g3h"])
+@pytest.mark.parametrize("name", ["c3h", "c3", "c4", "c5", "g3h", "d3h", "d5"])
 def test_full_workload_sampled_rows(gpu_device, name):
     w = wl.WORKLOADS[name]
     print(f"full workload {name}", flush=True)
     c = wl.generate(w)
     g = _to_dev(c, gpu_device)
-    info = _meta(gpu_device, w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, g)
+    dense = None if c["dense"] is None else c["dense"].numpy()
+    if dense is not None:
+        info = sp.dense_mask_info_build(w.B, w.H, c["dense"], w.head_masks, w.block_q, w.block_kv,
+                                        device=gpu_device)
+    else:
+        info = _meta(gpu_device, w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, g)
     fn = sp.pointwise_fwd if w.pointwise else sp.splash_fwd
     out = fn(g["q"], g["k"], g["v"], info, scale=w.scale)
     torch.cuda.synchronize()
@@ -210,7 +215,8 @@ def test_full_workload_sampled_rows(gpu_device, name):
             cache[(b, hk)] = (to64(c["k"][b, hk]), to64(c["v"][b, hk]))
         k64, v64 = cache[(b, hk)]
         head = w.head_masks[0] if len(w.head_masks) == 1 else w.head_masks[h]
-        m = oracle.element_mask(w.S, w.S, head, None if qs is None else qs[b], None if qs is None else qs[b], rows=[t])
+        m = oracle.element_mask(w.S, w.S, head, None if qs is None else qs[b], None if qs is None else qs[b], rows=[t],
+                                dense=dense)
         q64 = to64(c["q"][b, h, t:t + 1])
         if w.pointwise:
             r = oracle.pointwise_attention_rows(q64, k64, v64, w.scale, m, w.S)
