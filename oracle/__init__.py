@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for block-sparse masked attention forward.
+"""fp64 CPU oracle for block-sparse masked attention (forward, pointwise backward).
 
 TEST INFRASTRUCTURE ONLY. This package is the independent, slow, plainly
 written reference that the GPU path is checked against. Only the test suite,
@@ -20,6 +20,7 @@ from .splash_oracle import (  # noqa: F401
     next_nonempty,
     mask_info,
     mask_info_row,
+    mask_info_dkv,
     softmax_attention,
     softmax_attention_rows,
     online_softmax_rows,
@@ -29,4 +30,6 @@ from .splash_oracle import (  # noqa: F401
     element_flops,
     kv_head_of,
     partial_blocks,
+    pointwise_attention_bwd,
+    pointwise_attention_bwd_rows,
 )

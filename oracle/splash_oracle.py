@@ -24,6 +24,13 @@ blocking, fusion or reordering beyond what a definition states:
   correction alpha = e^{m_A - m_AB}).
 * Grouped-query attention: page 3, section 21 (query head h reads K/V head
   h // q_heads_per_kv_head).
+* Pointwise backward: "hstu_ops.py", ``_pointwise_splash_attention_bwd_kernel_impl``
+  (per kv block: scores qk = scale * k q^T, sigmoid masked to 0,
+  p = qk * sigmoid / seq_len, dv += p do, dp = v do^T,
+  ds = dp * sigmoid * (1 + qk (1 - sigmoid)) / seq_len, dk += scale ds q,
+  dq += scale ds^T k) and ``_pointwise_splash_attention_bwd_kernel`` (grid over
+  kv blocks, then heads, then q blocks; the q block fetched at step i is
+  ``data_next[h, i, j]`` of the dK/dV metadata, ``_next_nonzero(next_i=True)``).
 * Pointwise attention: "hstu_ops.py", ``_pointwise_splash_attention_fwd_kernel_impl``
   (scores times scale, times logistic(scores), divided by the query sequence
   length, masked entries set to 0, then times V), with the contributions of
@@ -191,6 +198,28 @@ def mask_info(B: int, H: int, q_len: int, kv_len: int, bq: int, bkv: int, heads,
                 bmask[b, hm, i], dnext[b, hm, i] = mask_info_row(
                     q_len, kv_len, bq, bkv, head, i, qs, ks, dense=dm)
     return bmask, dnext
+
+
+def mask_info_dkv(B: int, H: int, q_len: int, kv_len: int, bq: int, bkv: int, heads,
+                  q_seg=None, kv_seg=None):
+    """(block_mask, data_next) of the dK/dV pass, both [Bm, Hm, nq, nk].
+
+    "hstu_ops.py", ``_pointwise_splash_attention_bwd_kernel``: the grid runs
+    over kv blocks j, then heads, then q steps i, and the q block fetched at
+    step i is ``data_next[h, i, j]`` (``_next_nonzero(..., next_i=True)``),
+    from metadata that ``process_mask_dkv`` builds for the same mask. Reading:
+    the classes are those of the forward (they only depend on the block's
+    pairs), and ``data_next[..., i, j]`` is the first q block i' >= i of
+    column j that is not empty, else nq (the sentinel read as for the
+    forward's walk).
+    """
+    bm, _ = mask_info(B, H, q_len, kv_len, bq, bkv, heads, q_seg, kv_seg)
+    dn = np.empty(bm.shape, dtype=np.int32)
+    for b in range(bm.shape[0]):
+        for h in range(bm.shape[1]):
+            for j in range(bm.shape[3]):
+                dn[b, h, :, j] = next_nonempty(bm[b, h, :, j])
+    return bm, dn
 
 
 def partial_blocks(H: int, q_len: int, kv_len: int, bq: int, bkv: int, heads, dense):
@@ -390,3 +419,82 @@ def pointwise_attention(q, k, v, scale: float, heads, q_seg=None, kv_seg=None,
     """Pointwise SiLU attention [B, H, Sq, Dv] (fp64), divided by Sq; k and v
     may have fewer heads than q (``kv_head_of``)."""
     return _attention("pointwise", q, k, v, scale, heads, q_seg, kv_seg, row_chunk, dense)
+
+
+# ---------------------------------------------------------------------------
+# pointwise backward
+# ---------------------------------------------------------------------------
+
+
+def _logistic(x):
+    """1 / (1 + e^-x) without overflow warnings (e^-x = inf gives 0)."""
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def pointwise_attention_bwd_rows(q_rows, k, v, do_rows, scale: float, mask_rows, seq_len: int):
+    """Contributions of some query rows to the pointwise attention gradients.
+
+    q_rows, do_rows [R, D]; k, v [Skv, D]; mask_rows bool [R, Skv]. Returns
+    (dq_rows [R, D], dk [Skv, D], dv [Skv, D]): dq of these rows, and what
+    these rows add to dk and dv. "hstu_ops.py",
+    ``_pointwise_splash_attention_bwd_kernel_impl``, in its orientation (keys
+    x queries):
+      qk = scale * k q^T; sig = logistic(qk), 0 where masked;
+      p = qk * sig / seq_len; dv = p do;
+      dp = v do^T; ds = dp * sig * (1 + qk (1 - sig)) / seq_len;
+      dk = scale * ds q; dq = scale * ds^T k.
+    This is the derivative of ``pointwise_attention_rows`` (d/dx of
+    x logistic(x) is logistic(x) (1 + x (1 - logistic(x)))).
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do_rows = np.asarray(do_rows, dtype=np.float64)
+    qk = (k @ q_rows.T) * float(scale)                    # [Skv, R]
+    sig = np.where(np.asarray(mask_rows).T, _logistic(qk), 0.0)
+    p = qk * sig / float(seq_len)
+    dv = p @ do_rows
+    dp = v @ do_rows.T
+    ds = dp * sig * (1.0 + qk * (1.0 - sig)) / float(seq_len)
+    dk = float(scale) * (ds @ q_rows)
+    dq = float(scale) * (ds.T @ k)
+    return dq, dk, dv
+
+
+def pointwise_attention_bwd(q, k, v, do, scale: float, heads, q_seg=None, kv_seg=None,
+                            row_chunk: int = 512):
+    """Gradients (dq [B, H, Sq, D], dk, dv [B, Hk, Skv, D]) of
+    ``pointwise_attention`` for the output gradient ``do``, fp64.
+
+    Query rows are taken ``row_chunk`` at a time and their contributions to dk
+    and dv summed (the kernel's sum over q blocks for each kv block). With
+    fewer K/V heads than query heads (``kv_head_of``), a K/V head's dk and dv
+    sum over the query heads that read it.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, Sq, _ = q.shape
+    Skv = k.shape[2]
+    kv_heads = k.shape[1]
+    heads = _heads_list(heads, H)
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(B):
+        qs = None if q_seg is None else np.asarray(q_seg)[b]
+        ks = None if kv_seg is None else np.asarray(kv_seg)[b]
+        for h in range(H):
+            hd = heads[0] if len(heads) == 1 else heads[h]
+            hk = kv_head_of(h, H, kv_heads)
+            for r0 in range(0, Sq, row_chunk):
+                rows = np.arange(r0, min(Sq, r0 + row_chunk))
+                m = element_mask(Sq, Skv, hd, qs, ks, rows=rows)
+                a, bk, bv = pointwise_attention_bwd_rows(q[b, h, rows], k[b, hk], v[b, hk], do[b, h, rows],
+                                                         scale, m, Sq)
+                dq[b, h, rows] = a
+                dk[b, hk] += bk
+                dv[b, hk] += bv
+    return dq, dk, dv

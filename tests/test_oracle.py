@@ -527,3 +527,189 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(so.np, "exp", real_exp)
     assert calls["n"] > 0
     assert not np.allclose(a, b, rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# pointwise backward
+# ---------------------------------------------------------------------------
+
+
+def _loss_grads_fd(q, k, v, do, scale, heads, qs, ks, h=1e-5):
+    """Central differences of sum(do * pointwise_attention(q, k, v)) with
+    respect to every element of q, k and v (the forward is pinned on its
+    own above)."""
+    def loss(qq, kk, vv):
+        return float((oracle.pointwise_attention(qq, kk, vv, scale, heads, qs, ks) * do).sum())
+
+    grads = []
+    for which in range(3):
+        args = [q.copy(), k.copy(), v.copy()]
+        g = np.zeros_like(args[which])
+        for idx in np.ndindex(g.shape):
+            x0 = args[which][idx]
+            args[which][idx] = x0 + h
+            up = loss(*args)
+            args[which][idx] = x0 - h
+            dn = loss(*args)
+            args[which][idx] = x0
+            g[idx] = (up - dn) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+def _small_bwd_case(seed, H, kv_heads, Sq, Skv, D):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, H, Sq, D))
+    k = rng.standard_normal((1, kv_heads, Skv, D))
+    v = rng.standard_normal((1, kv_heads, Skv, D))
+    do = rng.standard_normal((1, H, Sq, D))
+    qs = rng.integers(0, 2, size=(1, Sq)).astype(np.int32)
+    ks = rng.integers(0, 2, size=(1, Skv)).astype(np.int32)
+    return q, k, v, do, qs, ks
+
+
+@pytest.mark.parametrize("kv_heads", [2, 1])
+def test_pointwise_bwd_matches_finite_differences(kv_heads):
+    """The gradients are those of the (separately pinned) forward: central
+    differences of sum(do * out), every element of q, k and v, with head masks,
+    segment ids and (kv_heads = 1) two query heads sharing one K/V head."""
+    H, Sq, Skv, D = 2, 7, 9, 3
+    q, k, v, do, qs, ks = _small_bwd_case(5 + kv_heads, H, kv_heads, Sq, Skv, D)
+    heads = [CAUSAL, (0, 2, 3)]
+    dq, dk, dv = oracle.pointwise_attention_bwd(q, k, v, do, 0.7, heads, qs, ks, row_chunk=3)
+    fq, fk, fv = _loss_grads_fd(q, k, v, do, 0.7, heads, qs, ks)
+    for got, want in ((dq, fq), (dk, fk), (dv, fv)):
+        assert np.abs(want).max() > 1e-3
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-8)
+
+
+@pytest.mark.parametrize("head", [FULL, CAUSAL, (1, 9, 9), (0, 5, 3)])
+def test_pointwise_bwd_matches_torch_autograd(head):
+    """torch autograd through torch's own SiLU (a library derivative) in
+    float64: out = silu(scale q k^T) / Sq, masked to 0, times v."""
+    B, H, S, D = 2, 2, 61, 16
+    q, k, v, qs, ks = _case(71, B, H, S, S, D, sigma=0.8, segments="docs")
+    do = np.random.default_rng(72).standard_normal(q.shape)
+    scale = 1 / math.sqrt(D)
+    dq, dk, dv = oracle.pointwise_attention_bwd(q, k, v, do, scale, [head], qs, ks, row_chunk=20)
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    total = 0
+    for b in range(B):
+        m = torch.from_numpy(oracle.element_mask(S, S, head, qs[b], ks[b]))
+        x = scale * (tq[b] @ tk[b].transpose(-1, -2))
+        p = torch.where(m, torch.nn.functional.silu(x), torch.zeros((), dtype=torch.float64)) / S
+        total = total + ((p @ tv[b]) * torch.from_numpy(do[b])).sum()
+    total.backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_pointwise_bwd_closed_forms():
+    S, D = 40, 8
+    q, k, v, _, _ = _case(73, 1, 1, S, S, D, sigma=0.6)
+    do = np.random.default_rng(74).standard_normal(q.shape)
+    scale = 0.35
+    mask = oracle.element_mask(S, S, CAUSAL)
+    q0, k0, v0, do0 = q[0, 0], k[0, 0], v[0, 0], do[0, 0]
+    # do = 0: nothing flows back
+    for g in oracle.pointwise_attention_bwd_rows(q0, k0, v0, np.zeros_like(do0), scale, mask, S):
+        assert (g == 0).all()
+    # v = 0: dp = 0, so dq = dk = 0; dv = P^T do with P the forward's weights
+    # (the forward with v = identity returns P itself)
+    dq, dk, dv = oracle.pointwise_attention_bwd_rows(q0, k0, np.zeros_like(v0), do0, scale, mask, S)
+    assert (dq == 0).all() and (dk == 0).all()
+    P = oracle.pointwise_attention_rows(q0, k0, np.eye(S), scale, mask, S)
+    np.testing.assert_allclose(dv, P.T @ do0, rtol=1e-12, atol=1e-15)
+    # q = 0: every score is 0, silu'(0) = 1/2, silu(0) = 0:
+    # dv = 0, dk = 0, dq_t = scale / (2 S) sum_{k <= t} (do_t . v_k) k_k
+    dq, dk, dv = oracle.pointwise_attention_bwd_rows(np.zeros_like(q0), k0, v0, do0, scale, mask, S)
+    assert (dv == 0).all() and (dk == 0).all()
+    for t in range(S):
+        want = sum(float(np.dot(do0[t], v0[j])) * k0[j] for j in range(t + 1)) * scale / (2 * S)
+        np.testing.assert_allclose(dq[t], want, rtol=1e-12, atol=1e-15)
+    # causal: the last key is seen only by the last query
+    dq, dk, dv = oracle.pointwise_attention_bwd_rows(q0, k0, v0, do0, scale, mask, S)
+    x = scale * float(np.dot(q0[S - 1], k0[S - 1]))
+    sig = 1 / (1 + math.exp(-x))
+    np.testing.assert_allclose(dv[S - 1], x * sig / S * do0[S - 1], rtol=1e-12, atol=0)
+    ds = float(np.dot(do0[S - 1], v0[S - 1])) * sig * (1 + x * (1 - sig)) / S
+    np.testing.assert_allclose(dk[S - 1], scale * ds * q0[S - 1], rtol=1e-12, atol=0)
+
+
+def test_pointwise_bwd_masked_keys_get_no_gradient():
+    """Keys that no query may see get dk = dv = 0, and changing them leaves dq
+    unchanged (documents: a key whose id no query has)."""
+    B, H, S, D = 1, 2, 50, 8
+    q, k, v, qs, ks = _case(75, B, H, S, S, D)
+    do = np.random.default_rng(76).standard_normal(q.shape)
+    qs = np.zeros((1, S), np.int32)
+    ks = np.zeros((1, S), np.int32)
+    ks[0, 10:20] = 7
+    dq, dk, dv = oracle.pointwise_attention_bwd(q, k, v, do, 0.5, [FULL], qs, ks)
+    assert (dk[0, :, 10:20] == 0).all() and (dv[0, :, 10:20] == 0).all()
+    assert np.abs(dk[0, :, :10]).min() > 0
+    k2, v2 = k.copy(), v.copy()
+    k2[0, :, 10:20] += 3.0
+    v2[0, :, 10:20] -= 1.0
+    dq2, _, _ = oracle.pointwise_attention_bwd(q, k2, v2, do, 0.5, [FULL], qs, ks)
+    np.testing.assert_array_equal(dq, dq2)
+
+
+def test_pointwise_bwd_pins_catch_planted_mistakes(monkeypatch):
+    """Mutants of the backward (a dropped term, a lost scale, an unmasked
+    sigmoid, a missing 1/seq_len) all fail the finite-difference pin."""
+    import inspect
+    import oracle.splash_oracle as so
+
+    H, Sq, Skv, D = 2, 6, 6, 3
+    q, k, v, do, qs, ks = _small_bwd_case(77, H, 2, Sq, Skv, D)
+    heads = [CAUSAL]
+    fd = _loss_grads_fd(q, k, v, do, 0.6, heads, qs, ks)
+    src = inspect.getsource(so.pointwise_attention_bwd_rows)
+    mutations = [
+        ("* (1.0 + qk * (1.0 - sig))", "* (qk * (1.0 - sig))"),
+        ("dk = float(scale) * (ds @ q_rows)", "dk = ds @ q_rows"),
+        ("sig = np.where(np.asarray(mask_rows).T, _logistic(qk), 0.0)", "sig = _logistic(qk)"),
+        ("ds = dp * sig * (1.0 + qk * (1.0 - sig)) / float(seq_len)", "ds = dp * sig * (1.0 + qk * (1.0 - sig))"),
+    ]
+    for old, new in mutations:
+        assert old in src, old
+        ns = dict(so.__dict__)
+        exec(src.replace(old, new), ns)
+        monkeypatch.setattr(so, "pointwise_attention_bwd_rows", ns["pointwise_attention_bwd_rows"])
+        got = so.pointwise_attention_bwd(q, k, v, do, 0.6, heads, qs, ks)
+        err = max(np.abs(g - f).max() for g, f in zip(got, fd))
+        assert err > 1e-4, (old, err)
+    monkeypatch.undo()
+    got = so.pointwise_attention_bwd(q, k, v, do, 0.6, heads, qs, ks)
+    assert max(np.abs(g - f).max() for g, f in zip(got, fd)) < 1e-8
+
+
+def test_dkv_metadata_closed_forms_and_brute_force():
+    """Column walk of the dK/dV pass: causal square blocks give
+    data_next[i, j] = max(i, j) (column j is non-empty from q block j on);
+    every case matches a scalar scan down each column, and the classes are
+    the forward's."""
+    S, b = 1000, 64
+    nq = -(-S // b)
+    bm, dn = oracle.mask_info_dkv(1, 1, S, S, b, b, [CAUSAL])
+    for i in range(nq):
+        for j in range(nq):
+            assert dn[0, 0, i, j] == max(i, j)
+    rng = np.random.default_rng(78)
+    for trial in range(6):
+        Sq, Skv = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+        bq, bkv = int(rng.choice([16, 32, 64])), int(rng.choice([16, 32, 64]))
+        heads = [(int(rng.integers(0, 2)), int(rng.integers(-1, 40)), int(rng.integers(-1, 40))) for _ in range(2)]
+        _, _, _, qs, ks = _case(300 + trial, 2, 1, Sq, Skv, 4, segments="random")
+        fbm, _ = oracle.mask_info(2, 2, Sq, Skv, bq, bkv, heads, qs, ks)
+        bm, dn = oracle.mask_info_dkv(2, 2, Sq, Skv, bq, bkv, heads, qs, ks)
+        np.testing.assert_array_equal(bm, fbm)
+        Bm, Hm, nq, nk = bm.shape
+        for bb in range(Bm):
+            for h in range(Hm):
+                for j in range(nk):
+                    for i in range(nq):
+                        later = [ii for ii in range(i, nq) if bm[bb, h, ii, j] != 0]
+                        assert dn[bb, h, i, j] == (later[0] if later else nq)
