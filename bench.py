@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak
 METRIC = "splash fwd TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, causal S=8192"
-KERNEL_SOURCES = ["splash_fwd_bf16.hip", "splash_fwd_f32.hip", "internal.h"]
+KERNEL_SOURCES = ["splash_fwd_bf16.hip", "splash_fwd_f32.hip", "splash_bwd_bf16.hip", "splash_bwd_f32.hip",
+                  "cdna4.h", "internal.h"]
 
 
 def kernel_source_hash() -> str:
@@ -85,13 +86,16 @@ def cpu_baseline(w, gen, budget_s: float = 12.0):
         m = oracle.element_mask(S, S, head, None if qs is None else qs[b], None if qs is None else qs[b], rows=rows,
                                 dense=dense)
         q64 = gen["q"][b, h, rows[0]:rows[-1] + 1].to(torch.float64).numpy()
-        if w.pointwise:
+        if w.backward:
+            do64 = gen["d_o"][b, h, rows[0]:rows[-1] + 1].to(torch.float64).numpy()
+            oracle.pointwise_attention_bwd_rows(q64, k64, v64, do64, w.scale, m, S)
+        elif w.pointwise:
             oracle.pointwise_attention_rows(q64, k64, v64, w.scale, m, S)
         else:
             oracle.softmax_attention_rows(q64, k64, v64, w.scale, m)
         cls, _ = oracle.mask_info_row(S, S, bq, bkv, head, i, None if qs is None else qs[b],
                                       None if qs is None else qs[b], dense=dense)
-        flops += int(np.count_nonzero(cls)) * 4 * bq * bkv * D
+        flops += int(np.count_nonzero(cls)) * (10 if w.backward else 4) * bq * bkv * D
         done += 1
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
@@ -160,16 +164,33 @@ def main():
     Bm, Hm = info.block_mask.shape[:2]
     per_bh = nonempty.expand(w.B if Bm == 1 else Bm, w.H if Hm == 1 else Hm)
     blocks = int(per_bh.sum().item())
-    flops = blocks * 4 * w.block_q * w.block_kv * w.D
+    # forward: Q Kᵀ and P V per non-empty block; backward: Q Kᵀ, dO Vᵀ, P'ᵀ dO,
+    # dS'ᵀ Q and dS' K (the five products of the page's backward kernel)
+    flops = blocks * (10 if w.backward else 4) * w.block_q * w.block_kv * w.D
+
+    if w.backward:
+        d_o = gen["d_o"].to(dev)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        info_dkv = sp.mask_info_build_dkv(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg,
+                                          device=dev)
 
     def build_metadata():
         if dense is None:
             sp.mask_info_build(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg, device=dev,
                                out=info)
+        if w.backward:
+            sp.mask_info_build_dkv(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg, device=dev,
+                                   out=info_dkv)
+
+    def run_kernels():
+        if w.backward:
+            sp.pointwise_bwd(q, k, v, d_o, info, info_dkv, scale=w.scale, out=grads)
+        else:
+            fwd(q, k, v, info, scale=w.scale, out=out)
 
     def step():
         build_metadata()
-        fwd(q, k, v, info, scale=w.scale, out=out)
+        run_kernels()
 
     for _ in range(args.warmup):
         step()
@@ -182,7 +203,7 @@ def main():
     for s in range(args.steps):
         build_metadata()
         ev[s][0].record(stream)
-        fwd(q, k, v, info, scale=w.scale, out=out)
+        run_kernels()
         ev[s][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -212,8 +233,12 @@ def main():
         "d3h": "dense-mask MHA B=2 H=32 S=8192 D=128 bf16, the causal pattern as an [S, S] array, block 128x128",
         "d5": "dense-mask pointwise SiLU B=8 H=8 S=4096 D=64 bf16, the causal pattern as an [S, S] array, "
               "N(0,0.5^2), block 128x128",
+        "b5": "pointwise SiLU backward (dq, dk, dv) B=8 H=8 S=4096 D=64 bf16 causal, N(0,0.5^2) inputs, "
+              "N(0,1) output gradient, blocks 128x128 for both walks",
+        "b5h": "pointwise SiLU backward (dq, dk, dv) B=2 H=16 S=4096 D=128 bf16 causal, N(0,0.5^2) inputs, "
+               "N(0,1) output gradient, blocks 128x128 for both walks",
     }[w.name]
-    fwd_name = "pointwise_fwd" if w.pointwise else "splash_fwd"
+    fwd_name = "pointwise_bwd" if w.backward else ("pointwise_fwd" if w.pointwise else "splash_fwd")
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -232,8 +257,10 @@ def main():
                    "head_dim": w.D, "block_q": w.block_q, "block_kv": w.block_kv,
                    "nonempty_blocks": blocks, "flops_per_step": flops,
                    "step": (f"{fwd_name} (dense-mask metadata built once on the host, before timing)"
-                            if dense is not None else "mask_info_build + " + fwd_name)},
-        "fwd_kernel_ms": round(kernel_ms, 5),
+                            if dense is not None else
+                            "mask_info_build + mask_info_build_dkv + " + fwd_name if w.backward else
+                            "mask_info_build + " + fwd_name)},
+        "kernel_ms": round(kernel_ms, 5),
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma" if not in_f32 else "alu", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),

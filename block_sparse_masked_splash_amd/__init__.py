@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     dense_mask_info_build,
     load_library,
     mask_info_build,
+    mask_info_build_dkv,
+    pointwise_bwd,
     pointwise_fwd,
     splash_fwd,
 )

@@ -36,6 +36,8 @@ SYMBOLS = (
     "splash_gqa_pointwise_fwd",
     "splash_dense_mask_info_host",
     "splash_masked_fwd",
+    "splash_mask_info_build_dkv",
+    "splash_pointwise_bwd",
     "splash_status_string",
     "splash_last_error",
     "splash_abi_version",
@@ -81,6 +83,10 @@ _FWD_ARGS = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_in
 _GQA_ARGS = _FWD_ARGS[:4] + [ctypes.c_int] + _FWD_ARGS[4:]
 # general form: pointwise flag first, partial masks before the stream
 _MASKED_ARGS = [ctypes.c_int] + _GQA_ARGS[:-1] + [ctypes.POINTER(PartialMasksC), ctypes.c_void_p]
+_T = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
+_BWD_ARGS = ([ctypes.c_int] * 8 + _T * 7
+             + [ctypes.c_float, ctypes.POINTER(MaskDescC), ctypes.POINTER(MaskInfoC), ctypes.POINTER(MaskInfoC),
+                ctypes.c_void_p])
 
 _lib = None
 
@@ -97,9 +103,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     lib.splash_mask_info_entries.restype = ctypes.c_size_t
     lib.splash_mask_info_entries.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(MaskDescC)]
-    lib.splash_mask_info_build.restype = ctypes.c_int
-    lib.splash_mask_info_build.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(MaskDescC),
-                                                                ctypes.POINTER(MaskInfoC), ctypes.c_void_p]
+    for name in ("splash_mask_info_build", "splash_mask_info_build_dkv"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(MaskDescC), ctypes.POINTER(MaskInfoC), ctypes.c_void_p]
+    lib.splash_pointwise_bwd.restype = ctypes.c_int
+    lib.splash_pointwise_bwd.argtypes = _BWD_ARGS
     for name in ("splash_fwd", "splash_pointwise_fwd"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -251,6 +260,21 @@ def mask_info_build(B: int, H: int, q_len: int, kv_len: int, head_masks, block_q
     ``head_masks``: one (causal, window_left, window_right) triple for every
     head, or a single one broadcast to all heads. ``out`` reuses the buffers of
     an earlier MaskInfo of the same shape."""
+    return _mask_info(False, B, H, q_len, kv_len, head_masks, block_q, block_kv, q_segment_ids, kv_segment_ids,
+                      device, out)
+
+
+def mask_info_build_dkv(B: int, H: int, q_len: int, kv_len: int, head_masks, block_q: int = 128,
+                        block_kv: int = 128, q_segment_ids=None, kv_segment_ids=None,
+                        device="cuda", out: MaskInfo | None = None) -> MaskInfo:
+    """Metadata of the backward's dK/dV pass: the same block classes, with
+    ``data_next`` walking each kv-block column over q blocks."""
+    return _mask_info(True, B, H, q_len, kv_len, head_masks, block_q, block_kv, q_segment_ids, kv_segment_ids,
+                      device, out)
+
+
+def _mask_info(dkv: bool, B, H, q_len, kv_len, head_masks, block_q, block_kv, q_segment_ids, kv_segment_ids,
+               device, out) -> MaskInfo:
     lib = load_library()
     device = torch.device(device)
     head_masks = tuple(tuple(int(x) for x in m) for m in head_masks)
@@ -273,8 +297,9 @@ def mask_info_build(B: int, H: int, q_len: int, kv_len: int, head_masks, block_q
                     bmask, dnext)
     desc, keep = info.mask_desc()
     cinfo = info.info_struct()
-    st = lib.splash_mask_info_build(B, H, q_len, kv_len, block_q, block_kv, ctypes.byref(desc),
-                                    ctypes.byref(cinfo), ctypes.c_void_p(_stream(device)))
+    fn = lib.splash_mask_info_build_dkv if dkv else lib.splash_mask_info_build
+    st = fn(B, H, q_len, kv_len, block_q, block_kv, ctypes.byref(desc), ctypes.byref(cinfo),
+            ctypes.c_void_p(_stream(device)))
     del keep
     _check(st)
     return info
@@ -360,3 +385,61 @@ def pointwise_fwd(q, k, v, info: MaskInfo, scale: float | None = None, out=None,
     """Pointwise SiLU attention forward: (1/Sq) sum_k silu(scale q.k) v_k;
     k/v may have fewer heads than q, as for ``splash_fwd``."""
     return _forward(True, q, k, v, info, scale, out, out_dtype, layout)
+
+
+# ---------------------------------------------------------------------------
+# pointwise backward
+# ---------------------------------------------------------------------------
+
+
+def pointwise_bwd(q, k, v, d_o, info: MaskInfo, info_dkv: MaskInfo, scale: float | None = None,
+                  out_dtype=None, layout: str = "bhsd", out=None):
+    """Gradients (dq, dk, dv) of ``pointwise_fwd`` for the output gradient
+    ``d_o``: ``info`` from ``mask_info_build`` (dQ pass), ``info_dkv`` from
+    ``mask_info_build_dkv`` (dK/dV pass), both for the same mask. k and v may
+    have fewer heads than q (a K/V head's gradients sum over its query
+    heads). ``out``: an optional (dq, dk, dv) to write into."""
+    lib = load_library()
+    if q.dtype not in _DT or any(t.dtype != q.dtype for t in (k, v, d_o)):
+        raise ValueError("q, k, v, d_o must share dtype float32 or bfloat16")
+    if not all(t.is_cuda for t in (q, k, v, d_o)):
+        raise ValueError("q, k, v, d_o must be GPU tensors")
+    qs, (B, H, Sq, D) = _strides(q, layout)
+    ks, (Bk, Hk, Skv, Dk) = _strides(k, layout)
+    vs, vshape = _strides(v, layout)
+    dos, doshape = _strides(d_o, layout)
+    if (Bk, Dk) != (B, D) or vshape != (B, Hk, Skv, D) or doshape != (B, H, Sq, D) or Hk < 1 or H % Hk:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)} "
+                         f"d_o {tuple(d_o.shape)} ({layout})")
+    if out_dtype is None:
+        out_dtype = q.dtype if out is None else out[0].dtype
+    if out is None:
+        out = (torch.empty_like(q, dtype=out_dtype), torch.empty_like(k, dtype=out_dtype),
+               torch.empty_like(v, dtype=out_dtype))
+    dq, dk, dv = out
+    if any(t.dtype != out_dtype for t in out) or out_dtype not in _DT:
+        raise ValueError("bad gradient dtype")
+    dqs, dqshape = _strides(dq, layout)
+    dks, dkshape = _strides(dk, layout)
+    dvs, dvshape = _strides(dv, layout)
+    if dqshape != (B, H, Sq, D) or dkshape != (B, Hk, Skv, D) or dvshape != (B, Hk, Skv, D):
+        raise ValueError("gradient shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    for m in (info, info_dkv):
+        if (m.B, m.H, m.q_len, m.kv_len) != (B, H, Sq, Skv) or m.dense:
+            raise SplashError(SPLASH_ERR_METADATA_MISMATCH,
+                              f"metadata built for B={m.B} H={m.H} q_len={m.q_len} kv_len={m.kv_len}"
+                              + (" (dense masks)" if m.dense else ""))
+    if info.head_masks != info_dkv.head_masks:
+        raise ValueError("info and info_dkv were built for different masks")
+    desc, keep = info.mask_desc()
+    c1, c2 = info.info_struct(), info_dkv.info_struct()
+    st = lib.splash_pointwise_bwd(_DT[q.dtype], _DT[out_dtype], B, H, Hk, Sq, Skv, D,
+                                  q.data_ptr(), qs, k.data_ptr(), ks, v.data_ptr(), vs, d_o.data_ptr(), dos,
+                                  dq.data_ptr(), dqs, dk.data_ptr(), dks, dv.data_ptr(), dvs,
+                                  float(scale), ctypes.byref(desc), ctypes.byref(c1), ctypes.byref(c2),
+                                  ctypes.c_void_p(_stream(q.device)))
+    del keep
+    _check(st)
+    return dq, dk, dv

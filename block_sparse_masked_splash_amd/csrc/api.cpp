@@ -212,6 +212,131 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
   return hip_status(e, pointwise ? "pointwise forward launch" : "softmax forward launch");
 }
 
+// Checks one metadata struct against the call; `what` names it in messages.
+splash_status check_info(const char* what, const splash_mask_info* info, int B, int H, int q_len, int kv_len,
+                         bool seg, int nm, bool work) {
+  if (info == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s is null", what);
+  const int bq = info->block_q, bkv = info->block_kv;
+  if (bq <= 0 || bkv <= 0)
+    return record_error(SPLASH_ERR_METADATA_MISMATCH, "%s block sizes %d x %d", what, bq, bkv);
+  const int64_t nq = ceil_div(q_len, bq), nk = ceil_div(kv_len, bkv);
+  if (info->meta_batch != (seg ? B : 1) || info->meta_heads != nm || info->num_q_blocks != nq ||
+      info->num_kv_blocks != nk)
+    return record_error(SPLASH_ERR_METADATA_MISMATCH,
+                        "%s [%d,%d,%d,%d] but this call needs [%d,%d,%lld,%lld] (segment ids %s)", what,
+                        info->meta_batch, info->meta_heads, info->num_q_blocks, info->num_kv_blocks, seg ? B : 1, nm,
+                        (long long)nq, (long long)nk, seg ? "given" : "absent");
+  (void)H;
+  if (work && nq > 0 && nk > 0 && (info->block_mask == nullptr || info->data_next == nullptr))
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s arrays are null", what);
+  return SPLASH_OK;
+}
+
+splash_status bwd_common(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads, int q_len,
+                         int kv_len, int head_dim, const void* q, const int64_t q_strides[3], const void* k,
+                         const int64_t k_strides[3], const void* v, const int64_t v_strides[3], const void* d_o,
+                         const int64_t do_strides[3], void* dq, const int64_t dq_strides[3], void* dk,
+                         const int64_t dk_strides[3], void* dv, const int64_t dv_strides[3], float scale,
+                         const splash_mask_desc* mask, const splash_mask_info* info,
+                         const splash_mask_info* info_dkv, hipStream_t stream) {
+  splash_status s = check_sizes(B, H, q_len, kv_len);
+  if (s != SPLASH_OK) return s;
+  if (kv_heads < 1 || kv_heads > H || H % kv_heads != 0)
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "kv_heads=%d must divide H=%d", kv_heads, H);
+  const bool f32 = in_dtype == SPLASH_F32 && out_dtype == SPLASH_F32;
+  const bool bf16 = in_dtype == SPLASH_BF16 && (out_dtype == SPLASH_BF16 || out_dtype == SPLASH_F32);
+  if (!f32 && !bf16)
+    return record_error(SPLASH_ERR_UNSUPPORTED, "dtype pair in=%d out=%d (supported: f32->f32, bf16->bf16, bf16->f32)",
+                        (int)in_dtype, (int)out_dtype);
+  if (head_dim <= 0) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "head_dim=%d", head_dim);
+  if (head_dim != 64 && head_dim != 128)
+    return record_error(SPLASH_ERR_UNSUPPORTED, "head_dim=%d (supported: 64, 128)", head_dim);
+  if (!std::isfinite(scale)) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "scale is not finite");
+
+  splash::BwdParams p{};
+  s = check_mask(H, mask, p.band);
+  if (s != SPLASH_OK) return s;
+  const bool seg = mask->q_segment_ids != nullptr;
+  const int nm = mask->num_mask_heads;
+  const bool qwork = (int64_t)B * H * q_len > 0;
+  const bool kwork = (int64_t)B * kv_heads * kv_len > 0;
+  const bool work = qwork || kwork;
+  if ((s = check_info("info", info, B, H, q_len, kv_len, seg, nm, work)) != SPLASH_OK) return s;
+  if ((s = check_info("info_dkv", info_dkv, B, H, q_len, kv_len, seg, nm, work)) != SPLASH_OK) return s;
+  const int bq = info->block_q, bkv = info->block_kv;
+  if ((bq != 64 && bq != 128 && bq != 256) || (bkv != 64 && bkv != 128))
+    return record_error(SPLASH_ERR_UNSUPPORTED, "info block sizes %d x %d (supported: block_q 64, 128 or 256; "
+                        "block_kv 64 or 128)", bq, bkv);
+  const int cbq = info_dkv->block_q, cbkv = info_dkv->block_kv;
+  if (cbq % 32 != 0 || cbq > 1024 || (cbkv != 64 && cbkv != 128))
+    return record_error(SPLASH_ERR_UNSUPPORTED, "info_dkv block sizes %d x %d (supported: block_q a multiple of 32 "
+                        "up to 1024; block_kv 64 or 128)", cbq, cbkv);
+
+  const int in_bytes = in_dtype == SPLASH_F32 ? 4 : 2;
+  const int out_bytes = out_dtype == SPLASH_F32 ? 4 : 2;
+  const bool both = qwork && kwork;  // q-side and kv-side rows exist
+  if ((s = check_tensor("q", q, q_strides, in_bytes, both)) != SPLASH_OK) return s;
+  if ((s = check_tensor("k", k, k_strides, in_bytes, both)) != SPLASH_OK) return s;
+  if ((s = check_tensor("v", v, v_strides, in_bytes, both)) != SPLASH_OK) return s;
+  if ((s = check_tensor("d_o", d_o, do_strides, in_bytes, both)) != SPLASH_OK) return s;
+  if ((s = check_tensor("dq", dq, dq_strides, out_bytes, qwork)) != SPLASH_OK) return s;
+  if ((s = check_tensor("dk", dk, dk_strides, out_bytes, kwork)) != SPLASH_OK) return s;
+  if ((s = check_tensor("dv", dv, dv_strides, out_bytes, kwork)) != SPLASH_OK) return s;
+  if (!work) return ok();
+  const int64_t nq = ceil_div(q_len, bq), nk = ceil_div(kv_len, bkv);
+  const int64_t cnq = ceil_div(q_len, cbq), cnk = ceil_div(kv_len, cbkv);
+  if (nq * B * H >= (int64_t)1 << 31 || cnk * B * kv_heads >= (int64_t)1 << 31)
+    return record_error(SPLASH_ERR_UNSUPPORTED, "too many workgroups for one launch");
+
+  p.B = B;
+  p.H = H;
+  p.band_heads = nm;
+  p.kv_heads = kv_heads;
+  p.kv_group = H / kv_heads;
+  p.q_len = q_len;
+  p.kv_len = kv_len;
+  p.head_dim = head_dim;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.d_o = d_o;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.q_sb = q_strides[0], p.q_sh = q_strides[1], p.q_ss = q_strides[2];
+  p.k_sb = k_strides[0], p.k_sh = k_strides[1], p.k_ss = k_strides[2];
+  p.v_sb = v_strides[0], p.v_sh = v_strides[1], p.v_ss = v_strides[2];
+  p.do_sb = do_strides[0], p.do_sh = do_strides[1], p.do_ss = do_strides[2];
+  p.dq_sb = dq_strides[0], p.dq_sh = dq_strides[1], p.dq_ss = dq_strides[2];
+  p.dk_sb = dk_strides[0], p.dk_sh = dk_strides[1], p.dk_ss = dk_strides[2];
+  p.dv_sb = dv_strides[0], p.dv_sh = dv_strides[1], p.dv_ss = dv_strides[2];
+  p.scale = scale;
+  p.inv_q_len = q_len > 0 ? 1.0f / (float)q_len : 0.0f;
+  p.meta_batch = seg ? B : 1;
+  p.block_q = bq;
+  p.block_kv = bkv;
+  p.nq = (int)nq;
+  p.nk = (int)nk;
+  p.meta_heads = info->meta_heads;
+  p.block_mask = info->block_mask;
+  p.data_next = info->data_next;
+  p.c_block_q = cbq;
+  p.c_block_kv = cbkv;
+  p.c_nq = (int)cnq;
+  p.c_nk = (int)cnk;
+  p.c_meta_heads = info_dkv->meta_heads;
+  p.c_block_mask = info_dkv->block_mask;
+  p.c_data_next = info_dkv->data_next;
+  p.q_seg = mask->q_segment_ids;
+  p.kv_seg = mask->kv_segment_ids;
+  hipError_t e = f32 ? splash::launch_pointwise_bwd_f32(p, stream)
+                     : splash::launch_pointwise_bwd_bf16(p, out_dtype == SPLASH_F32, stream);
+  return hip_status(e, "pointwise backward launch");
+}
+
+splash_status mask_info_common(bool dkv, int B, int H, int q_len, int kv_len, int block_q, int block_kv,
+                               const splash_mask_desc* mask, const splash_mask_info* info, hipStream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -245,6 +370,34 @@ size_t splash_mask_info_entries(int B, int H, int q_len, int kv_len, int block_q
 splash_status splash_mask_info_build(int B, int H, int q_len, int kv_len, int block_q, int block_kv,
                                      const splash_mask_desc* mask, const splash_mask_info* info,
                                      hipStream_t stream) {
+  return mask_info_common(false, B, H, q_len, kv_len, block_q, block_kv, mask, info, stream);
+}
+
+splash_status splash_mask_info_build_dkv(int B, int H, int q_len, int kv_len, int block_q, int block_kv,
+                                         const splash_mask_desc* mask, const splash_mask_info* info,
+                                         hipStream_t stream) {
+  return mask_info_common(true, B, H, q_len, kv_len, block_q, block_kv, mask, info, stream);
+}
+
+splash_status splash_pointwise_bwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
+                                   int q_len, int kv_len, int head_dim, const void* q, const int64_t q_strides[3],
+                                   const void* k, const int64_t k_strides[3], const void* v,
+                                   const int64_t v_strides[3], const void* d_o, const int64_t do_strides[3],
+                                   void* dq, const int64_t dq_strides[3], void* dk, const int64_t dk_strides[3],
+                                   void* dv, const int64_t dv_strides[3], float scale,
+                                   const splash_mask_desc* mask, const splash_mask_info* info,
+                                   const splash_mask_info* info_dkv, hipStream_t stream) {
+  return bwd_common(in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides, v,
+                    v_strides, d_o, do_strides, dq, dq_strides, dk, dk_strides, dv, dv_strides, scale, mask, info,
+                    info_dkv, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+splash_status mask_info_common(bool dkv, int B, int H, int q_len, int kv_len, int block_q, int block_kv,
+                               const splash_mask_desc* mask, const splash_mask_info* info, hipStream_t stream) {
   splash_status s = check_sizes(B, H, q_len, kv_len);
   if (s != SPLASH_OK) return s;
   if (block_q < 1 || block_q > 1024 || block_kv < 1 || block_kv > 1024)
@@ -280,8 +433,13 @@ splash_status splash_mask_info_build(int B, int H, int q_len, int kv_len, int bl
   p.kv_seg = mask->kv_segment_ids;
   p.block_mask = info->block_mask;
   p.data_next = info->data_next;
-  return hip_status(splash::launch_mask_info(p, stream), "splash_mask_info_build launch");
+  return dkv ? hip_status(splash::launch_mask_info_dkv(p, stream), "splash_mask_info_build_dkv launch")
+             : hip_status(splash::launch_mask_info(p, stream), "splash_mask_info_build launch");
 }
+
+}  // namespace
+
+extern "C" {
 
 splash_status splash_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int q_len, int kv_len,
                          int head_dim, const void* q, const int64_t q_strides[3], const void* k,

@@ -67,11 +67,53 @@ struct FwdParams {
   HeadBand band[SPLASH_MAX_MASK_HEADS];
 };
 
+// Pointwise backward: dQ over the row walk (data_next along kv blocks), dK
+// and dV over the column walk (data_next along q blocks).
+struct BwdParams {
+  int B, H, q_len, kv_len, head_dim;
+  int band_heads;    // head masks in band[] (1: shared by every head)
+  int kv_heads;      // K/V heads; query head h reads kv head h / kv_group
+  int kv_group;      // H / kv_heads
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* d_o;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int64_t v_sb, v_sh, v_ss;
+  int64_t do_sb, do_sh, do_ss;
+  int64_t dq_sb, dq_sh, dq_ss;
+  int64_t dk_sb, dk_sh, dk_ss;
+  int64_t dv_sb, dv_sh, dv_ss;
+  float scale;       // score scale
+  float inv_q_len;   // 1 / q_len
+  int meta_batch;    // 1 or B, both walks
+  // row walk (dQ): [meta_batch, meta_heads, nq, nk]
+  int block_q, block_kv, nq, nk, meta_heads;
+  const int8_t* block_mask;
+  const int32_t* data_next;
+  // column walk (dK, dV): [meta_batch, c_meta_heads, c_nq, c_nk]
+  int c_block_q, c_block_kv, c_nq, c_nk, c_meta_heads;
+  const int8_t* c_block_mask;
+  const int32_t* c_data_next;
+  const int32_t* q_seg;
+  const int32_t* kv_seg;
+  HeadBand band[SPLASH_MAX_MASK_HEADS];
+};
+
 // Launchers; return the launch error (hipSuccess when enqueued).
 hipError_t launch_mask_info(const MaskInfoParams& p, hipStream_t stream);
+// Same classes, data_next along the q blocks of each kv-block column.
+hipError_t launch_mask_info_dkv(const MaskInfoParams& p, hipStream_t stream);
 // bf16 inputs, matrix-core path. out_f32 selects an fp32 output.
 hipError_t launch_fwd_bf16(const FwdParams& p, bool pointwise, bool out_f32, hipStream_t stream);
 // fp32 inputs and output.
 hipError_t launch_fwd_f32(const FwdParams& p, bool pointwise, hipStream_t stream);
+// Pointwise backward, bf16 inputs (gradients bf16 or fp32) and fp32 inputs.
+hipError_t launch_pointwise_bwd_bf16(const BwdParams& p, bool out_f32, hipStream_t stream);
+hipError_t launch_pointwise_bwd_f32(const BwdParams& p, hipStream_t stream);
 
 }  // namespace splash

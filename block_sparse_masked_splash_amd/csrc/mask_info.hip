@@ -19,6 +19,12 @@
 // row: the row is walked back to front in chunks of 64 kv blocks, a ballot
 // marks the non-empty ones, and each lane takes the lowest marked block at or
 // after it, else the carry from the chunks already done.
+//
+// The dK/dV pass of the pointwise backward walks columns instead ("hstu_ops.py",
+// _pointwise_splash_attention_bwd_kernel: grid over kv blocks, then heads,
+// then q steps; _next_nonzero(next_i=True) reads data_next[h, i, j] as the
+// q block to fetch). Its metadata has the same classes, and data_next[.., i, j]
+// is the first non-empty q block at or after i in column j (nq if none).
 
 #include "internal.h"
 
@@ -202,7 +208,40 @@ __global__ __launch_bounds__(256) void row_scan_kernel(MaskInfoParams p) {
   }
 }
 
+// Column walk of the dK/dV pass: one wavefront per (metadata batch, head,
+// kv block) column, the same back-to-front ballot scan over its q blocks.
+__global__ __launch_bounds__(256) void column_scan_kernel(MaskInfoParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t col = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t cols = (int64_t)p.meta_batch * p.meta_heads * p.nk;
+  if (col >= cols) return;
+  const int j = (int)(col % p.nk);
+  const int64_t plane = col / p.nk;  // (bm, hm)
+  const int8_t* bmask = p.block_mask + plane * p.nq * p.nk + j;
+  int32_t* dnext = p.data_next + plane * p.nq * p.nk + j;
+  int carry = p.nq;
+  const int nchunks = (p.nq + 63) / 64;
+  for (int c = nchunks - 1; c >= 0; --c) {
+    const int i = c * 64 + lane;
+    const int cls = i < p.nq ? bmask[(int64_t)i * p.nk] : 0;
+    const uint64_t bits = __ballot(cls != 0);
+    const uint64_t at_or_after = bits >> lane;
+    if (i < p.nq) dnext[(int64_t)i * p.nk] = at_or_after ? i + __builtin_ctzll(at_or_after) : carry;
+    if (bits) carry = c * 64 + __builtin_ctzll(bits);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mask_info_dkv(const MaskInfoParams& p, hipStream_t stream) {
+  // classes (and a row scan whose data_next the column scan then replaces)
+  hipError_t e = launch_mask_info(p, stream);
+  if (e != hipSuccess) return e;
+  const int64_t cols = (int64_t)p.meta_batch * p.meta_heads * p.nk;
+  if (cols == 0 || p.nq == 0) return hipSuccess;
+  hipLaunchKernelGGL(column_scan_kernel, dim3((unsigned)((cols + 3) / 4)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_mask_info(const MaskInfoParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.meta_batch * p.meta_heads * p.nq;

@@ -1,0 +1,624 @@
+// Pointwise (SiLU) attention backward, bf16 inputs, CDNA4 matrix cores.
+//
+// What is computed ("hstu_ops.py" (RecML), _pointwise_splash_attention_bwd_kernel_impl):
+// with x = scale q·k, sig = logistic(x) (0 where the mask forbids the pair),
+//   p  = x sig / q_len                      dV_k += sum_q p dO_q
+//   dp = dO_q · v_k
+//   ds = dp sig (1 + x (1 - sig)) / q_len   dK_k += scale sum_q ds q_q
+//                                           dQ_q += scale sum_k ds k_k
+// Here the weights are kept without the constant factors (p' = x sig,
+// ds' = dp (sig + p' (1 - sig)), the same as dp sig (1 + x (1 - sig))); the
+// factors 1 / q_len and scale / q_len are applied once to the sums.
+//
+// Two kernels, each with its own walk over the non-empty blocks, neither
+// needing any cross-workgroup reduction:
+//   * dK / dV: one workgroup per (b, K/V head, kv block j), wavefront w owning
+//     keys j bkv + 32 w .. + 31. The kv block's column is walked over q
+//     blocks with the column metadata (data_next along q blocks, as the
+//     page's dK/dV grid walks q steps with _next_nonzero(next_i=True)),
+//     for every query head that reads this K/V head. Q and dO come through
+//     LDS in tiles of 32 queries (direct HBM -> LDS copies, double-buffered);
+//     the wavefront's K and V rows stay in registers as B operands:
+//       S  = Q Kᵀ,  dP = dO Vᵀ        (A = Q / dO rows from LDS)
+//       dVᵀ += dOᵀ P',  dKᵀ += Qᵀ dS'  (A = transposing LDS reads of dO / Q)
+//     so the probabilities go from the accumulator straight into the B
+//     operand, as in the forward.
+//   * dQ: one workgroup per (b, query head, q block i), the forward's row walk
+//     with Q and dO in registers: Sᵀ = K Qᵀ, dPᵀ = V dOᵀ, dQᵀ += Kᵀ dSᵀ.
+// The dK/dV pass recomputes S and dP that the dQ pass also forms (7 products
+// per block pair instead of 5), in exchange for deterministic sums with no
+// atomics and no per-kv-block partial dQ.
+
+#include <type_traits>
+
+#include "cdna4.h"
+
+namespace splash {
+namespace {
+
+// sig, p' = x sig and ds' = dp (sig + p' (1 - sig)) of one score; masked
+// pairs get sig = 0, hence p' = ds' = 0. nl = -scale log2(e).
+struct Weights {
+  float p, ds;
+};
+__device__ inline Weights pointwise_weights(float acc, float dp, float scale, float nl, bool ok) {
+  const float x = acc * scale;
+  const float sg = ok ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(acc * nl)) : 0.0f;
+  const float pv = x * sg;
+  return {pv, dp * __builtin_fmaf(pv, 1.0f - sg, sg)};
+}
+
+// XCD-aware work order shared by both passes: workgroup ids are dealt
+// round-robin to the 8 XCDs; XCD x takes units x, x + 8, ... when the number
+// of units is a multiple of 8, else a contiguous eighth of the work list.
+// Returns false for an id past the end of the list.
+__device__ inline bool work_item(int per_unit, int total_work, int work_per_xcd, int units_interleaved, int& unit,
+                                 int& rest) {
+  const int xcd = (int)(blockIdx.x & 7), k_in_xcd = (int)(blockIdx.x >> 3);
+  if (units_interleaved) {
+    const int uk = k_in_xcd / per_unit;
+    unit = xcd + 8 * uk;
+    rest = k_in_xcd - uk * per_unit;
+    return true;
+  }
+  const int wid = xcd * work_per_xcd + k_in_xcd;
+  if (wid >= total_work) return false;
+  unit = wid / per_unit;
+  rest = wid - unit * per_unit;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV
+// ---------------------------------------------------------------------------
+
+template <int D, int NW>
+struct DkvTiling {
+  static constexpr int QC = 32;                  // queries per LDS tile
+  static constexpr int ROWB = D * 2;
+  static constexpr int RPI = 64 / (D / 8);       // rows per direct-copy instruction
+  static constexpr int TILE = QC * ROWB;
+  static constexpr int LOADS = (QC / RPI) / NW;  // copies per wave per matrix per tile
+  static constexpr int SEG_ROWS = QC / NW;       // query ids copied per wave per tile
+  static constexpr int NS = D / 16;
+  static constexpr int ND = D / 32;
+  static constexpr int SEG_OFF = 2 * 2 * TILE;   // [stage][Q | dO][TILE], then [stage][QC] ids
+  static constexpr int LDS_BYTES = SEG_OFF + 2 * QC * 4;
+  static_assert(LOADS >= 1, "tile too small for the workgroup");
+};
+
+// D = 64: about 160 VGPRs, three wavefronts per SIMD. D = 128: K, V and the
+// two accumulators alone take 192 VGPRs, and the whole step about 270, more
+// than two wavefronts per SIMD can hold without spilling: one.
+template <int D>
+constexpr int dkv_waves() {
+  return D == 64 ? 3 : 1;
+}
+
+template <int D, int NW, typename OutT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dkv_waves<D>(), dkv_waves<D>())))
+void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
+  using T = DkvTiling<D, NW>;
+  constexpr int NS = T::NS;
+  constexpr int ND = T::ND;
+  constexpr int QC = T::QC;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+
+  int unit, j;
+  if (!work_item(p.c_nk, total_work, work_per_xcd, units_interleaved, unit, j)) return;
+  // j ascending: under causal masks the first kv blocks have the longest columns
+  const int b = unit / p.kv_heads;
+  const int hk = unit - b * p.kv_heads;
+  const int bm = p.meta_batch == 1 ? 0 : b;
+  const int G = p.kv_group;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int key = j * p.c_block_kv + wave * 32 + l32;
+  const bool kvalid = key < p.kv_len;
+  const bool has_seg = p.q_seg != nullptr;
+
+  // ---- this lane's key: K and V rows as B operands (head-dim 16 s + 8 hh ..) ----
+  bf16x8 kreg[NS], vreg[NS];
+  {
+    const __bf16* kr = reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh + (int64_t)key * p.k_ss;
+    const __bf16* vr = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh + (int64_t)key * p.v_ss;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      i16x8 a = {0, 0, 0, 0, 0, 0, 0, 0}, c = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (kvalid) {
+        a = *reinterpret_cast<const i16x8*>(kr + 16 * s + 8 * hh);
+        c = *reinterpret_cast<const i16x8*>(vr + 16 * s + 8 * hh);
+      }
+      kreg[s] = __builtin_bit_cast(bf16x8, a);
+      vreg[s] = __builtin_bit_cast(bf16x8, c);
+    }
+  }
+  const int32_t kseg = (has_seg && kvalid) ? p.kv_seg[(int64_t)b * p.kv_len + key] : 0;
+
+  int aoff[NS];
+  row_operand_offsets<D>(lane, aoff);
+  int toff[2][ND];
+  transpose_operand_offsets<D>(lane, toff);
+  const int64_t q_rs = p.q_ss * 2, do_rs = p.do_ss * 2;
+  uint32_t qsel[T::LOADS], dsel[T::LOADS];
+  tile_copy_offsets<D, NW>(lane, wave, q_rs, qsel);
+  tile_copy_offsets<D, NW>(lane, wave, do_rs, dsel);
+
+  // ---- column walk over (query head of the group, q block, 32-query tile) ----
+  auto entry = [&](int g, int i) -> int64_t {
+    const int h = hk * G + g;
+    const int hm = p.c_meta_heads == 1 ? 0 : h;
+    return (((int64_t)bm * p.c_meta_heads + hm) * p.c_nq + i) * p.c_nk + j;
+  };
+  // data_next is only followed forward and within [0, nq], so any metadata
+  // content ends the walk in bounds.
+  auto first_i = [&](int g) {
+    if (p.c_nq == 0) return p.c_nq;
+    const int i = scalar_load_i32(p.c_data_next + entry(g, 0));
+    return (i >= 0 && i <= p.c_nq) ? i : p.c_nq;
+  };
+  auto next_i = [&](int g, int i) {
+    const int in = (i + 1 < p.c_nq) ? scalar_load_i32(p.c_data_next + entry(g, i + 1)) : p.c_nq;
+    return (in > i && in <= p.c_nq) ? in : p.c_nq;
+  };
+  // the first (g, i) at or after head g with a non-empty block (g == G: none)
+  auto settle = [&](int& g, int& i) {
+    while (i >= p.c_nq) {
+      if (++g >= G) return;
+      i = first_i(g);
+    }
+  };
+  auto class_of = [&](int g, int i) {
+    const int64_t e = entry(g, i);
+    return block_class(p.c_block_mask + (e - j), j);
+  };
+
+  auto issue_tile = [&](int stage, int g, int i, int t) {
+    const int h = hk * G + g;
+    const int q0 = i * p.c_block_q + t;
+    const int rows = p.q_len - q0 < QC ? p.q_len - q0 : QC;  // rows past the end read as 0
+    const char* qg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh);
+    const char* dg =
+        reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.d_o) + b * p.do_sb + h * p.do_sh);
+    char* qdst = smem + stage * 2 * T::TILE;
+    char* ddst = qdst + T::TILE;
+    const u32x4 qrs = buffer_rsrc(qg + q0 * q_rs, (uint32_t)(rows * q_rs));
+    const u32x4 drs = buffer_rsrc(dg + q0 * do_rs, (uint32_t)(rows * do_rs));
+    lds_copy_rows<T::LOADS, NW * 1024>(qrs, qsel, (uint32_t)(wave * T::RPI * q_rs), (uint32_t)(NW * T::RPI * q_rs),
+                                       lds_addr(qdst + wave * T::RPI * T::ROWB));
+    lds_copy_rows<T::LOADS, NW * 1024>(drs, dsel, (uint32_t)(wave * T::RPI * do_rs), (uint32_t)(NW * T::RPI * do_rs),
+                                       lds_addr(ddst + wave * T::RPI * T::ROWB));
+    if (has_seg) {
+      const uint32_t sdst =
+          lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * QC + wave * T::SEG_ROWS);
+      const u32x4 srs = buffer_rsrc(p.q_seg + (int64_t)b * p.q_len + q0, (uint32_t)(rows * 4));
+      if (lane < T::SEG_ROWS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), sdst);
+    }
+  };
+
+  // Zeroed tiles: rows a clipped copy leaves unwritten hold zeros, never NaN.
+  for (int o = tid * 16; o < T::SEG_OFF; o += NW * 64 * 16)
+    *reinterpret_cast<uint4*>(smem + o) = uint4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  f32x16 dk[ND], dv[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[db][r] = 0.0f;
+      dv[db][r] = 0.0f;
+    }
+  const float scale = p.scale;
+  const float nl = -p.scale * 1.4426950408889634f;
+
+  int cur_g = 0, cur_i = first_i(0), cur_t = 0;
+  settle(cur_g, cur_i);
+  if (cur_g < G) issue_tile(0, cur_g, cur_i, 0);
+
+  auto step = [&](auto stage_tag) -> bool {
+    constexpr int stage = decltype(stage_tag)::value;
+    int ng = cur_g, ni = cur_i, nt = cur_t + QC;
+    if (nt >= p.c_block_q || ni * p.c_block_q + nt >= p.q_len) {
+      ni = next_i(ng, ni);
+      nt = 0;
+      settle(ng, ni);
+    }
+    wait_vmcnt<0>();  // this wave's copies of the current tile are in LDS
+    barrier_only();   // everyone's are, and the other stage is free again
+    if (ng < G) issue_tile(stage ^ 1, ng, ni, nt);
+
+    const int h = hk * G + cur_g;
+    const HeadBand band = p.band[p.band_heads == 1 ? 0 : h];
+    const bool partial = class_of(cur_g, cur_i) == 1;
+    const int q0 = cur_i * p.c_block_q + cur_t;
+    const char* qt = smem + stage * 2 * T::TILE;
+    const char* dt = qt + T::TILE;
+    const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * QC;
+
+    // ---- S = Q Kᵀ and dP = dO Vᵀ: 32 queries (rows) x this wave's 32 keys ----
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sacc[r] = 0.0f;
+      pacc[r] = 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qt + aoff[s]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[s], sacc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(dt + aoff[s]);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vreg[s], pacc, 0, 0, 0);
+    }
+
+    // element r: query q0 + 8 (r / 4) + 4 hh + r % 4, key `key`. On a partial
+    // block the band, the sequence ends and (with ids) segment equality leave
+    // the lane's key one run of queries [a, e] of the tile plus the id test.
+    bool ok[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ok[r] = true;
+    if (partial) {
+      int a = key - band.hi - q0;
+      int e = key - band.lo - q0;
+      a = a > 0 ? a : 0;
+      e = e < p.q_len - 1 - q0 ? e : p.q_len - 1 - q0;
+      e = e < QC - 1 ? e : QC - 1;
+      if (e < a || !kvalid) a = e = QC;  // no query of the tile
+      const uint32_t width = (uint32_t)(e - a);
+      const int base = 4 * hh - a;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ok[r] = (uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width;
+      if (has_seg) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int4 qs4 = *reinterpret_cast<const int4*>(sseg + 8 * u + 4 * hh);
+          ok[4 * u + 0] &= qs4.x == kseg;
+          ok[4 * u + 1] &= qs4.y == kseg;
+          ok[4 * u + 2] &= qs4.z == kseg;
+          ok[4 * u + 3] &= qs4.w == kseg;
+        }
+      }
+    }
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const Weights w = pointwise_weights(sacc[r], pacc[r], scale, nl, ok[r]);
+      pb[r >> 3][r & 7] = (__bf16)w.p;
+      sb[r >> 3][r & 7] = (__bf16)w.ds;
+    }
+
+    // ---- dVᵀ += dOᵀ P', dKᵀ += Qᵀ dS' over the 32 queries ----
+#pragma unroll
+    for (int g2 = 0; g2 < 2; ++g2) {
+      const int rowbase = 16 * g2 * T::ROWB;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(dt + rowbase + toff[0][db]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(dt + rowbase + toff[1][db]));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g2], dv[db], 0, 0, 0);
+      }
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(qt + rowbase + toff[0][db]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(qt + rowbase + toff[1][db]));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[g2], dk[db], 0, 0, 0);
+      }
+    }
+
+    cur_g = ng;
+    cur_i = ni;
+    cur_t = nt;
+    return cur_g < G;
+  };
+  while (cur_g < G) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
+  }
+
+  // ---- dK = (scale / q_len) dK', dV = dV' / q_len; lane's key row ----
+  if (kvalid) {
+    const float ck = p.scale * p.inv_q_len, cv = p.inv_q_len;
+    OutT* dkr = reinterpret_cast<OutT*>(p.dk) + b * p.dk_sb + hk * p.dk_sh + (int64_t)key * p.dk_ss;
+    OutT* dvr = reinterpret_cast<OutT*>(p.dv) + b * p.dv_sb + hk * p.dv_sh + (int64_t)key * p.dv_ss;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * hh;
+        store4<OutT>(dkr + col, dk[db][4 * g] * ck, dk[db][4 * g + 1] * ck, dk[db][4 * g + 2] * ck,
+                     dk[db][4 * g + 3] * ck);
+        store4<OutT>(dvr + col, dv[db][4 * g] * cv, dv[db][4 * g + 1] * cv, dv[db][4 * g + 2] * cv,
+                     dv[db][4 * g + 3] * cv);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+
+template <int D, int NW>
+struct DqTiling {
+  static constexpr int KC = D == 128 ? 32 : 64;  // keys per LDS tile
+  static constexpr int ROWB = D * 2;
+  static constexpr int RPI = 64 / (D / 8);
+  static constexpr int TILE = KC * ROWB;
+  static constexpr int LOADS = (KC / RPI) / NW;
+  static constexpr int SEG_KEYS = KC / NW;
+  static constexpr int NS = D / 16;
+  static constexpr int ND = D / 32;
+  static constexpr int SEG_OFF = 2 * 2 * TILE;   // [stage][K | V][TILE], then [stage][KC] ids
+  static constexpr int LDS_BYTES = SEG_OFF + 2 * KC * 4;
+  static_assert(LOADS >= 1, "tile too small for the workgroup");
+};
+
+// about 135 VGPRs at D = 64 and 215 at D = 128
+template <int D>
+constexpr int dq_waves() {
+  return D == 64 ? 3 : 2;
+}
+
+template <int D, int NW, typename OutT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_waves<D>(), dq_waves<D>())))
+void pointwise_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
+  using T = DqTiling<D, NW>;
+  constexpr int KC = T::KC;
+  constexpr int NS = T::NS;
+  constexpr int ND = T::ND;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+
+  // unit = (b, K/V head) with its query heads; heaviest q blocks first
+  int unit, rest;
+  if (!work_item(p.nq * p.kv_group, total_work, work_per_xcd, units_interleaved, unit, rest)) return;
+  const int ri = rest / p.kv_group;
+  const int i = p.nq - 1 - ri;
+  const int b = unit / p.kv_heads;
+  const int hk = unit - b * p.kv_heads;
+  const int h = hk * p.kv_group + (rest - ri * p.kv_group);
+  const int hm = p.meta_heads == 1 ? 0 : h;
+  const int bm = p.meta_batch == 1 ? 0 : b;
+  const HeadBand band = p.band[p.band_heads == 1 ? 0 : h];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const char* kg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh);
+  const char* vg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh);
+  const int64_t k_rs = p.k_ss * 2, v_rs = p.v_ss * 2;
+  const bool has_seg = p.q_seg != nullptr;
+  const int32_t* kvseg_g = has_seg ? p.kv_seg + (int64_t)b * p.kv_len : nullptr;
+
+  // ---- this lane's query: Q and dO rows as B operands ----
+  const int qrow = i * p.block_q + wave * 32 + l32;
+  const bool qvalid = qrow < p.q_len;
+  bf16x8 qreg[NS], oreg[NS];
+  {
+    const __bf16* qr = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)qrow * p.q_ss;
+    const __bf16* orr = reinterpret_cast<const __bf16*>(p.d_o) + b * p.do_sb + h * p.do_sh + (int64_t)qrow * p.do_ss;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      i16x8 a = {0, 0, 0, 0, 0, 0, 0, 0}, c = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (qvalid) {
+        a = *reinterpret_cast<const i16x8*>(qr + 16 * s + 8 * hh);
+        c = *reinterpret_cast<const i16x8*>(orr + 16 * s + 8 * hh);
+      }
+      qreg[s] = __builtin_bit_cast(bf16x8, a);
+      oreg[s] = __builtin_bit_cast(bf16x8, c);
+    }
+  }
+  const int32_t myseg = (has_seg && qvalid) ? p.q_seg[(int64_t)b * p.q_len + qrow] : 0;
+
+  int aoff[NS];
+  row_operand_offsets<D>(lane, aoff);
+  int toff[2][ND];
+  transpose_operand_offsets<D>(lane, toff);
+  uint32_t ksel[T::LOADS], vsel[T::LOADS];
+  tile_copy_offsets<D, NW>(lane, wave, k_rs, ksel);
+  tile_copy_offsets<D, NW>(lane, wave, v_rs, vsel);
+
+  const int64_t mrow = (((int64_t)bm * p.meta_heads + hm) * p.nq + i) * p.nk;
+  const int8_t* bmask = p.block_mask + mrow;
+  const int32_t* dnext = p.data_next + mrow;
+
+  auto issue_tile = [&](int stage, int jj, int t) {
+    const int key0 = jj * p.block_kv + t;
+    char* kdst = smem + stage * 2 * T::TILE;
+    char* vdst = kdst + T::TILE;
+    const int rows = p.kv_len - key0 < KC ? p.kv_len - key0 : KC;
+    const u32x4 krs = buffer_rsrc(kg + key0 * k_rs, (uint32_t)(rows * k_rs));
+    const u32x4 vrs = buffer_rsrc(vg + key0 * v_rs, (uint32_t)(rows * v_rs));
+    lds_copy_rows<T::LOADS, NW * 1024>(krs, ksel, (uint32_t)(wave * T::RPI * k_rs), (uint32_t)(NW * T::RPI * k_rs),
+                                       lds_addr(kdst + wave * T::RPI * T::ROWB));
+    lds_copy_rows<T::LOADS, NW * 1024>(vrs, vsel, (uint32_t)(wave * T::RPI * v_rs), (uint32_t)(NW * T::RPI * v_rs),
+                                       lds_addr(vdst + wave * T::RPI * T::ROWB));
+    if (has_seg) {
+      const uint32_t sdst = lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * KC + wave * T::SEG_KEYS);
+      const u32x4 srs = buffer_rsrc(kvseg_g + key0, (uint32_t)(rows * 4));
+      if (lane < T::SEG_KEYS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_KEYS * 4), sdst);
+    }
+  };
+
+  for (int o = tid * 16; o < T::SEG_OFF; o += NW * 64 * 16)
+    *reinterpret_cast<uint4*>(smem + o) = uint4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  f32x16 dq[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
+  const float scale = p.scale;
+  const float nl = -p.scale * 1.4426950408889634f;
+
+  auto next_block = [&](int jj) {
+    const int jn = (jj + 1 < p.nk) ? scalar_load_i32(dnext + jj + 1) : p.nk;
+    return (jn > jj && jn <= p.nk) ? jn : p.nk;
+  };
+  int cur_j = p.nk > 0 ? scalar_load_i32(dnext) : p.nk;
+  if (cur_j < 0 || cur_j > p.nk) cur_j = p.nk;
+  int cur_t = 0;
+  if (cur_j < p.nk) issue_tile(0, cur_j, 0);
+
+  auto step = [&](auto stage_tag) -> bool {
+    constexpr int stage = decltype(stage_tag)::value;
+    int nxt_j = cur_j, nxt_t = cur_t + KC;
+    if (nxt_t >= p.block_kv || cur_j * p.block_kv + nxt_t >= p.kv_len) {
+      nxt_j = next_block(cur_j);
+      nxt_t = 0;
+    }
+    wait_vmcnt<0>();
+    barrier_only();
+    if (nxt_j < p.nk) issue_tile(stage ^ 1, nxt_j, nxt_t);
+
+    const int k0 = cur_j * p.block_kv + cur_t;
+    const bool partial = block_class(bmask, cur_j) == 1;
+    const char* kt = smem + stage * 2 * T::TILE;
+    const char* vt = kt + T::TILE;
+    const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * KC;
+#pragma unroll
+    for (int kb = 0; kb < KC / 32; ++kb) {
+      // ---- Sᵀ = K Qᵀ, dPᵀ = V dOᵀ: 32 keys (rows) x this wave's 32 queries ----
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[r] = 0.0f;
+        pacc[r] = 0.0f;
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * T::ROWB + aoff[s]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + kb * 32 * T::ROWB + aoff[s]);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, oreg[s], pacc, 0, 0, 0);
+      }
+      // element r: key k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4, query qrow
+      bool ok[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ok[r] = true;
+      if (partial) {
+        int a = qrow + band.lo - k0;
+        int e = qrow + band.hi - k0;
+        a = a > 0 ? a : 0;
+        e = e < p.kv_len - 1 - k0 ? e : p.kv_len - 1 - k0;
+        e = e < KC - 1 ? e : KC - 1;
+        if (e < a || !qvalid) a = e = KC;
+        const uint32_t width = (uint32_t)(e - a);
+        const int base = 4 * hh - a;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ok[r] = (uint32_t)(base + 32 * kb + 8 * (r >> 2) + (r & 3)) <= width;
+        if (has_seg) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int4 ks4 = *reinterpret_cast<const int4*>(sseg + 32 * kb + 8 * u + 4 * hh);
+            ok[4 * u + 0] &= ks4.x == myseg;
+            ok[4 * u + 1] &= ks4.y == myseg;
+            ok[4 * u + 2] &= ks4.z == myseg;
+            ok[4 * u + 3] &= ks4.w == myseg;
+          }
+        }
+      }
+      bf16x8 sb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sb[r >> 3][r & 7] = (__bf16)pointwise_weights(sacc[r], pacc[r], scale, nl, ok[r]).ds;
+
+      // ---- dQᵀ += Kᵀ dSᵀ over these 32 keys ----
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int rowbase = (32 * kb + 16 * g2) * T::ROWB;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(kt + rowbase + toff[0][db]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(kt + rowbase + toff[1][db]));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[g2], dq[db], 0, 0, 0);
+        }
+      }
+    }
+    cur_j = nxt_j;
+    cur_t = nxt_t;
+    return cur_j < p.nk;
+  };
+  while (cur_j < p.nk) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
+  }
+
+  if (qvalid) {
+    const float cq = p.scale * p.inv_q_len;
+    OutT* dqr = reinterpret_cast<OutT*>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)qrow * p.dq_ss;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * hh;
+        store4<OutT>(dqr + col, dq[db][4 * g] * cq, dq[db][4 * g + 1] * cq, dq[db][4 * g + 2] * cq,
+                     dq[db][4 * g + 3] * cq);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+
+struct Order {
+  int64_t total, per_xcd;
+  int interleaved;
+};
+// Units: (b, K/V head); a grid of 8 * ceil(work / 8) ids.
+Order order_for(int64_t units, int64_t per_unit) {
+  const int64_t total = units * per_unit;
+  return {total, (total + 7) / 8, units % 8 == 0 ? 1 : 0};
+}
+
+template <int D, int NW, typename OutT>
+hipError_t launch_dkv(const BwdParams& p, hipStream_t stream) {
+  const Order o = order_for((int64_t)p.B * p.kv_heads, p.c_nk);
+  if (o.total == 0) return hipSuccess;
+  hipLaunchKernelGGL((pointwise_dkv_bf16_kernel<D, NW, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
+                     stream, p, (int)o.total, (int)o.per_xcd, o.interleaved);
+  return hipGetLastError();
+}
+
+template <int D, int NW, typename OutT>
+hipError_t launch_dq(const BwdParams& p, hipStream_t stream) {
+  const Order o = order_for((int64_t)p.B * p.kv_heads, (int64_t)p.nq * p.kv_group);
+  if (o.total == 0) return hipSuccess;
+  hipLaunchKernelGGL((pointwise_dq_bf16_kernel<D, NW, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
+                     stream, p, (int)o.total, (int)o.per_xcd, o.interleaved);
+  return hipGetLastError();
+}
+
+template <int D, typename OutT>
+hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
+  hipError_t e = p.c_block_kv == 64 ? launch_dkv<D, 2, OutT>(p, stream) : launch_dkv<D, 4, OutT>(p, stream);
+  if (e != hipSuccess) return e;
+  if (p.block_q == 64) return launch_dq<D, 2, OutT>(p, stream);
+  if (p.block_q == 256) return launch_dq<D, 8, OutT>(p, stream);
+  return launch_dq<D, 4, OutT>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_pointwise_bwd_bf16(const BwdParams& p, bool out_f32, hipStream_t stream) {
+  if (p.head_dim == 64) return out_f32 ? launch_d<64, float>(p, stream) : launch_d<64, __bf16>(p, stream);
+  return out_f32 ? launch_d<128, float>(p, stream) : launch_d<128, __bf16>(p, stream);
+}
+
+}  // namespace splash

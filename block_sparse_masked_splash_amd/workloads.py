@@ -12,7 +12,9 @@ Recipe (shared by every test and by the benchmark):
   * bf16 workloads round those float32 values to bfloat16 with
     round-to-nearest-even (``torch.Tensor.to(torch.bfloat16)``); the oracle
     receives the rounded values upcast exactly to float64.
-  * Packed documents (segment ids): after v, with the same generator, each
+  * Backward workloads: after v, with the same generator, the output
+    gradient d_o as float32 ``standard_normal`` of q's shape (sigma 1).
+  * Packed documents (segment ids): after that, with the same generator, each
     batch row draws integer document lengths uniformly in [lo, hi] until the
     running total reaches S, the last document is cut at S, and documents are
     numbered 0, 1, 2, ... along the row; q and kv share the ids.
@@ -63,6 +65,7 @@ class Workload:
     seed: int
     kv_heads: int = 0       # K/V heads (0: H, plain multi-head attention)
     dense: str = ""         # "" (none) or "tril": the causal pattern as a dense [S, S] array
+    backward: bool = False  # also an output gradient d_o (the pointwise backward's input)
 
     @property
     def n_kv_heads(self) -> int:
@@ -99,6 +102,10 @@ WORKLOADS = {
     "d3h": Workload("d3h", 2, 32, 8192, 128, "bf16", 1.0, (FULL,), 128, 128, False, False, 7, dense="tril"),
     # c5's pointwise attention with its causal pattern as a dense mask array
     "d5": Workload("d5", 8, 8, 4096, 64, "bf16", 0.5, (FULL,), 128, 128, False, True, 8, dense="tril"),
+    # the pointwise backward at c5's shape, output gradient N(0, 1)
+    "b5": Workload("b5", 8, 8, 4096, 64, "bf16", 0.5, (CAUSAL,), 128, 128, False, True, 9, backward=True),
+    # the pointwise backward at D = 128: B=2 H=16 S=4096
+    "b5h": Workload("b5h", 2, 16, 4096, 128, "bf16", 0.5, (CAUSAL,), 128, 128, False, True, 10, backward=True),
 }
 
 
@@ -151,9 +158,10 @@ def generate(w: Workload, *, B: int | None = None, H: int | None = None,
              S: int | None = None, seed: int | None = None) -> dict:
     """CPU torch tensors for workload ``w`` (sizes overridable for small cases).
 
-    Returns dict(q, k, v, q_segment_ids, kv_segment_ids, dense) where the
-    segment ids are int32 torch tensors [B, S] or None and ``dense`` is the
-    boolean [S, S] mask or None.
+    Returns dict(q, k, v, q_segment_ids, kv_segment_ids, dense, d_o) where the
+    segment ids are int32 torch tensors [B, S] or None, ``dense`` is the
+    boolean [S, S] mask or None and ``d_o`` the output gradient (backward
+    workloads) or None.
     """
     B = w.B if B is None else B
     Hk = w.n_kv_heads if H is None else max(1, H // (w.H // w.n_kv_heads))
@@ -162,7 +170,9 @@ def generate(w: Workload, *, B: int | None = None, H: int | None = None,
     rng = np.random.default_rng(w.seed if seed is None else seed)
     q, k, v = draw_qkv_f32(rng, B, H, S, S, w.D, w.sigma, Hk)
     out = dict(q=_store(q, w.dtype), k=_store(k, w.dtype), v=_store(v, w.dtype),
-               q_segment_ids=None, kv_segment_ids=None, dense=dense_mask(w, S))
+               q_segment_ids=None, kv_segment_ids=None, dense=dense_mask(w, S), d_o=None)
+    if w.backward:
+        out["d_o"] = _store(rng.standard_normal(q.shape, dtype=np.float32), w.dtype)
     del q, k, v
     if w.segments:
         import torch

@@ -246,6 +246,55 @@ splash_status splash_masked_fwd(int pointwise, splash_dtype in_dtype, splash_dty
                                 const splash_mask_info* info, const splash_partial_masks* partial,
                                 hipStream_t stream);
 
+/* ---- Pointwise backward ----
+ *
+ * "hstu_ops.py" (RecML), _pointwise_splash_attention_bwd_kernel_impl and
+ * _pointwise_splash_attention_bwd_kernel: the gradients of
+ * splash_pointwise_fwd. With x = scale q·k, sig = logistic(x) (0 where the
+ * mask forbids the pair) and dO the gradient of the output:
+ *   p  = x sig / q_len,                     dV_k = sum_q p dO_q
+ *   ds = (dO_q·v_k) sig (1 + x (1 - sig)) / q_len
+ *   dK_k = scale sum_q ds q_q,              dQ_q = scale sum_k ds k_k
+ * dQ is computed over the row walk (metadata of splash_mask_info_build), dK
+ * and dV over the column walk that the page's dK/dV grid uses (metadata of
+ * splash_mask_info_build_dkv, possibly with other block sizes). */
+
+/* Metadata of the dK/dV pass: block_mask exactly as splash_mask_info_build
+ * gives it for the same arguments, and data_next[.., i, j] = the first q
+ * block i' >= i of kv-block column j whose class is not 0, else nq
+ * (_next_nonzero with next_i=True reads data_next[h, i, j] as the q block to
+ * fetch). Same arguments, checks, shapes and errors as
+ * splash_mask_info_build; enqueued on `stream`. */
+splash_status splash_mask_info_build_dkv(int B, int H, int q_len, int kv_len, int block_q, int block_kv,
+                                         const splash_mask_desc* mask, const splash_mask_info* info,
+                                         hipStream_t stream);
+
+/* dq [B, H, q_len, D], dk and dv [B, kv_heads, kv_len, D] from q, k, v and
+ * d_o ([B, H, q_len, D], the output gradient), for the mask `mask`.
+ * Strides, dtypes (f32 -> f32, bf16 -> bf16, bf16 -> f32: the gradients take
+ * out_dtype), head_dim (64, 128) and kv_heads (a divisor of H; query head h
+ * reads K/V head h / (H / kv_heads), and a K/V head's gradients sum over its
+ * query heads) are as for splash_gqa_pointwise_fwd. `info` (row walk) must
+ * come from splash_mask_info_build with block_q in {64, 128, 256} and
+ * block_kv in {64, 128}; `info_dkv` (column walk) from
+ * splash_mask_info_build_dkv with block_q a multiple of 32 in [32, 1024] and
+ * block_kv in {64, 128}. Both for this call's shapes, mask heads and
+ * segment ids (METADATA_MISMATCH otherwise). dq, dk and dv are fully
+ * overwritten (0 for rows no pair reaches); inputs are read only; the output
+ * buffers must not overlap the inputs or each other. Enqueued on `stream`. */
+splash_status splash_pointwise_bwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
+                                   int q_len, int kv_len, int head_dim,
+                                   const void* q, const int64_t q_strides[3],
+                                   const void* k, const int64_t k_strides[3],
+                                   const void* v, const int64_t v_strides[3],
+                                   const void* d_o, const int64_t do_strides[3],
+                                   void* dq, const int64_t dq_strides[3],
+                                   void* dk, const int64_t dk_strides[3],
+                                   void* dv, const int64_t dv_strides[3],
+                                   float scale, const splash_mask_desc* mask,
+                                   const splash_mask_info* info, const splash_mask_info* info_dkv,
+                                   hipStream_t stream);
+
 /* Static name of a status code. */
 const char* splash_status_string(splash_status s);
 /* Detail of the last failure on the calling thread ("" if none). */

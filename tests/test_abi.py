@@ -167,3 +167,51 @@ def test_binding_refuses_missing_library(tmp_path):
             bd.load_library(str(tmp_path / "libsplash.so"))
     finally:
         bd._lib = saved
+
+
+def test_pointwise_bwd_validation_errors():
+    """Host-side checks of the backward: every call here fails before any
+    launch (fake device addresses are never touched)."""
+    lib = bd.load_library()
+    d, keep = _desc()
+    row = _info(bq=64, bkv=64)
+    col = _info(bq=64, bkv=64)
+
+    def call(in_dt=1, out_dt=1, H=4, kv_heads=2, D=128, info=row, info_dkv=col, desc=d, scale=0.1, align=0):
+        st = [bd._I64x3(H * 256 * D, 256 * D, D) for _ in range(7)]
+        ptrs = [0x100000 * (n + 1) + align for n in range(7)]
+        args = []
+        for p, s in zip(ptrs, st):
+            args += [p, s]
+        return lib.splash_pointwise_bwd(in_dt, out_dt, 1, H, kv_heads, 256, 256, D, *args, scale,
+                                        ctypes.byref(desc) if desc else None,
+                                        ctypes.byref(info) if info else None,
+                                        ctypes.byref(info_dkv) if info_dkv else None, None)
+
+    assert call(kv_heads=3) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(D=96) == bd.SPLASH_ERR_UNSUPPORTED
+    assert call(in_dt=0, out_dt=1) == bd.SPLASH_ERR_UNSUPPORTED
+    assert call(scale=float("nan")) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(info=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(info_dkv=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert b"info_dkv" in lib.splash_last_error()
+    assert call(desc=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert call(info=_info(nq=3)) == bd.SPLASH_ERR_METADATA_MISMATCH
+    assert call(info_dkv=_info(nk=3)) == bd.SPLASH_ERR_METADATA_MISMATCH
+    # block sizes without a compiled kernel
+    assert call(info=_info(nq=8, bq=32)) == bd.SPLASH_ERR_UNSUPPORTED
+    assert call(info_dkv=_info(nq=16, nk=16, bq=16, bkv=16)) == bd.SPLASH_ERR_UNSUPPORTED
+    assert call(info_dkv=_info(nk=8, bkv=32)) == bd.SPLASH_ERR_UNSUPPORTED
+    assert call(align=8) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert b"aligned" in lib.splash_last_error()
+
+
+def test_mask_info_build_dkv_validation_errors():
+    lib = bd.load_library()
+    d, keep = _desc()
+    assert lib.splash_mask_info_build_dkv(1, 1, 256, 256, 64, 64, ctypes.byref(d), None, None) == \
+        bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert lib.splash_mask_info_build_dkv(1, 1, 256, 256, 64, 64, ctypes.byref(d), ctypes.byref(_info(nq=3)),
+                                          None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert lib.splash_mask_info_build_dkv(1, 1, 0, 256, 64, 64, ctypes.byref(d), ctypes.byref(_info(nq=0)),
+                                          None) == bd.SPLASH_OK
