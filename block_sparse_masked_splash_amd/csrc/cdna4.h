@@ -161,17 +161,24 @@ __device__ inline void store4<float>(float* dst, float a, float b, float c, floa
   *reinterpret_cast<f32x4*>(dst) = v;
 }
 
-// LDS chunk position of logical 16-byte chunk c of key row r. The mask mixes
-// row bits so that the 8 keys x 4 chunks touched by one transposing V read
-// land on distinct banks (64 banks of 4 bytes; a 128-dim row spans all of
-// them, a 64-dim row half of them); the K operand reads are conflict-free
-// under any such row-dependent XOR.
+// LDS chunk position of logical 16-byte chunk c of tile row r (64 banks of
+// 4 bytes). Two access patterns must be free of bank conflicts:
+//   * row operand reads (ds_read_b128, 16 lanes per pass): rows r .. r + 15
+//     at one logical chunk must land on 16 distinct 4-bank groups;
+//   * transposing reads (ds_read_b64_tr_b16, 32 lanes per pass): rows
+//     4m .. 4m + 3, each at the 4 chunks of one 64-byte head-dim span, must
+//     cover all 64 banks.
+// A 128-dim row spans all 64 banks: XOR with r & 15 (bits swapped in pairs)
+// gives 16 distinct positions per 16 rows and keeps a 4-chunk span whole. A
+// 64-dim row spans half of them (rows of one parity share a half): the XOR
+// takes row bits 1-3, bit 1 onto chunk bit 2 so that rows 4m and 4m + 2 use
+// opposite 4-chunk halves, bits 2-3 onto chunk bits 0-1.
 template <int D>
 __device__ constexpr int swz(int c, int r) {
   if constexpr (D == 128) {
     return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
   } else {
-    return c ^ (((r >> 1) & 1) << 2);
+    return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
   }
 }
 

@@ -6,9 +6,10 @@
 //   dp = dO_q · v_k
 //   ds = dp sig (1 + x (1 - sig)) / q_len   dK_k += scale sum_q ds q_q
 //                                           dQ_q += scale sum_k ds k_k
-// Here the weights are kept without the constant factors (p' = x sig,
-// ds' = dp (sig + p' (1 - sig)), the same as dp sig (1 + x (1 - sig))); the
-// factors 1 / q_len and scale / q_len are applied once to the sums.
+// Here the weights are kept without the constant factors (p' = t sig with
+// t = -scale log2(e) q·k, ds' = dp (sig + x sig (1 - sig)), the same as
+// dp sig (1 + x (1 - sig))); the factors -ln 2 / q_len (dV) and scale / q_len
+// (dK, dQ) are applied once to each sum.
 //
 // Two kernels, each with its own walk over the non-empty blocks, neither
 // needing any cross-workgroup reduction:
@@ -36,16 +37,23 @@
 namespace splash {
 namespace {
 
-// sig, p' = x sig and ds' = dp (sig + p' (1 - sig)) of one score; masked
-// pairs get sig = 0, hence p' = ds' = 0. nl = -scale log2(e).
+// Weights of one score from t = nl q·k (nl = -scale log2(e), so that
+// 2^t = e^-x with x = scale q·k = -t ln 2): sig = 1 / (1 + 2^t),
+// p = t sig (= -x sig / ln 2: the factor -ln 2 goes into dV's final factor)
+// and ds' = dp (sig + x sig (1 - sig)) = dp (sig + p (sig - 1) ln 2), that
+// last factor formed with two fmas. A masked score is given t = kMaskedT:
+// 2^t overflows, sig = 0 and p = ds' = 0 through the same arithmetic (any
+// t > 128 does the same, so large real exponents are safe too).
 struct Weights {
   float p, ds;
 };
-__device__ inline Weights pointwise_weights(float acc, float dp, float scale, float nl, bool ok) {
-  const float x = acc * scale;
-  const float sg = ok ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(acc * nl)) : 0.0f;
-  const float pv = x * sg;
-  return {pv, dp * __builtin_fmaf(pv, 1.0f - sg, sg)};
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kMaskedT = 256.0f;
+__device__ inline Weights pointwise_weights(float t, float dp) {
+  const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+  const float pt = t * sg;
+  const float w = __builtin_fmaf(sg, kLn2, -kLn2);  // (sig - 1) ln 2
+  return {pt, dp * __builtin_fmaf(pt, w, sg)};
 }
 
 // XCD-aware work order shared by both passes: workgroup ids are dealt
@@ -87,12 +95,12 @@ struct DkvTiling {
   static_assert(LOADS >= 1, "tile too small for the workgroup");
 };
 
-// D = 64: about 160 VGPRs, three wavefronts per SIMD. D = 128: K, V and the
+// D = 64: about 170 VGPRs, two wavefronts per SIMD. D = 128: K, V and the
 // two accumulators alone take 192 VGPRs, and the whole step about 270, more
 // than two wavefronts per SIMD can hold without spilling: one.
 template <int D>
 constexpr int dkv_waves() {
-  return D == 64 ? 3 : 1;
+  return D == 64 ? 2 : 1;
 }
 
 template <int D, int NW, typename OutT>
@@ -214,7 +222,6 @@ void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, in
       dk[db][r] = 0.0f;
       dv[db][r] = 0.0f;
     }
-  const float scale = p.scale;
   const float nl = -p.scale * 1.4426950408889634f;
 
   int cur_g = 0, cur_i = first_i(0), cur_t = 0;
@@ -261,10 +268,11 @@ void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, in
 
     // element r: query q0 + 8 (r / 4) + 4 hh + r % 4, key `key`. On a partial
     // block the band, the sequence ends and (with ids) segment equality leave
-    // the lane's key one run of queries [a, e] of the tile plus the id test.
-    bool ok[16];
+    // the lane's key one run of queries [a, e] of the tile plus the id test;
+    // full blocks take a path with no per-score test at all.
+    f32x16& t = sacc;  // t = nl q·k, in place
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ok[r] = true;
+    for (int r = 0; r < 16; ++r) t[r] = sacc[r] * nl;
     if (partial) {
       int a = key - band.hi - q0;
       int e = key - band.lo - q0;
@@ -274,23 +282,27 @@ void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, in
       if (e < a || !kvalid) a = e = QC;  // no query of the tile
       const uint32_t width = (uint32_t)(e - a);
       const int base = 4 * hh - a;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ok[r] = (uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width;
       if (has_seg) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int4 qs4 = *reinterpret_cast<const int4*>(sseg + 8 * u + 4 * hh);
-          ok[4 * u + 0] &= qs4.x == kseg;
-          ok[4 * u + 1] &= qs4.y == kseg;
-          ok[4 * u + 2] &= qs4.z == kseg;
-          ok[4 * u + 3] &= qs4.w == kseg;
+          const int ids[4] = {qs4.x, qs4.y, qs4.z, qs4.w};
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int r = 4 * u + v4;
+            const bool ok = ((uint32_t)(base + 8 * u + v4) <= width) & (ids[v4] == kseg);
+            t[r] = ok ? t[r] : kMaskedT;
+          }
         }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = ((uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width) ? t[r] : kMaskedT;
       }
     }
     bf16x8 pb[2], sb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const Weights w = pointwise_weights(sacc[r], pacc[r], scale, nl, ok[r]);
+      const Weights w = pointwise_weights(t[r], pacc[r]);
       pb[r >> 3][r & 7] = (__bf16)w.p;
       sb[r >> 3][r & 7] = (__bf16)w.ds;
     }
@@ -325,9 +337,9 @@ void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, in
     if (!step(std::integral_constant<int, 1>{})) break;
   }
 
-  // ---- dK = (scale / q_len) dK', dV = dV' / q_len; lane's key row ----
+  // ---- dK = (scale / q_len) dK', dV = (-ln 2 / q_len) dV'; lane's key row ----
   if (kvalid) {
-    const float ck = p.scale * p.inv_q_len, cv = p.inv_q_len;
+    const float ck = p.scale * p.inv_q_len, cv = -kLn2 * p.inv_q_len;
     OutT* dkr = reinterpret_cast<OutT*>(p.dk) + b * p.dk_sb + hk * p.dk_sh + (int64_t)key * p.dk_ss;
     OutT* dvr = reinterpret_cast<OutT*>(p.dv) + b * p.dv_sb + hk * p.dv_sh + (int64_t)key * p.dv_ss;
 #pragma unroll
@@ -460,7 +472,6 @@ void pointwise_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
-  const float scale = p.scale;
   const float nl = -p.scale * 1.4426950408889634f;
 
   auto next_block = [&](int jj) {
@@ -508,9 +519,9 @@ void pointwise_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, oreg[s], pacc, 0, 0, 0);
       }
       // element r: key k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4, query qrow
-      bool ok[16];
+      f32x16& t = sacc;  // t = nl q·k, in place
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ok[r] = true;
+      for (int r = 0; r < 16; ++r) t[r] = sacc[r] * nl;
       if (partial) {
         int a = qrow + band.lo - k0;
         int e = qrow + band.hi - k0;
@@ -519,23 +530,27 @@ void pointwise_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
         e = e < KC - 1 ? e : KC - 1;
         if (e < a || !qvalid) a = e = KC;
         const uint32_t width = (uint32_t)(e - a);
-        const int base = 4 * hh - a;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ok[r] = (uint32_t)(base + 32 * kb + 8 * (r >> 2) + (r & 3)) <= width;
+        const int base = 4 * hh - a + 32 * kb;
         if (has_seg) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int4 ks4 = *reinterpret_cast<const int4*>(sseg + 32 * kb + 8 * u + 4 * hh);
-            ok[4 * u + 0] &= ks4.x == myseg;
-            ok[4 * u + 1] &= ks4.y == myseg;
-            ok[4 * u + 2] &= ks4.z == myseg;
-            ok[4 * u + 3] &= ks4.w == myseg;
+            const int ids[4] = {ks4.x, ks4.y, ks4.z, ks4.w};
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+              const int r = 4 * u + v4;
+              const bool ok = ((uint32_t)(base + 8 * u + v4) <= width) & (ids[v4] == myseg);
+              t[r] = ok ? t[r] : kMaskedT;
+            }
           }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) t[r] = ((uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width) ? t[r] : kMaskedT;
         }
       }
       bf16x8 sb[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sb[r >> 3][r & 7] = (__bf16)pointwise_weights(sacc[r], pacc[r], scale, nl, ok[r]).ds;
+      for (int r = 0; r < 16; ++r) sb[r >> 3][r & 7] = (__bf16)pointwise_weights(t[r], pacc[r]).ds;
 
       // ---- dQᵀ += Kᵀ dSᵀ over these 32 keys ----
 #pragma unroll
