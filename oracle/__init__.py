@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for block-sparse masked attention (forward, pointwise backward).
+"""fp64 CPU oracle for block-sparse masked attention (forwards, log-sum-exp, backwards).
 
 TEST INFRASTRUCTURE ONLY. This package is the independent, slow, plainly
 written reference that the GPU path is checked against. Only the test suite,
@@ -32,4 +32,8 @@ from .splash_oracle import (  # noqa: F401
     partial_blocks,
     pointwise_attention_bwd,
     pointwise_attention_bwd_rows,
+    softmax_lse,
+    softmax_lse_rows,
+    softmax_attention_bwd,
+    softmax_attention_bwd_rows,
 )

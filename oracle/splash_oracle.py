@@ -31,6 +31,12 @@ blocking, fusion or reordering beyond what a definition states:
   dq += scale ds^T k) and ``_pointwise_splash_attention_bwd_kernel`` (grid over
   kv blocks, then heads, then q blocks; the q block fetched at step i is
   ``data_next[h, i, j]`` of the dK/dV metadata, ``_next_nonzero(next_i=True)``).
+* Softmax log-sum-exp and backward: page 3, section 15 (per row, the running
+  max m and sum L give log sum e^a = m + log L) and section 12's definition of
+  softmax attention, differentiated; "hstu_ops.py" (``custom_vjp``: the
+  forward hands the backward its residuals). The pages give no softmax
+  backward kernel: the reading taken is the gradient of the definition, with
+  the forward's log-sum-exp as the residual.
 * Pointwise attention: "hstu_ops.py", ``_pointwise_splash_attention_fwd_kernel_impl``
   (scores times scale, times logistic(scores), divided by the query sequence
   length, masked entries set to 0, then times V), with the contributions of
@@ -494,6 +500,113 @@ def pointwise_attention_bwd(q, k, v, do, scale: float, heads, q_seg=None, kv_seg
                 m = element_mask(Sq, Skv, hd, qs, ks, rows=rows)
                 a, bk, bv = pointwise_attention_bwd_rows(q[b, h, rows], k[b, hk], v[b, hk], do[b, h, rows],
                                                          scale, m, Sq)
+                dq[b, h, rows] = a
+                dk[b, hk] += bk
+                dv[b, hk] += bv
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# softmax log-sum-exp and backward
+# ---------------------------------------------------------------------------
+
+
+def softmax_lse_rows(q_rows, k, scale: float, mask_rows) -> np.ndarray:
+    """log sum_k e^{a_k} over the allowed keys of each row, a = scale q.k
+    (page 3, section 15: with M the row max, log sum e^a = M + log sum
+    e^{a - M}); -inf for a row with no allowed key (nothing to sum)."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    a = (q_rows @ k.T) * float(scale)
+    mask_rows = np.asarray(mask_rows)
+    out = np.full(q_rows.shape[0], -np.inf)
+    has = mask_rows.any(axis=1)
+    if has.any():
+        ah = np.where(mask_rows[has], a[has], -np.inf)
+        m = ah.max(axis=1)
+        out[has] = m + np.log(np.exp(ah - m[:, None]).sum(axis=1))
+    return out
+
+
+def softmax_attention_bwd_rows(q_rows, k, v, do_rows, scale: float, mask_rows):
+    """Contributions of some query rows to the softmax attention gradients:
+    (dq_rows, dk, dv), the derivative of ``softmax_attention_rows``.
+
+    With P the row softmax of the allowed scores a = scale q.k (0 elsewhere,
+    and 0 for a row with no allowed key), O = P v:
+      dv = P^T do;  dP = do v^T;  delta = rowsum(do * O);
+      dS = P (dP - delta);  dq = scale dS k;  dk = scale dS^T q.
+    (d softmax: dS_j = P_j (dP_j - sum_l P_l dP_l), and sum_l P_l dP_l =
+    do . O.)
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do_rows = np.asarray(do_rows, dtype=np.float64)
+    mask_rows = np.asarray(mask_rows)
+    a = (q_rows @ k.T) * float(scale)
+    P = np.zeros_like(a)
+    has = mask_rows.any(axis=1)
+    if has.any():
+        ah = np.where(mask_rows[has], a[has], -np.inf)
+        e = np.exp(ah - ah.max(axis=1, keepdims=True))
+        P[has] = e / e.sum(axis=1, keepdims=True)
+    O = P @ v
+    dv = P.T @ do_rows
+    dP = do_rows @ v.T
+    delta = (do_rows * O).sum(axis=1, keepdims=True)
+    dS = P * (dP - delta)
+    dq = float(scale) * (dS @ k)
+    dk = float(scale) * (dS.T @ q_rows)
+    return dq, dk, dv
+
+
+def softmax_lse(q, k, scale: float, heads, q_seg=None, kv_seg=None) -> np.ndarray:
+    """Log-sum-exp [B, H, Sq] of every row (``softmax_lse_rows``); k may have
+    fewer heads than q (``kv_head_of``)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, Sq, _ = q.shape
+    Skv = k.shape[2]
+    heads = _heads_list(heads, H)
+    out = np.zeros((B, H, Sq))
+    for b in range(B):
+        qs = None if q_seg is None else np.asarray(q_seg)[b]
+        ks = None if kv_seg is None else np.asarray(kv_seg)[b]
+        for h in range(H):
+            hd = heads[0] if len(heads) == 1 else heads[h]
+            m = element_mask(Sq, Skv, hd, qs, ks)
+            out[b, h] = softmax_lse_rows(q[b, h], k[b, kv_head_of(h, H, k.shape[1])], scale, m)
+    return out
+
+
+def softmax_attention_bwd(q, k, v, do, scale: float, heads, q_seg=None, kv_seg=None,
+                          row_chunk: int = 512):
+    """Gradients (dq [B, H, Sq, D], dk, dv [B, Hk, Skv, D]) of
+    ``softmax_attention`` for the output gradient ``do``, fp64; rows are
+    taken ``row_chunk`` at a time and their dk, dv contributions summed, and
+    a K/V head's gradients sum over the query heads that read it."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, Sq, _ = q.shape
+    Skv = k.shape[2]
+    kv_heads = k.shape[1]
+    heads = _heads_list(heads, H)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        qs = None if q_seg is None else np.asarray(q_seg)[b]
+        ks = None if kv_seg is None else np.asarray(kv_seg)[b]
+        for h in range(H):
+            hd = heads[0] if len(heads) == 1 else heads[h]
+            hk = kv_head_of(h, H, kv_heads)
+            for r0 in range(0, Sq, row_chunk):
+                rows = np.arange(r0, min(Sq, r0 + row_chunk))
+                m = element_mask(Sq, Skv, hd, qs, ks, rows=rows)
+                a, bk, bv = softmax_attention_bwd_rows(q[b, h, rows], k[b, hk], v[b, hk], do[b, h, rows], scale, m)
                 dq[b, h, rows] = a
                 dk[b, hk] += bk
                 dv[b, hk] += bv

@@ -713,3 +713,118 @@ def test_dkv_metadata_closed_forms_and_brute_force():
                     for i in range(nq):
                         later = [ii for ii in range(i, nq) if bm[bb, h, ii, j] != 0]
                         assert dn[bb, h, i, j] == (later[0] if later else nq)
+
+
+# ---------------------------------------------------------------------------
+# softmax log-sum-exp and backward
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("head", [FULL, CAUSAL, (1, 9, 9), (0, 5, 3)])
+def test_softmax_lse_matches_torch_logsumexp(head):
+    """torch.logsumexp (a library routine) over the allowed scores; rows with
+    no allowed key give -inf."""
+    B, H, S, D = 2, 2, 70, 16
+    q, k, v, qs, ks = _case(81, B, H, S, S, D, segments="docs")
+    got = oracle.softmax_lse(q, k, 0.3, [head], qs, ks)
+    for b in range(B):
+        m = torch.from_numpy(oracle.element_mask(S, S, head, qs[b], ks[b]))
+        for h in range(H):
+            a = 0.3 * torch.from_numpy(q[b, h]) @ torch.from_numpy(k[b, h]).T
+            want = torch.logsumexp(a.masked_fill(~m, float("-inf")), dim=1).numpy()
+            np.testing.assert_allclose(got[b, h], want, rtol=1e-13, atol=1e-13)
+    # identical keys: log(n e^x) = x + log n, n = allowed keys of the row
+    kk = np.tile(k[0, 0, 3], (S, 1))
+    lse = oracle.softmax_lse_rows(q[0, 0], kk, 0.3, oracle.element_mask(S, S, CAUSAL))
+    for t in range(S):
+        x = 0.3 * float(np.dot(q[0, 0, t], k[0, 0, 3]))
+        assert abs(lse[t] - (x + math.log(t + 1))) < 1e-12
+    # no allowed key
+    none = oracle.softmax_lse_rows(q[0, 0, :2], k[0, 0], 1.0, np.zeros((2, S), bool))
+    assert (none == -np.inf).all()
+
+
+@pytest.mark.parametrize("head", [FULL, CAUSAL, (1, 9, 9), (0, 5, 3)])
+def test_softmax_bwd_matches_torch_sdpa_autograd(head):
+    """Autograd through torch's scaled_dot_product_attention in float64 (a
+    library definition and derivative) with a boolean mask."""
+    B, H, S, D = 2, 2, 61, 16
+    q, k, v, qs, ks = _case(83, B, H, S, S, D, segments="docs")
+    do = np.random.default_rng(84).standard_normal(q.shape)
+    scale = 1 / math.sqrt(D)
+    dq, dk, dv = oracle.softmax_attention_bwd(q, k, v, do, scale, [head], qs, ks, row_chunk=25)
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    total = 0
+    for b in range(B):
+        m = torch.from_numpy(oracle.element_mask(S, S, head, qs[b], ks[b]))
+        assert m.any(dim=1).all()
+        o = torch.nn.functional.scaled_dot_product_attention(tq[b], tk[b], tv[b], attn_mask=m, scale=scale)
+        total = total + (o * torch.from_numpy(do[b])).sum()
+    total.backward()
+    for got, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("kv_heads", [2, 1])
+def test_softmax_bwd_matches_finite_differences(kv_heads):
+    """Central differences of sum(do * softmax_attention) (the forward is
+    pinned above), with head masks, segment ids and a shared K/V head."""
+    H, Sq, Skv, D = 2, 7, 9, 3
+    q, k, v, do, qs, ks = _small_bwd_case(85 + kv_heads, H, kv_heads, Sq, Skv, D)
+    heads = [CAUSAL, (0, 2, 3)]
+    qs[:] = 0
+    ks[:] = 0
+    ks[0, ::3] = 1   # some keys in another document
+    dq, dk, dv = oracle.softmax_attention_bwd(q, k, v, do, 0.7, heads, qs, ks, row_chunk=3)
+
+    def loss(qq, kk, vv):
+        return float((oracle.softmax_attention(qq, kk, vv, 0.7, heads, qs, ks) * do).sum())
+
+    for which, got in enumerate((dq, dk, dv)):
+        args = [q.copy(), k.copy(), v.copy()]
+        g = np.zeros_like(args[which])
+        for idx in np.ndindex(g.shape):
+            x0 = args[which][idx]
+            args[which][idx] = x0 + 1e-5
+            up = loss(*args)
+            args[which][idx] = x0 - 1e-5
+            dn = loss(*args)
+            args[which][idx] = x0
+            g[idx] = (up - dn) / 2e-5
+        assert np.abs(g).max() > 1e-3
+        np.testing.assert_allclose(got, g, rtol=0, atol=1e-8)
+
+
+def test_softmax_bwd_closed_forms_and_mutants(monkeypatch):
+    """v constant: every row's output is that constant whatever the scores,
+    so dq = dk = 0 and dv = P^T do (P from the forward with v = identity).
+    Mutants (delta dropped, scale lost) fail the closed forms or torch."""
+    import inspect
+    import oracle.splash_oracle as so
+
+    S, D = 40, 8
+    q, k, v, _, _ = _case(87, 1, 1, S, S, D)
+    do = np.random.default_rng(88).standard_normal((S, D))
+    mask = oracle.element_mask(S, S, CAUSAL)
+    c = np.linspace(-1, 1, D)
+    dq, dk, dv = oracle.softmax_attention_bwd_rows(q[0, 0], k[0, 0], np.tile(c, (S, 1)), do, 0.4, mask)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+    P = oracle.softmax_attention_rows(q[0, 0], k[0, 0], np.eye(S), 0.4, mask)
+    np.testing.assert_allclose(dv, P.T @ do, rtol=1e-12, atol=1e-14)
+    # a row with no allowed key contributes nothing
+    none = np.zeros((2, S), bool)
+    for g in oracle.softmax_attention_bwd_rows(q[0, 0, :2], k[0, 0], v[0, 0], do[:2], 0.4, none):
+        assert (g == 0).all()
+
+    src = inspect.getsource(so.softmax_attention_bwd_rows)
+    ref = oracle.softmax_attention_bwd_rows(q[0, 0], k[0, 0], v[0, 0], do, 0.4, mask)
+    for old, new in [("dS = P * (dP - delta)", "dS = P * dP"),
+                     ("dq = float(scale) * (dS @ k)", "dq = dS @ k"),
+                     ("dv = P.T @ do_rows", "dv = P @ do_rows")]:
+        assert old in src
+        ns = dict(so.__dict__)
+        exec(src.replace(old, new), ns)
+        got = ns["softmax_attention_bwd_rows"](q[0, 0], k[0, 0], v[0, 0], do, 0.4, mask)
+        err = max(np.abs(a - b).max() for a, b in zip(got, ref))
+        # the real function is pinned to torch above; a mutant moves away from it
+        assert err > 1e-3, old
