@@ -28,7 +28,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CU x 4096 FLOP/
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak
 METRIC = "splash fwd TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, causal S=8192"
 KERNEL_SOURCES = ["splash_fwd_bf16.hip", "splash_fwd_f32.hip", "splash_bwd_bf16.hip", "splash_bwd_f32.hip",
-                  "cdna4.h", "internal.h"]
+                  "softmax_delta.hip", "cdna4.h", "internal.h"]
 
 
 def kernel_source_hash() -> str:
@@ -88,7 +88,10 @@ def cpu_baseline(w, gen, budget_s: float = 12.0):
         q64 = gen["q"][b, h, rows[0]:rows[-1] + 1].to(torch.float64).numpy()
         if w.backward:
             do64 = gen["d_o"][b, h, rows[0]:rows[-1] + 1].to(torch.float64).numpy()
-            oracle.pointwise_attention_bwd_rows(q64, k64, v64, do64, w.scale, m, S)
+            if w.pointwise:
+                oracle.pointwise_attention_bwd_rows(q64, k64, v64, do64, w.scale, m, S)
+            else:
+                oracle.softmax_attention_bwd_rows(q64, k64, v64, do64, w.scale, m)
         elif w.pointwise:
             oracle.pointwise_attention_rows(q64, k64, v64, w.scale, m, S)
         else:
@@ -173,6 +176,10 @@ def main():
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
         info_dkv = sp.mask_info_build_dkv(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, seg, seg,
                                           device=dev)
+        if not w.pointwise:
+            # the forward's output and log-sum-exp are the backward's inputs (made before timing)
+            o_fwd, lse = sp.splash_fwd_lse(q, k, v, info, scale=w.scale)
+            delta = torch.empty_like(lse)
 
     def build_metadata():
         if dense is None:
@@ -183,7 +190,10 @@ def main():
                                    out=info_dkv)
 
     def run_kernels():
-        if w.backward:
+        if w.backward and not w.pointwise:
+            sp.softmax_bwd_preprocess(o_fwd, d_o, delta=delta)
+            sp.softmax_bwd(q, k, v, d_o, lse, delta, info, info_dkv, scale=w.scale, out=grads)
+        elif w.backward:
             sp.pointwise_bwd(q, k, v, d_o, info, info_dkv, scale=w.scale, out=grads)
         else:
             fwd(q, k, v, info, scale=w.scale, out=out)
@@ -237,8 +247,11 @@ def main():
               "N(0,1) output gradient, blocks 128x128 for both walks",
         "b5h": "pointwise SiLU backward (dq, dk, dv) B=2 H=16 S=4096 D=128 bf16 causal, N(0,0.5^2) inputs, "
                "N(0,1) output gradient, blocks 128x128 for both walks",
+        "s3h": "softmax backward (delta, dq, dk, dv) B=2 H=32 S=8192 D=128 bf16 causal, N(0,1) inputs and "
+               "output gradient, blocks 128x128 for both walks",
     }[w.name]
-    fwd_name = "pointwise_bwd" if w.backward else ("pointwise_fwd" if w.pointwise else "splash_fwd")
+    fwd_name = (("pointwise_bwd" if w.pointwise else "softmax_bwd_preprocess + softmax_bwd") if w.backward
+                else ("pointwise_fwd" if w.pointwise else "splash_fwd"))
     line = {
         "metric": METRIC,
         "value": round(value, 3),

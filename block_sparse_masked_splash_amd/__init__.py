@@ -14,6 +14,9 @@ from .binding import (  # noqa: F401
     mask_info_build_dkv,
     pointwise_bwd,
     pointwise_fwd,
+    softmax_bwd,
+    softmax_bwd_preprocess,
     splash_fwd,
+    splash_fwd_lse,
 )
 from .workloads import CAUSAL, FULL, local_causal  # noqa: F401

@@ -38,6 +38,9 @@ SYMBOLS = (
     "splash_masked_fwd",
     "splash_mask_info_build_dkv",
     "splash_pointwise_bwd",
+    "splash_fwd_lse",
+    "splash_softmax_bwd_preprocess",
+    "splash_softmax_bwd",
     "splash_status_string",
     "splash_last_error",
     "splash_abi_version",
@@ -87,6 +90,13 @@ _T = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]
 _BWD_ARGS = ([ctypes.c_int] * 8 + _T * 7
              + [ctypes.c_float, ctypes.POINTER(MaskDescC), ctypes.POINTER(MaskInfoC), ctypes.POINTER(MaskInfoC),
                 ctypes.c_void_p])
+_I64p = ctypes.POINTER(ctypes.c_int64)
+_SM_BWD_ARGS = ([ctypes.c_int] * 8 + _T * 4 + [ctypes.c_void_p, ctypes.c_void_p, _I64p] + _T * 3
+                + [ctypes.c_float, ctypes.POINTER(MaskDescC), ctypes.POINTER(MaskInfoC), ctypes.POINTER(MaskInfoC),
+                   ctypes.c_void_p])
+_LSE_ARGS = ([ctypes.c_int] * 8 + _T * 4 + [ctypes.c_void_p, _I64p]
+             + [ctypes.c_float, ctypes.POINTER(MaskDescC), ctypes.POINTER(MaskInfoC), ctypes.c_void_p])
+_I64x2 = ctypes.c_int64 * 2
 
 _lib = None
 
@@ -109,6 +119,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(MaskDescC), ctypes.POINTER(MaskInfoC), ctypes.c_void_p]
     lib.splash_pointwise_bwd.restype = ctypes.c_int
     lib.splash_pointwise_bwd.argtypes = _BWD_ARGS
+    lib.splash_softmax_bwd.restype = ctypes.c_int
+    lib.splash_softmax_bwd.argtypes = _SM_BWD_ARGS
+    lib.splash_fwd_lse.restype = ctypes.c_int
+    lib.splash_fwd_lse.argtypes = _LSE_ARGS
+    lib.splash_softmax_bwd_preprocess.restype = ctypes.c_int
+    lib.splash_softmax_bwd_preprocess.argtypes = [ctypes.c_int] * 5 + _T * 2 + [ctypes.c_void_p, _I64p,
+                                                                                ctypes.c_void_p]
     for name in ("splash_fwd", "splash_pointwise_fwd"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -392,13 +409,15 @@ def pointwise_fwd(q, k, v, info: MaskInfo, scale: float | None = None, out=None,
 # ---------------------------------------------------------------------------
 
 
-def pointwise_bwd(q, k, v, d_o, info: MaskInfo, info_dkv: MaskInfo, scale: float | None = None,
-                  out_dtype=None, layout: str = "bhsd", out=None):
-    """Gradients (dq, dk, dv) of ``pointwise_fwd`` for the output gradient
-    ``d_o``: ``info`` from ``mask_info_build`` (dQ pass), ``info_dkv`` from
-    ``mask_info_build_dkv`` (dK/dV pass), both for the same mask. k and v may
-    have fewer heads than q (a K/V head's gradients sum over its query
-    heads). ``out``: an optional (dq, dk, dv) to write into."""
+def _stat_strides(t: torch.Tensor, B: int, H: int, Sq: int):
+    """(batch, head) element strides of an fp32 [B, H, Sq] GPU tensor with
+    rows contiguous."""
+    if t.dtype != torch.float32 or not t.is_cuda or tuple(t.shape) != (B, H, Sq) or (Sq > 1 and t.stride(2) != 1):
+        raise ValueError(f"expected a float32 GPU tensor [B, H, Sq] = {(B, H, Sq)} with contiguous rows")
+    return _I64x2(t.stride(0), t.stride(1))
+
+
+def _backward(softmax: bool, q, k, v, d_o, info, info_dkv, scale, out_dtype, layout, out, lse=None, delta=None):
     lib = load_library()
     if q.dtype not in _DT or any(t.dtype != q.dtype for t in (k, v, d_o)):
         raise ValueError("q, k, v, d_o must share dtype float32 or bfloat16")
@@ -435,11 +454,99 @@ def pointwise_bwd(q, k, v, d_o, info: MaskInfo, info_dkv: MaskInfo, scale: float
         raise ValueError("info and info_dkv were built for different masks")
     desc, keep = info.mask_desc()
     c1, c2 = info.info_struct(), info_dkv.info_struct()
-    st = lib.splash_pointwise_bwd(_DT[q.dtype], _DT[out_dtype], B, H, Hk, Sq, Skv, D,
-                                  q.data_ptr(), qs, k.data_ptr(), ks, v.data_ptr(), vs, d_o.data_ptr(), dos,
-                                  dq.data_ptr(), dqs, dk.data_ptr(), dks, dv.data_ptr(), dvs,
-                                  float(scale), ctypes.byref(desc), ctypes.byref(c1), ctypes.byref(c2),
-                                  ctypes.c_void_p(_stream(q.device)))
+    head = (_DT[q.dtype], _DT[out_dtype], B, H, Hk, Sq, Skv, D,
+            q.data_ptr(), qs, k.data_ptr(), ks, v.data_ptr(), vs, d_o.data_ptr(), dos)
+    tail = (dq.data_ptr(), dqs, dk.data_ptr(), dks, dv.data_ptr(), dvs,
+            float(scale), ctypes.byref(desc), ctypes.byref(c1), ctypes.byref(c2), ctypes.c_void_p(_stream(q.device)))
+    if softmax:
+        ss = _stat_strides(lse, B, H, Sq)
+        if tuple(_stat_strides(delta, B, H, Sq)) != tuple(ss):
+            raise ValueError("lse and delta must share strides")
+        st = lib.splash_softmax_bwd(*head, lse.data_ptr(), delta.data_ptr(), ss, *tail)
+    else:
+        st = lib.splash_pointwise_bwd(*head, *tail)
     del keep
     _check(st)
     return dq, dk, dv
+
+
+def pointwise_bwd(q, k, v, d_o, info: MaskInfo, info_dkv: MaskInfo, scale: float | None = None,
+                  out_dtype=None, layout: str = "bhsd", out=None):
+    """Gradients (dq, dk, dv) of ``pointwise_fwd`` for the output gradient
+    ``d_o``: ``info`` from ``mask_info_build`` (dQ pass), ``info_dkv`` from
+    ``mask_info_build_dkv`` (dK/dV pass), both for the same mask. k and v may
+    have fewer heads than q (a K/V head's gradients sum over its query
+    heads). ``out``: an optional (dq, dk, dv) to write into."""
+    return _backward(False, q, k, v, d_o, info, info_dkv, scale, out_dtype, layout, out)
+
+
+# ---------------------------------------------------------------------------
+# softmax log-sum-exp and backward
+# ---------------------------------------------------------------------------
+
+
+def splash_fwd_lse(q, k, v, info: MaskInfo, scale: float | None = None, out=None, out_dtype=None,
+                   layout: str = "bhsd", lse=None):
+    """``splash_fwd`` that also returns the per-row log-sum-exp of the scores
+    (fp32 [B, H, Sq]; -inf for rows with no allowed key): (out, lse)."""
+    lib = load_library()
+    if info.dense:
+        raise ValueError("splash_fwd_lse takes head-mask metadata (no dense masks)")
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    qs, (B, H, Sq, D) = _strides(q, layout)
+    ks, (Bk, Hk, Skv, Dk) = _strides(k, layout)
+    vs, vshape = _strides(v, layout)
+    if (Bk, Dk) != (B, D) or vshape != (B, Hk, Skv, D) or Hk < 1 or H % Hk:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)} ({layout})")
+    if out_dtype is None:
+        out_dtype = q.dtype if out is None else out.dtype
+    if out is None:
+        shape = (B, H, Sq, D) if layout == "bhsd" else (B, Sq, H, D)
+        out = torch.empty(shape, dtype=out_dtype, device=q.device)
+    os_, oshape = _strides(out, layout)
+    if oshape != (B, H, Sq, D) or out.dtype != out_dtype or out_dtype not in _DT:
+        raise ValueError("bad output")
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    ls = _stat_strides(lse, B, H, Sq)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if (info.B, info.H, info.q_len, info.kv_len) != (B, H, Sq, Skv):
+        raise SplashError(SPLASH_ERR_METADATA_MISMATCH,
+                          f"metadata built for B={info.B} H={info.H} q_len={info.q_len} kv_len={info.kv_len}")
+    desc, keep = info.mask_desc()
+    cinfo = info.info_struct()
+    st = lib.splash_fwd_lse(_DT[q.dtype], _DT[out_dtype], B, H, Hk, Sq, Skv, D, q.data_ptr(), qs, k.data_ptr(), ks,
+                            v.data_ptr(), vs, out.data_ptr(), os_, lse.data_ptr(), ls, float(scale),
+                            ctypes.byref(desc), ctypes.byref(cinfo), ctypes.c_void_p(_stream(q.device)))
+    del keep
+    _check(st)
+    return out, lse
+
+
+def softmax_bwd_preprocess(o, d_o, layout: str = "bhsd", delta=None):
+    """delta = rowsum(o * d_o) in fp32 [B, H, Sq] (the softmax backward's
+    row term)."""
+    lib = load_library()
+    if o.dtype not in _DT or d_o.dtype != o.dtype or not (o.is_cuda and d_o.is_cuda):
+        raise ValueError("o and d_o must be GPU tensors of one dtype, float32 or bfloat16")
+    os_, (B, H, Sq, D) = _strides(o, layout)
+    ds_, dshape = _strides(d_o, layout)
+    if dshape != (B, H, Sq, D):
+        raise ValueError("o and d_o shapes differ")
+    if delta is None:
+        delta = torch.empty((B, H, Sq), dtype=torch.float32, device=o.device)
+    st = lib.splash_softmax_bwd_preprocess(_DT[o.dtype], B, H, Sq, D, o.data_ptr(), os_, d_o.data_ptr(), ds_,
+                                           delta.data_ptr(), _stat_strides(delta, B, H, Sq),
+                                           ctypes.c_void_p(_stream(o.device)))
+    _check(st)
+    return delta
+
+
+def softmax_bwd(q, k, v, d_o, lse, delta, info: MaskInfo, info_dkv: MaskInfo, scale: float | None = None,
+                out_dtype=None, layout: str = "bhsd", out=None):
+    """Gradients (dq, dk, dv) of ``splash_fwd``, given the forward's ``lse``
+    (``splash_fwd_lse``) and ``delta`` (``softmax_bwd_preprocess``); metadata
+    as for ``pointwise_bwd``."""
+    return _backward(True, q, k, v, d_o, info, info_dkv, scale, out_dtype, layout, out, lse, delta)

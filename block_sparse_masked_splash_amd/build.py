@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsplash.so")
 SOURCES = ["api.cpp", "dense_mask.cpp", "mask_info.hip", "splash_fwd_bf16.hip", "splash_fwd_f32.hip",
-           "splash_bwd_bf16.hip", "splash_bwd_f32.hip"]
+           "splash_bwd_bf16.hip", "splash_bwd_f32.hip", "softmax_delta.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 vector instructions are kept out of the device code.

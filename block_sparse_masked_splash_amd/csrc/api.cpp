@@ -112,7 +112,8 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
                          int q_len, int kv_len, int head_dim, const void* q, const int64_t q_strides[3], const void* k,
                          const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* o,
                          const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
-                         const splash_mask_info* info, const splash_partial_masks* partial, hipStream_t stream) {
+                         const splash_mask_info* info, const splash_partial_masks* partial, float* lse,
+                         const int64_t* lse_strides, hipStream_t stream) {
   splash_status s = check_sizes(B, H, q_len, kv_len);
   if (s != SPLASH_OK) return s;
   if (kv_heads < 1 || kv_heads > H || H % kv_heads != 0)
@@ -139,6 +140,12 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
   if ((s = check_tensor("k", k, k_strides, in_bytes, work && kv_len > 0)) != SPLASH_OK) return s;
   if ((s = check_tensor("v", v, v_strides, in_bytes, work && kv_len > 0)) != SPLASH_OK) return s;
   if ((s = check_tensor("o", o, o_strides, out_bytes, work)) != SPLASH_OK) return s;
+  if (lse_strides != nullptr) {  // log-sum-exp requested (softmax only)
+    if (pointwise) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "log-sum-exp is defined for softmax only");
+    if (work && lse == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse is null");
+    if (lse_strides[0] < 0 || lse_strides[1] < 0)
+      return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse strides must be >= 0");
+  }
 
   const bool seg = mask->q_segment_ids != nullptr;
   if (partial != nullptr && seg)
@@ -201,6 +208,11 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
   p.data_next = info->data_next;
   p.q_seg = mask->q_segment_ids;
   p.kv_seg = mask->kv_segment_ids;
+  if (lse_strides != nullptr) {
+    p.lse = lse;
+    p.lse_sb = lse_strides[0];
+    p.lse_sh = lse_strides[1];
+  }
   if (partial != nullptr) {
     p.mask_next = partial->mask_next;
     p.mask_blocks = partial->num_blocks > 0 ? partial->mask_blocks : nullptr;
@@ -232,10 +244,11 @@ splash_status check_info(const char* what, const splash_mask_info* info, int B, 
   return SPLASH_OK;
 }
 
-splash_status bwd_common(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads, int q_len,
-                         int kv_len, int head_dim, const void* q, const int64_t q_strides[3], const void* k,
+splash_status bwd_common(bool softmax, splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
+                         int q_len, int kv_len, int head_dim, const void* q, const int64_t q_strides[3], const void* k,
                          const int64_t k_strides[3], const void* v, const int64_t v_strides[3], const void* d_o,
-                         const int64_t do_strides[3], void* dq, const int64_t dq_strides[3], void* dk,
+                         const int64_t do_strides[3], const float* lse, const float* delta,
+                         const int64_t* stat_strides, void* dq, const int64_t dq_strides[3], void* dk,
                          const int64_t dk_strides[3], void* dv, const int64_t dv_strides[3], float scale,
                          const splash_mask_desc* mask, const splash_mask_info* info,
                          const splash_mask_info* info_dkv, hipStream_t stream) {
@@ -282,6 +295,15 @@ splash_status bwd_common(splash_dtype in_dtype, splash_dtype out_dtype, int B, i
   if ((s = check_tensor("dq", dq, dq_strides, out_bytes, qwork)) != SPLASH_OK) return s;
   if ((s = check_tensor("dk", dk, dk_strides, out_bytes, kwork)) != SPLASH_OK) return s;
   if ((s = check_tensor("dv", dv, dv_strides, out_bytes, kwork)) != SPLASH_OK) return s;
+  if (softmax) {
+    if (stat_strides == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse / delta strides are null");
+    if (stat_strides[0] < 0 || stat_strides[1] < 0)
+      return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse / delta strides must be >= 0");
+    if (both && (lse == nullptr || delta == nullptr))
+      return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse or delta is null");
+    if (both && (reinterpret_cast<uintptr_t>(lse) % 4 != 0 || reinterpret_cast<uintptr_t>(delta) % 4 != 0))
+      return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse and delta must be 4-byte aligned");
+  }
   if (!work) return ok();
   const int64_t nq = ceil_div(q_len, bq), nk = ceil_div(kv_len, bkv);
   const int64_t cnq = ceil_div(q_len, cbq), cnk = ceil_div(kv_len, cbkv);
@@ -329,9 +351,16 @@ splash_status bwd_common(splash_dtype in_dtype, splash_dtype out_dtype, int B, i
   p.c_data_next = info_dkv->data_next;
   p.q_seg = mask->q_segment_ids;
   p.kv_seg = mask->kv_segment_ids;
+  p.softmax = softmax ? 1 : 0;
+  if (softmax) {
+    p.lse = lse;
+    p.delta = delta;
+    p.st_sb = stat_strides[0];
+    p.st_sh = stat_strides[1];
+  }
   hipError_t e = f32 ? splash::launch_pointwise_bwd_f32(p, stream)
                      : splash::launch_pointwise_bwd_bf16(p, out_dtype == SPLASH_F32, stream);
-  return hip_status(e, "pointwise backward launch");
+  return hip_status(e, softmax ? "softmax backward launch" : "pointwise backward launch");
 }
 
 splash_status mask_info_common(bool dkv, int B, int H, int q_len, int kv_len, int block_q, int block_kv,
@@ -387,9 +416,58 @@ splash_status splash_pointwise_bwd(splash_dtype in_dtype, splash_dtype out_dtype
                                    void* dv, const int64_t dv_strides[3], float scale,
                                    const splash_mask_desc* mask, const splash_mask_info* info,
                                    const splash_mask_info* info_dkv, hipStream_t stream) {
-  return bwd_common(in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides, v,
-                    v_strides, d_o, do_strides, dq, dq_strides, dk, dk_strides, dv, dv_strides, scale, mask, info,
-                    info_dkv, stream);
+  return bwd_common(false, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides,
+                    v, v_strides, d_o, do_strides, nullptr, nullptr, nullptr, dq, dq_strides, dk, dk_strides, dv,
+                    dv_strides, scale, mask, info, info_dkv, stream);
+}
+
+splash_status splash_softmax_bwd_preprocess(splash_dtype dtype, int B, int H, int q_len, int head_dim,
+                                            const void* o, const int64_t o_strides[3], const void* d_o,
+                                            const int64_t do_strides[3], float* delta,
+                                            const int64_t delta_strides[2], hipStream_t stream) {
+  if (B < 0 || H < 0 || !len_ok(q_len))
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d q_len=%d", B, H, q_len);
+  if (dtype != SPLASH_F32 && dtype != SPLASH_BF16) return record_error(SPLASH_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return record_error(head_dim <= 0 ? SPLASH_ERR_INVALID_ARGUMENT : SPLASH_ERR_UNSUPPORTED,
+                        "head_dim=%d (supported: 64, 128)", head_dim);
+  const bool work = (int64_t)B * H * q_len > 0;
+  const int eb = dtype == SPLASH_F32 ? 4 : 2;
+  splash_status s;
+  if ((s = check_tensor("o", o, o_strides, eb, work)) != SPLASH_OK) return s;
+  if ((s = check_tensor("d_o", d_o, do_strides, eb, work)) != SPLASH_OK) return s;
+  if (delta_strides == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "delta strides are null");
+  if (delta_strides[0] < 0 || delta_strides[1] < 0)
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "delta strides must be >= 0");
+  if (work && (delta == nullptr || reinterpret_cast<uintptr_t>(delta) % 4 != 0))
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "delta is null or not 4-byte aligned");
+  if (!work) return ok();
+  splash::DeltaParams p{};
+  p.B = B;
+  p.H = H;
+  p.q_len = q_len;
+  p.head_dim = head_dim;
+  p.o = o;
+  p.d_o = d_o;
+  p.delta = delta;
+  p.o_sb = o_strides[0], p.o_sh = o_strides[1], p.o_ss = o_strides[2];
+  p.do_sb = do_strides[0], p.do_sh = do_strides[1], p.do_ss = do_strides[2];
+  p.d_sb = delta_strides[0], p.d_sh = delta_strides[1];
+  return hip_status(splash::launch_softmax_delta(p, dtype == SPLASH_BF16, stream), "softmax delta launch");
+}
+
+splash_status splash_softmax_bwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
+                                 int q_len, int kv_len, int head_dim, const void* q, const int64_t q_strides[3],
+                                 const void* k, const int64_t k_strides[3], const void* v,
+                                 const int64_t v_strides[3], const void* d_o, const int64_t do_strides[3],
+                                 const float* lse, const float* delta, const int64_t stat_strides[2], void* dq,
+                                 const int64_t dq_strides[3], void* dk, const int64_t dk_strides[3], void* dv,
+                                 const int64_t dv_strides[3], float scale, const splash_mask_desc* mask,
+                                 const splash_mask_info* info, const splash_mask_info* info_dkv,
+                                 hipStream_t stream) {
+  return bwd_common(true, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides, v,
+                    v_strides, d_o, do_strides, lse, delta, stat_strides, dq, dq_strides, dk, dk_strides, dv,
+                    dv_strides, scale, mask, info, info_dkv, stream);
 }
 
 }  // extern "C"
@@ -447,7 +525,7 @@ splash_status splash_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, i
                          const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
                          const splash_mask_info* info, hipStream_t stream) {
   return fwd_common(false, in_dtype, out_dtype, B, H, H, q_len, kv_len, head_dim, q, q_strides, k, k_strides, v,
-                    v_strides, o, o_strides, scale, mask, info, nullptr, stream);
+                    v_strides, o, o_strides, scale, mask, info, nullptr, nullptr, nullptr, stream);
 }
 
 splash_status splash_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int q_len,
@@ -457,7 +535,7 @@ splash_status splash_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_dtype
                                    const splash_mask_desc* mask, const splash_mask_info* info,
                                    hipStream_t stream) {
   return fwd_common(true, in_dtype, out_dtype, B, H, H, q_len, kv_len, head_dim, q, q_strides, k, k_strides, v,
-                    v_strides, o, o_strides, scale, mask, info, nullptr, stream);
+                    v_strides, o, o_strides, scale, mask, info, nullptr, nullptr, nullptr, stream);
 }
 
 splash_status splash_gqa_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads, int q_len,
@@ -466,7 +544,7 @@ splash_status splash_gqa_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int 
                              const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
                              const splash_mask_info* info, hipStream_t stream) {
   return fwd_common(false, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides,
-                    v, v_strides, o, o_strides, scale, mask, info, nullptr, stream);
+                    v, v_strides, o, o_strides, scale, mask, info, nullptr, nullptr, nullptr, stream);
 }
 
 splash_status splash_gqa_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
@@ -476,7 +554,17 @@ splash_status splash_gqa_pointwise_fwd(splash_dtype in_dtype, splash_dtype out_d
                                        const int64_t o_strides[3], float scale, const splash_mask_desc* mask,
                                        const splash_mask_info* info, hipStream_t stream) {
   return fwd_common(true, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides,
-                    v, v_strides, o, o_strides, scale, mask, info, nullptr, stream);
+                    v, v_strides, o, o_strides, scale, mask, info, nullptr, nullptr, nullptr, stream);
+}
+
+splash_status splash_fwd_lse(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads, int q_len,
+                             int kv_len, int head_dim, const void* q, const int64_t q_strides[3], const void* k,
+                             const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* o,
+                             const int64_t o_strides[3], float* lse, const int64_t lse_strides[2], float scale,
+                             const splash_mask_desc* mask, const splash_mask_info* info, hipStream_t stream) {
+  if (lse_strides == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse strides are null");
+  return fwd_common(false, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides,
+                    v, v_strides, o, o_strides, scale, mask, info, nullptr, lse, lse_strides, stream);
 }
 
 splash_status splash_masked_fwd(int pointwise, splash_dtype in_dtype, splash_dtype out_dtype, int B, int H,
@@ -488,7 +576,7 @@ splash_status splash_masked_fwd(int pointwise, splash_dtype in_dtype, splash_dty
   if (pointwise != 0 && pointwise != 1)
     return record_error(SPLASH_ERR_INVALID_ARGUMENT, "pointwise=%d must be 0 or 1", pointwise);
   return fwd_common(pointwise == 1, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k,
-                    k_strides, v, v_strides, o, o_strides, scale, mask, info, partial, stream);
+                    k_strides, v, v_strides, o, o_strides, scale, mask, info, partial, nullptr, nullptr, stream);
 }
 
 }  // extern "C"

@@ -64,6 +64,9 @@ struct FwdParams {
   const int32_t* mask_next;
   const uint32_t* mask_blocks;
   int64_t num_mask_blocks;
+  // softmax: per-row log-sum-exp [B, H, q_len] (rows contiguous), or null
+  float* lse;
+  int64_t lse_sb, lse_sh;
   HeadBand band[SPLASH_MAX_MASK_HEADS];
 };
 
@@ -101,7 +104,24 @@ struct BwdParams {
   const int32_t* c_data_next;
   const int32_t* q_seg;
   const int32_t* kv_seg;
+  // softmax backward: per-row log-sum-exp of the forward and
+  // delta = rowsum(dO * O), both [B, H, q_len] fp32 (rows contiguous)
+  int softmax;
+  const float* lse;
+  const float* delta;
+  int64_t st_sb, st_sh;
   HeadBand band[SPLASH_MAX_MASK_HEADS];
+};
+
+// delta = rowsum(O * dO) per (b, h, query), fp32.
+struct DeltaParams {
+  int B, H, q_len, head_dim;
+  const void* o;
+  const void* d_o;
+  float* delta;
+  int64_t o_sb, o_sh, o_ss;
+  int64_t do_sb, do_sh, do_ss;
+  int64_t d_sb, d_sh;
 };
 
 // Launchers; return the launch error (hipSuccess when enqueued).
@@ -115,5 +135,7 @@ hipError_t launch_fwd_f32(const FwdParams& p, bool pointwise, hipStream_t stream
 // Pointwise backward, bf16 inputs (gradients bf16 or fp32) and fp32 inputs.
 hipError_t launch_pointwise_bwd_bf16(const BwdParams& p, bool out_f32, hipStream_t stream);
 hipError_t launch_pointwise_bwd_f32(const BwdParams& p, hipStream_t stream);
+// (the softmax backward runs through the same two launchers with p.softmax set)
+hipError_t launch_softmax_delta(const DeltaParams& p, bool bf16, hipStream_t stream);
 
 }  // namespace splash

@@ -1,4 +1,4 @@
-// Pointwise (SiLU) attention backward, bf16 inputs, CDNA4 matrix cores.
+// Attention backward (pointwise SiLU and softmax), bf16 inputs, CDNA4 matrix cores.
 //
 // What is computed ("hstu_ops.py" (RecML), _pointwise_splash_attention_bwd_kernel_impl):
 // with x = scale q·k, sig = logistic(x) (0 where the mask forbids the pair),
@@ -29,6 +29,14 @@
 // The dK/dV pass recomputes S and dP that the dQ pass also forms (7 products
 // per block pair instead of 5), in exchange for deterministic sums with no
 // atomics and no per-kv-block partial dQ.
+//
+// Softmax attention (SM) runs through the same two kernels with the softmax
+// derivative instead (the gradient of page 3 section 12's definition, given
+// the forward's per-row log-sum-exp LSE and delta = rowsum(dO * O)):
+//   P = e^(x - LSE) (0 where masked), dV += Pᵀ dO, dS = P (dP - delta),
+//   dK += scale dSᵀ Q, dQ += scale dS K.
+// The dK/dV kernel copies the tile's LSE and delta values to LDS beside the
+// Q and dO tiles; the dQ kernel keeps its query's two values in registers.
 
 #include <type_traits>
 
@@ -91,7 +99,8 @@ struct DkvTiling {
   static constexpr int NS = D / 16;
   static constexpr int ND = D / 32;
   static constexpr int SEG_OFF = 2 * 2 * TILE;   // [stage][Q | dO][TILE], then [stage][QC] ids
-  static constexpr int LDS_BYTES = SEG_OFF + 2 * QC * 4;
+  static constexpr int STAT_OFF = SEG_OFF + 2 * QC * 4;  // softmax: [stage][LSE | delta][QC] floats
+  static constexpr int LDS_BYTES = STAT_OFF + 2 * 2 * QC * 4;
   static_assert(LOADS >= 1, "tile too small for the workgroup");
 };
 
@@ -103,9 +112,9 @@ constexpr int dkv_waves() {
   return D == 64 ? 2 : 1;
 }
 
-template <int D, int NW, typename OutT>
+template <int D, int NW, bool SM, typename OutT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dkv_waves<D>(), dkv_waves<D>())))
-void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
+void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
   using T = DkvTiling<D, NW>;
   constexpr int NS = T::NS;
   constexpr int ND = T::ND;
@@ -207,6 +216,16 @@ void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, in
       const u32x4 srs = buffer_rsrc(p.q_seg + (int64_t)b * p.q_len + q0, (uint32_t)(rows * 4));
       if (lane < T::SEG_ROWS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), sdst);
     }
+    if constexpr (SM) {
+      float* st = reinterpret_cast<float*>(smem + T::STAT_OFF) + stage * 2 * QC + wave * T::SEG_ROWS;
+      const int64_t off = b * p.st_sb + h * p.st_sh + q0;
+      const u32x4 lrs = buffer_rsrc(p.lse + off, (uint32_t)(rows * 4));
+      const u32x4 drs2 = buffer_rsrc(p.delta + off, (uint32_t)(rows * 4));
+      if (lane < T::SEG_ROWS) {
+        lds_copy4(lrs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st));
+        lds_copy4(drs2, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st + QC));
+      }
+    }
   };
 
   // Zeroed tiles: rows a clipped copy leaves unwritten hold zeros, never NaN.
@@ -223,6 +242,8 @@ void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, in
       dv[db][r] = 0.0f;
     }
   const float nl = -p.scale * 1.4426950408889634f;
+  const float cl = p.scale * 1.4426950408889634f;  // softmax: x log2(e) = cl q·k
+  constexpr float kMasked = SM ? -__builtin_inff() : kMaskedT;
 
   int cur_g = 0, cur_i = first_i(0), cur_t = 0;
   settle(cur_g, cur_i);
@@ -247,6 +268,7 @@ void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, in
     const char* qt = smem + stage * 2 * T::TILE;
     const char* dt = qt + T::TILE;
     const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * QC;
+    const float* sst = reinterpret_cast<const float*>(smem + T::STAT_OFF) + stage * 2 * QC;
 
     // ---- S = Q Kᵀ and dP = dO Vᵀ: 32 queries (rows) x this wave's 32 keys ----
     f32x16 sacc, pacc;
@@ -270,9 +292,19 @@ void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, in
     // block the band, the sequence ends and (with ids) segment equality leave
     // the lane's key one run of queries [a, e] of the tile plus the id test;
     // full blocks take a path with no per-score test at all.
-    f32x16& t = sacc;  // t = nl q·k, in place
+    // t: the exponent, in place (pointwise nl q·k; softmax (x - LSE) log2(e))
+    f32x16& t = sacc;
+    if constexpr (SM) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) t[r] = sacc[r] * nl;
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sst + 8 * u + 4 * hh);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) t[4 * u + v4] = __builtin_fmaf(sacc[4 * u + v4], cl, -kLog2e * l4[v4]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[r] = sacc[r] * nl;
+    }
     if (partial) {
       int a = key - band.hi - q0;
       int e = key - band.lo - q0;
@@ -291,20 +323,34 @@ void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, in
           for (int v4 = 0; v4 < 4; ++v4) {
             const int r = 4 * u + v4;
             const bool ok = ((uint32_t)(base + 8 * u + v4) <= width) & (ids[v4] == kseg);
-            t[r] = ok ? t[r] : kMaskedT;
+            t[r] = ok ? t[r] : kMasked;
           }
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) t[r] = ((uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width) ? t[r] : kMaskedT;
+        for (int r = 0; r < 16; ++r) t[r] = ((uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width) ? t[r] : kMasked;
       }
     }
     bf16x8 pb[2], sb[2];
+    if constexpr (SM) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const Weights w = pointwise_weights(t[r], pacc[r]);
-      pb[r >> 3][r & 7] = (__bf16)w.p;
-      sb[r >> 3][r & 7] = (__bf16)w.ds;
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sst + QC + 8 * u + 4 * hh);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int r = 4 * u + v4;
+          const float pr = __builtin_amdgcn_exp2f(t[r]);
+          pb[r >> 3][r & 7] = (__bf16)pr;
+          sb[r >> 3][r & 7] = (__bf16)(pr * (pacc[r] - d4[v4]));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const Weights w = pointwise_weights(t[r], pacc[r]);
+        pb[r >> 3][r & 7] = (__bf16)w.p;
+        sb[r >> 3][r & 7] = (__bf16)w.ds;
+      }
     }
 
     // ---- dVᵀ += dOᵀ P', dKᵀ += Qᵀ dS' over the 32 queries ----
@@ -337,9 +383,10 @@ void pointwise_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, in
     if (!step(std::integral_constant<int, 1>{})) break;
   }
 
-  // ---- dK = (scale / q_len) dK', dV = (-ln 2 / q_len) dV'; lane's key row ----
+  // ---- pointwise: dK = (scale / q_len) dK', dV = (-ln 2 / q_len) dV';
+  //      softmax:   dK = scale dK', dV = dV'; lane's key row ----
   if (kvalid) {
-    const float ck = p.scale * p.inv_q_len, cv = -kLn2 * p.inv_q_len;
+    const float ck = SM ? p.scale : p.scale * p.inv_q_len, cv = SM ? 1.0f : -kLn2 * p.inv_q_len;
     OutT* dkr = reinterpret_cast<OutT*>(p.dk) + b * p.dk_sb + hk * p.dk_sh + (int64_t)key * p.dk_ss;
     OutT* dvr = reinterpret_cast<OutT*>(p.dv) + b * p.dv_sb + hk * p.dv_sh + (int64_t)key * p.dv_ss;
 #pragma unroll
@@ -380,9 +427,9 @@ constexpr int dq_waves() {
   return D == 64 ? 3 : 2;
 }
 
-template <int D, int NW, typename OutT>
+template <int D, int NW, bool SM, typename OutT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_waves<D>(), dq_waves<D>())))
-void pointwise_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
+void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
   using T = DqTiling<D, NW>;
   constexpr int KC = T::KC;
   constexpr int NS = T::NS;
@@ -432,6 +479,13 @@ void pointwise_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
     }
   }
   const int32_t myseg = (has_seg && qvalid) ? p.q_seg[(int64_t)b * p.q_len + qrow] : 0;
+  // softmax: this query's LSE (log2 units) and delta
+  float lse2 = 0.0f, dlt = 0.0f;
+  if (SM && qvalid) {
+    const int64_t off = b * p.st_sb + h * p.st_sh + qrow;
+    lse2 = p.lse[off] * kLog2e;
+    dlt = p.delta[off];
+  }
 
   int aoff[NS];
   row_operand_offsets<D>(lane, aoff);
@@ -473,6 +527,8 @@ void pointwise_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
   const float nl = -p.scale * 1.4426950408889634f;
+  const float cl = p.scale * 1.4426950408889634f;
+  constexpr float kMasked = SM ? -__builtin_inff() : kMaskedT;
 
   auto next_block = [&](int jj) {
     const int jn = (jj + 1 < p.nk) ? scalar_load_i32(dnext + jj + 1) : p.nk;
@@ -519,9 +575,10 @@ void pointwise_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, oreg[s], pacc, 0, 0, 0);
       }
       // element r: key k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4, query qrow
-      f32x16& t = sacc;  // t = nl q·k, in place
+      // t: the exponent, in place (pointwise nl q·k; softmax (x - LSE) log2(e))
+      f32x16& t = sacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t[r] = sacc[r] * nl;
+      for (int r = 0; r < 16; ++r) t[r] = SM ? __builtin_fmaf(sacc[r], cl, -lse2) : sacc[r] * nl;
       if (partial) {
         int a = qrow + band.lo - k0;
         int e = qrow + band.hi - k0;
@@ -540,17 +597,19 @@ void pointwise_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
             for (int v4 = 0; v4 < 4; ++v4) {
               const int r = 4 * u + v4;
               const bool ok = ((uint32_t)(base + 8 * u + v4) <= width) & (ids[v4] == myseg);
-              t[r] = ok ? t[r] : kMaskedT;
+              t[r] = ok ? t[r] : kMasked;
             }
           }
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) t[r] = ((uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width) ? t[r] : kMaskedT;
+          for (int r = 0; r < 16; ++r) t[r] = ((uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width) ? t[r] : kMasked;
         }
       }
       bf16x8 sb[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sb[r >> 3][r & 7] = (__bf16)pointwise_weights(t[r], pacc[r]).ds;
+      for (int r = 0; r < 16; ++r)
+        sb[r >> 3][r & 7] = SM ? (__bf16)(__builtin_amdgcn_exp2f(t[r]) * (pacc[r] - dlt))
+                               : (__bf16)pointwise_weights(t[r], pacc[r]).ds;
 
       // ---- dQᵀ += Kᵀ dSᵀ over these 32 keys ----
 #pragma unroll
@@ -575,7 +634,7 @@ void pointwise_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
   }
 
   if (qvalid) {
-    const float cq = p.scale * p.inv_q_len;
+    const float cq = SM ? p.scale : p.scale * p.inv_q_len;
     OutT* dqr = reinterpret_cast<OutT*>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)qrow * p.dq_ss;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
@@ -602,31 +661,36 @@ Order order_for(int64_t units, int64_t per_unit) {
   return {total, (total + 7) / 8, units % 8 == 0 ? 1 : 0};
 }
 
-template <int D, int NW, typename OutT>
+template <int D, int NW, bool SM, typename OutT>
 hipError_t launch_dkv(const BwdParams& p, hipStream_t stream) {
   const Order o = order_for((int64_t)p.B * p.kv_heads, p.c_nk);
   if (o.total == 0) return hipSuccess;
-  hipLaunchKernelGGL((pointwise_dkv_bf16_kernel<D, NW, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((bwd_dkv_bf16_kernel<D, NW, SM, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
                      stream, p, (int)o.total, (int)o.per_xcd, o.interleaved);
   return hipGetLastError();
 }
 
-template <int D, int NW, typename OutT>
+template <int D, int NW, bool SM, typename OutT>
 hipError_t launch_dq(const BwdParams& p, hipStream_t stream) {
   const Order o = order_for((int64_t)p.B * p.kv_heads, (int64_t)p.nq * p.kv_group);
   if (o.total == 0) return hipSuccess;
-  hipLaunchKernelGGL((pointwise_dq_bf16_kernel<D, NW, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NW, SM, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
                      stream, p, (int)o.total, (int)o.per_xcd, o.interleaved);
   return hipGetLastError();
+}
+
+template <int D, bool SM, typename OutT>
+hipError_t launch_sm(const BwdParams& p, hipStream_t stream) {
+  hipError_t e = p.c_block_kv == 64 ? launch_dkv<D, 2, SM, OutT>(p, stream) : launch_dkv<D, 4, SM, OutT>(p, stream);
+  if (e != hipSuccess) return e;
+  if (p.block_q == 64) return launch_dq<D, 2, SM, OutT>(p, stream);
+  if (p.block_q == 256) return launch_dq<D, 8, SM, OutT>(p, stream);
+  return launch_dq<D, 4, SM, OutT>(p, stream);
 }
 
 template <int D, typename OutT>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
-  hipError_t e = p.c_block_kv == 64 ? launch_dkv<D, 2, OutT>(p, stream) : launch_dkv<D, 4, OutT>(p, stream);
-  if (e != hipSuccess) return e;
-  if (p.block_q == 64) return launch_dq<D, 2, OutT>(p, stream);
-  if (p.block_q == 256) return launch_dq<D, 8, OutT>(p, stream);
-  return launch_dq<D, 4, OutT>(p, stream);
+  return p.softmax ? launch_sm<D, true, OutT>(p, stream) : launch_sm<D, false, OutT>(p, stream);
 }
 
 }  // namespace

@@ -1,5 +1,5 @@
-// Pointwise (SiLU) attention backward for fp32 inputs, on the vector ALUs in
-// fp32 throughout.
+// Attention backward (pointwise SiLU and softmax) for fp32 inputs, on the
+// vector ALUs in fp32 throughout.
 //
 // Same arithmetic and walks as the bf16 kernels ("hstu_ops.py" (RecML),
 // _pointwise_splash_attention_bwd_kernel_impl): with x = scale q·k and
@@ -9,7 +9,9 @@
 // kv block), walking the block's column of q blocks for every query head of
 // the group; dQ: one workgroup per (b, query head, q block), walking its row
 // of kv blocks. D / 32 adjacent lanes share one key (or query) row, each
-// holding 32 of its head dimensions.
+// holding 32 of its head dimensions. Softmax (SM): P = e^(x - LSE),
+// dS = P (dp - delta), dV = sum P dO, dK = scale sum dS q, dQ = scale sum dS k,
+// with the forward's per-row LSE and delta = rowsum(dO * O).
 
 #include "internal.h"
 
@@ -27,14 +29,16 @@ __device__ inline float group_sum(float x) {
 
 __device__ inline float logistic(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-template <int D, int BKV>
-__global__ __launch_bounds__(BKV*(D / 32)) void pointwise_dkv_f32_kernel(BwdParams p) {
+template <int D, int BKV, bool SM>
+__global__ __launch_bounds__(BKV*(D / 32)) void bwd_dkv_f32_kernel(BwdParams p) {
   constexpr int G = D / 32;
   constexpr int NT = BKV * G;
   constexpr int STRIDE = D + 4;
   __shared__ __attribute__((aligned(16))) float sQ[TT * STRIDE];
   __shared__ __attribute__((aligned(16))) float sO[TT * STRIDE];
   __shared__ int32_t sQseg[TT];
+  __shared__ float sLse[TT];
+  __shared__ float sDelta[TT];
 
   const int tid = threadIdx.x;
   const int rl = tid / G;
@@ -92,6 +96,12 @@ __global__ __launch_bounds__(BKV*(D / 32)) void pointwise_dkv_f32_kernel(BwdPara
           const int q = q0 + tid;
           sQseg[tid] = q < p.q_len ? p.q_seg[(int64_t)b * p.q_len + q] : 0;
         }
+        if (SM && tid < TT) {
+          const int q = q0 + tid;
+          const int64_t off = b * p.st_sb + h * p.st_sh + q;
+          sLse[tid] = q < p.q_len ? p.lse[off] : 0.0f;
+          sDelta[tid] = q < p.q_len ? p.delta[off] : 0.0f;
+        }
         __syncthreads();
         for (int qq = 0; qq < TT; ++qq) {
           float s = 0.0f, dp = 0.0f;
@@ -109,9 +119,15 @@ __global__ __launch_bounds__(BKV*(D / 32)) void pointwise_dkv_f32_kernel(BwdPara
           }
           if (!ok) continue;
           const float x = s * p.scale;
-          const float sg = logistic(x);
-          const float pv = x * sg;
-          const float ds = dp * (sg + pv * (1.0f - sg));
+          float pv, ds;
+          if constexpr (SM) {
+            pv = expf(x - sLse[qq]);
+            ds = pv * (dp - sDelta[qq]);
+          } else {
+            const float sg = logistic(x);
+            pv = x * sg;
+            ds = dp * (sg + pv * (1.0f - sg));
+          }
           for (int d = 0; d < 32; ++d) {
             dv[d] = fmaf(pv, sO[qq * STRIDE + part * 32 + d], dv[d]);
             dk[d] = fmaf(ds, sQ[qq * STRIDE + part * 32 + d], dk[d]);
@@ -126,16 +142,16 @@ __global__ __launch_bounds__(BKV*(D / 32)) void pointwise_dkv_f32_kernel(BwdPara
   if (kvalid) {
     float* dkr = reinterpret_cast<float*>(p.dk) + b * p.dk_sb + hk * p.dk_sh + (int64_t)key * p.dk_ss + part * 32;
     float* dvr = reinterpret_cast<float*>(p.dv) + b * p.dv_sb + hk * p.dv_sh + (int64_t)key * p.dv_ss + part * 32;
-    const float ck = p.scale * p.inv_q_len;
+    const float ck = SM ? p.scale : p.scale * p.inv_q_len, cv = SM ? 1.0f : p.inv_q_len;
     for (int d = 0; d < 32; ++d) {
       dkr[d] = dk[d] * ck;
-      dvr[d] = dv[d] * p.inv_q_len;
+      dvr[d] = dv[d] * cv;
     }
   }
 }
 
-template <int D, int BQ>
-__global__ __launch_bounds__(BQ*(D / 32)) void pointwise_dq_f32_kernel(BwdParams p) {
+template <int D, int BQ, bool SM>
+__global__ __launch_bounds__(BQ*(D / 32)) void bwd_dq_f32_kernel(BwdParams p) {
   constexpr int G = D / 32;
   constexpr int NT = BQ * G;
   constexpr int STRIDE = D + 4;
@@ -171,6 +187,11 @@ __global__ __launch_bounds__(BQ*(D / 32)) void pointwise_dq_f32_kernel(BwdParams
     dq[d] = 0.0f;
   }
   const int32_t qseg = (has_seg && qvalid) ? p.q_seg[(int64_t)b * p.q_len + qrow] : 0;
+  float lse = 0.0f, dlt = 0.0f;
+  if (SM && qvalid) {
+    lse = p.lse[b * p.st_sb + h * p.st_sh + qrow];
+    dlt = p.delta[b * p.st_sb + h * p.st_sh + qrow];
+  }
 
   const int64_t mrow = (((int64_t)bm * p.meta_heads + hm) * p.nq + i) * p.nk;
   int jb = p.nk > 0 ? p.data_next[mrow] : p.nk;
@@ -214,8 +235,13 @@ __global__ __launch_bounds__(BQ*(D / 32)) void pointwise_dq_f32_kernel(BwdParams
         }
         if (!ok) continue;
         const float x = s * p.scale;
-        const float sg = logistic(x);
-        const float ds = dp * (sg + x * sg * (1.0f - sg));
+        float ds;
+        if constexpr (SM) {
+          ds = expf(x - lse) * (dp - dlt);
+        } else {
+          const float sg = logistic(x);
+          ds = dp * (sg + x * sg * (1.0f - sg));
+        }
         for (int d = 0; d < 32; ++d) dq[d] = fmaf(ds, sK[kk * STRIDE + part * 32 + d], dq[d]);
       }
     }
@@ -225,34 +251,39 @@ __global__ __launch_bounds__(BQ*(D / 32)) void pointwise_dq_f32_kernel(BwdParams
 
   if (qvalid) {
     float* dqr = reinterpret_cast<float*>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)qrow * p.dq_ss + part * 32;
-    const float cq = p.scale * p.inv_q_len;
+    const float cq = SM ? p.scale : p.scale * p.inv_q_len;
     for (int d = 0; d < 32; ++d) dqr[d] = dq[d] * cq;
   }
 }
 
-template <int D, int BKV>
+template <int D, int BKV, bool SM>
 hipError_t launch_dkv_f32(const BwdParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.B * p.kv_heads * p.c_nk;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((pointwise_dkv_f32_kernel<D, BKV>), dim3((unsigned)grid), dim3(BKV * (D / 32)), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkv_f32_kernel<D, BKV, SM>), dim3((unsigned)grid), dim3(BKV * (D / 32)), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int BQ>
+template <int D, int BQ, bool SM>
 hipError_t launch_dq_f32(const BwdParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.nq * p.B * p.H;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((pointwise_dq_f32_kernel<D, BQ>), dim3((unsigned)grid), dim3(BQ * (D / 32)), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, BQ, SM>), dim3((unsigned)grid), dim3(BQ * (D / 32)), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D, bool SM>
+hipError_t launch_sm_f32(const BwdParams& p, hipStream_t stream) {
+  hipError_t e = p.c_block_kv == 64 ? launch_dkv_f32<D, 64, SM>(p, stream) : launch_dkv_f32<D, 128, SM>(p, stream);
+  if (e != hipSuccess) return e;
+  if (p.block_q == 64) return launch_dq_f32<D, 64, SM>(p, stream);
+  if (p.block_q == 256) return launch_dq_f32<D, 256, SM>(p, stream);
+  return launch_dq_f32<D, 128, SM>(p, stream);
 }
 
 template <int D>
 hipError_t launch_d_f32(const BwdParams& p, hipStream_t stream) {
-  hipError_t e = p.c_block_kv == 64 ? launch_dkv_f32<D, 64>(p, stream) : launch_dkv_f32<D, 128>(p, stream);
-  if (e != hipSuccess) return e;
-  if (p.block_q == 64) return launch_dq_f32<D, 64>(p, stream);
-  if (p.block_q == 256) return launch_dq_f32<D, 256>(p, stream);
-  return launch_dq_f32<D, 128>(p, stream);
+  return p.softmax ? launch_sm_f32<D, true>(p, stream) : launch_sm_f32<D, false>(p, stream);
 }
 
 }  // namespace

@@ -407,6 +407,11 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
   if constexpr (!PW) {
     const float l = sum_xor32(lsum);
     inv = l > 0.0f ? 1.0f / l : 0.0f;
+    // log-sum-exp of the row's scores x = scale q·k: the probabilities are
+    // 2^(x log2(e) - m) summing to L, so log sum e^x = (m + log2 L) ln 2
+    // (-inf for a row with no allowed key)
+    if (p.lse != nullptr && hh == 0 && qrow < p.q_len)
+      p.lse[b * p.lse_sb + h * p.lse_sh + qrow] = l > 0.0f ? (mref + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : kNegInf;
   }
   if (qrow < p.q_len) {
     OutT* orow = og + (int64_t)qrow * p.o_ss;

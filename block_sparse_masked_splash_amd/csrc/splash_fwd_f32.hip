@@ -153,6 +153,10 @@ __global__ __launch_bounds__(BQ*(D / 32)) void splash_fwd_f32_kernel(FwdParams p
   if (qvalid) {
     float inv = 1.0f;
     if constexpr (!PW) inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    // log-sum-exp of the row's scores (-inf with no allowed key)
+    if constexpr (!PW)
+      if (p.lse != nullptr && part == 0)
+        p.lse[b * p.lse_sb + h * p.lse_sh + qrow] = l_run > 0.0f ? m_run + logf(l_run) : kNegInf;
     float* orow = og + (int64_t)qrow * p.o_ss + part * 32;
     for (int d = 0; d < 32; ++d) orow[d] = o[d] * inv;
   }

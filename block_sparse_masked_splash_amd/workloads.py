@@ -106,6 +106,8 @@ WORKLOADS = {
     "b5": Workload("b5", 8, 8, 4096, 64, "bf16", 0.5, (CAUSAL,), 128, 128, False, True, 9, backward=True),
     # the pointwise backward at D = 128: B=2 H=16 S=4096
     "b5h": Workload("b5h", 2, 16, 4096, 128, "bf16", 0.5, (CAUSAL,), 128, 128, False, True, 10, backward=True),
+    # the softmax backward at the causal S=8192 shape
+    "s3h": Workload("s3h", 2, 32, 8192, 128, "bf16", 1.0, (CAUSAL,), 128, 128, False, False, 11, backward=True),
 }
 
 

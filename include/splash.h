@@ -295,6 +295,58 @@ splash_status splash_pointwise_bwd(splash_dtype in_dtype, splash_dtype out_dtype
                                    const splash_mask_info* info, const splash_mask_info* info_dkv,
                                    hipStream_t stream);
 
+/* ---- Softmax log-sum-exp and backward ----
+ *
+ * The pages give the softmax forward (study notes "JAX 到 VLIW ...", sections
+ * 12 and 15) and, for the pointwise variant, the custom_vjp pattern in which
+ * the forward hands the backward its residuals ("hstu_ops.py"). The softmax
+ * backward here is the gradient of the softmax definition with the
+ * forward's per-row log-sum-exp as the residual: with x = scale q·k,
+ *   LSE_q = log sum_k e^{x_qk} (allowed keys; -inf for a row with none),
+ *   P = e^{x - LSE} (0 where masked),  delta_q = dO_q · O_q,
+ *   dV = Pᵀ dO,  dS = P (dO Vᵀ - delta),  dQ = scale dS K,  dK = scale dSᵀ Q. */
+
+/* splash_gqa_fwd (softmax) that also writes lse[b * lse_strides[0] +
+ * h * lse_strides[1] + i] = LSE of row i (fp32, rows contiguous, caller
+ * owned, 4-byte aligned). Same arguments, checks and errors otherwise. */
+splash_status splash_fwd_lse(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads, int q_len,
+                             int kv_len, int head_dim,
+                             const void* q, const int64_t q_strides[3],
+                             const void* k, const int64_t k_strides[3],
+                             const void* v, const int64_t v_strides[3],
+                             void* o, const int64_t o_strides[3],
+                             float* lse, const int64_t lse_strides[2],
+                             float scale, const splash_mask_desc* mask, const splash_mask_info* info,
+                             hipStream_t stream);
+
+/* delta[b * delta_strides[0] + h * delta_strides[1] + i] = sum_d o[b,h,i,d] *
+ * d_o[b,h,i,d] in fp32, for o and d_o [B, H, q_len, head_dim] of `dtype`
+ * (strided as the forward's tensors). The caller owns delta (fp32,
+ * 4-byte aligned). Enqueued on `stream`. */
+splash_status splash_softmax_bwd_preprocess(splash_dtype dtype, int B, int H, int q_len, int head_dim,
+                                            const void* o, const int64_t o_strides[3],
+                                            const void* d_o, const int64_t do_strides[3],
+                                            float* delta, const int64_t delta_strides[2], hipStream_t stream);
+
+/* dq, dk, dv of softmax attention (splash_gqa_fwd) from q, k, v, d_o and the
+ * forward's lse and the preprocess's delta (both fp32, indexed as
+ * b * stat_strides[0] + h * stat_strides[1] + i). Everything else (dtypes,
+ * head_dim, kv_heads, the two metadata structs, block sizes, overwriting and
+ * errors) is as for splash_pointwise_bwd. */
+splash_status splash_softmax_bwd(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
+                                 int q_len, int kv_len, int head_dim,
+                                 const void* q, const int64_t q_strides[3],
+                                 const void* k, const int64_t k_strides[3],
+                                 const void* v, const int64_t v_strides[3],
+                                 const void* d_o, const int64_t do_strides[3],
+                                 const float* lse, const float* delta, const int64_t stat_strides[2],
+                                 void* dq, const int64_t dq_strides[3],
+                                 void* dk, const int64_t dk_strides[3],
+                                 void* dv, const int64_t dv_strides[3],
+                                 float scale, const splash_mask_desc* mask,
+                                 const splash_mask_info* info, const splash_mask_info* info_dkv,
+                                 hipStream_t stream);
+
 /* Static name of a status code. */
 const char* splash_status_string(splash_status s);
 /* Detail of the last failure on the calling thread ("" if none). */

@@ -215,3 +215,43 @@ def test_mask_info_build_dkv_validation_errors():
                                           None) == bd.SPLASH_ERR_INVALID_ARGUMENT
     assert lib.splash_mask_info_build_dkv(1, 1, 0, 256, 64, 64, ctypes.byref(d), ctypes.byref(_info(nq=0)),
                                           None) == bd.SPLASH_OK
+
+
+def test_softmax_entry_points_validation_errors():
+    """splash_fwd_lse, splash_softmax_bwd_preprocess and splash_softmax_bwd
+    reject bad arguments on the host (nothing is launched)."""
+    lib = bd.load_library()
+    d, keep = _desc()
+    row = _info(bq=64, bkv=64)
+    st = [bd._I64x3(4 * 256 * 128, 256 * 128, 128) for _ in range(8)]
+    ss = (ctypes.c_int64 * 2)(4 * 256, 256)
+
+    def fwd_lse(lse=0x900000, strides=ss, H=4, kv_heads=2):
+        return lib.splash_fwd_lse(1, 1, 1, H, kv_heads, 256, 256, 128, 0x100000, st[0], 0x200000, st[1],
+                                  0x300000, st[2], 0x400000, st[3], lse, strides, 0.1, ctypes.byref(d),
+                                  ctypes.byref(row), None)
+
+    assert fwd_lse(strides=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert fwd_lse(lse=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert fwd_lse(kv_heads=3) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert fwd_lse(strides=(ctypes.c_int64 * 2)(-1, 0)) == bd.SPLASH_ERR_INVALID_ARGUMENT
+
+    def pre(dtype=1, D=128, delta=0x900000, strides=ss):
+        return lib.splash_softmax_bwd_preprocess(dtype, 1, 4, 256, D, 0x100000, st[0], 0x200000, st[1], delta,
+                                                 strides, None)
+
+    assert pre(D=96) == bd.SPLASH_ERR_UNSUPPORTED
+    assert pre(dtype=7) == bd.SPLASH_ERR_UNSUPPORTED
+    assert pre(delta=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert pre(strides=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+
+    def bwd(lse=0x900000, delta=0xA00000, strides=ss, info_dkv=row):
+        return lib.splash_softmax_bwd(1, 1, 1, 4, 2, 256, 256, 128, 0x100000, st[0], 0x200000, st[1], 0x300000,
+                                      st[2], 0x400000, st[3], lse, delta, strides, 0x500000, st[4], 0x600000, st[5],
+                                      0x700000, st[6], 0.1, ctypes.byref(d), ctypes.byref(row),
+                                      ctypes.byref(info_dkv) if info_dkv else None, None)
+
+    assert bwd(strides=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert bwd(lse=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert bwd(delta=0xA00002) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert bwd(info_dkv=None) == bd.SPLASH_ERR_INVALID_ARGUMENT

@@ -1,5 +1,7 @@
-"""GPU parity of the pointwise backward: the HIP kernels through the C ABI
-against the fp64 oracle (``oracle.pointwise_attention_bwd``).
+"""GPU parity of the backwards: the HIP kernels through the C ABI against the
+fp64 oracle (``oracle.pointwise_attention_bwd``; ``oracle.softmax_lse`` and
+``oracle.softmax_attention_bwd`` for the softmax forward's log-sum-exp and
+the softmax backward).
 
 Small cases (several tiles, ragged tails, GQA, segment ids, every supported
 block size and dtype) compare dq, dk and dv element by element; the full-size
@@ -195,3 +197,106 @@ def test_pointwise_bwd_full_workload_sampled(gpu_device):
         ref["dv"].append(bv)
     for n in ("dq", "dk", "dv"):
         print(n, check_close(np.concatenate(got[n]), np.concatenate(ref[n]), "bf16", f"b5 {n}"))
+
+
+# ---------------------------------------------------------------------------
+# softmax: log-sum-exp, delta, backward
+# ---------------------------------------------------------------------------
+
+SM_CASES = [
+    # B, H, Hk, Sq, Skv, D, heads, (bq, bkv) row walk, (bq, bkv) column walk, segments, dtype, out dtype, layout
+    (2, 2, 2, 333, 333, 128, [CAUSAL, wl.local_causal(50)], (128, 128), (128, 128), None, "bf16", "bf16", "bhsd"),
+    (2, 2, 2, 333, 333, 64, [CAUSAL], (128, 128), (128, 128), "docs", "bf16", "bf16", "bhsd"),
+    (1, 4, 2, 300, 420, 128, [FULL, CAUSAL, wl.local_causal(40), (0, 30, 60)], (64, 128), (64, 64), "random",
+     "bf16", "f32", "bhsd"),
+    (1, 4, 1, 517, 517, 64, [CAUSAL], (256, 64), (256, 128), "docs", "bf16", "bf16", "bshd"),
+    (1, 2, 2, 200, 200, 64, [CAUSAL], (64, 64), (64, 64), "docs", "f32", "f32", "bhsd"),
+    (1, 2, 1, 130, 190, 128, [CAUSAL, (0, 20, 20)], (128, 128), (64, 64), "random", "f32", "f32", "bhsd"),
+]
+
+
+def _run_softmax(dev, case, c):
+    """Forward with log-sum-exp, delta, backward: (out, lse, delta, (dq, dk, dv))."""
+    B, H, Hk, Sq, Skv, D, heads, (bq, bkv), (cbq, cbkv), seg, dt, odt, layout = case
+    g = {n: (None if c[n] is None else c[n].to(dev)) for n in c}
+    info, info_dkv = _infos(dev, B, H, Sq, Skv, heads, bq, bkv, cbq, cbkv, g)
+    out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
+    if layout == "bshd":
+        q, k, v, do = (g[n].transpose(1, 2).contiguous() for n in ("q", "k", "v", "d_o"))
+    else:
+        q, k, v, do = g["q"], g["k"], g["v"], g["d_o"]
+    out, lse = sp.splash_fwd_lse(q, k, v, info, layout=layout)
+    delta = sp.softmax_bwd_preprocess(out, do, layout=layout)
+    grads = sp.softmax_bwd(q, k, v, do, lse, delta, info, info_dkv, out_dtype=out_dtype, layout=layout)
+    torch.cuda.synchronize()
+    if layout == "bshd":
+        out = out.transpose(1, 2)
+        grads = tuple(t.transpose(1, 2) for t in grads)
+    return out, lse, delta, grads
+
+
+@pytest.mark.parametrize("case", SM_CASES, ids=[f"s{n}" for n in range(len(SM_CASES))])
+def test_softmax_lse_and_bwd_small_match_oracle(gpu_device, case):
+    B, H, Hk, Sq, Skv, D, heads, _, _, seg, dt, odt, layout = case
+    print(f"softmax backward case {case}", flush=True)
+    c = _case(51, B, H, Hk, Sq, Skv, D, dt, seg)
+    out, lse, delta, (dq, dk, dv) = _run_softmax(gpu_device, case, c)
+    q64, k64, v64, do64 = (to64(c[n]) for n in ("q", "k", "v", "d_o"))
+    qs, ks = _seg(c, "q_segment_ids"), _seg(c, "kv_segment_ids")
+    scale = 1 / math.sqrt(D)
+    tol = "f32" if dt == "f32" else "bf16"
+    # log-sum-exp: rows with no allowed key are -inf on both sides
+    want = oracle.softmax_lse(q64, k64, scale, heads, qs, ks)
+    got = lse.cpu().double().numpy()
+    inf = np.isneginf(want)
+    assert (np.isneginf(got) == inf).all()
+    d = np.abs(got[~inf] - want[~inf]).max(initial=0.0)
+    assert d <= (2e-5 if dt == "f32" else 1e-2), d
+    # delta = rowsum(out * d_o) on the library's own output (exact up to fp32 sums)
+    dref = (to64(out) * do64).sum(-1)
+    assert np.abs(delta.cpu().double().numpy() - dref).max() <= 1e-5 * (1 + np.abs(dref).max())
+    ref = oracle.softmax_attention_bwd(q64, k64, v64, do64, scale, heads, qs, ks)
+    for name, g, w in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        print(name, check_close(to64(g), w, tol, f"softmax {name} {case}"))
+
+
+def test_softmax_bwd_full_workload_sampled(gpu_device):
+    """The softmax backward at the headline shape (B=2 H=32 S=8192 D=128,
+    causal, 128x128 blocks): sampled dq rows, and dk / dv rows of sampled
+    keys, the oracle summing their contributions over all query rows."""
+    w = wl.WORKLOADS["s3h"]
+    print("full softmax backward workload s3h", flush=True)
+    c = wl.generate(w)
+    g = {n: c[n].to(gpu_device) for n in ("q", "k", "v", "d_o")}
+    info = sp.mask_info_build(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, device=gpu_device)
+    info_dkv = sp.mask_info_build_dkv(w.B, w.H, w.S, w.S, w.head_masks, w.block_q, w.block_kv, device=gpu_device)
+    out, lse = sp.splash_fwd_lse(g["q"], g["k"], g["v"], info, scale=w.scale)
+    delta = sp.softmax_bwd_preprocess(out, g["d_o"])
+    dq, dk, dv = sp.softmax_bwd(g["q"], g["k"], g["v"], g["d_o"], lse, delta, info, info_dkv, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2000 + w.seed)
+    got = {"dq": [], "dk": [], "dv": []}
+    ref = {"dq": [], "dk": [], "dv": []}
+    for _ in range(2):
+        b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
+        q64, k64, v64, do64 = (to64(c[n][b, h]) for n in ("q", "k", "v", "d_o"))
+        rows = sorted({0, w.S - 1, 127, 128, *map(int, rng.integers(0, w.S, 5))})
+        m = oracle.element_mask(w.S, w.S, w.head_masks[0], rows=rows)
+        a, _, _ = oracle.softmax_attention_bwd_rows(q64[rows], k64, v64, do64[rows], w.scale, m)
+        got["dq"].append(to64(dq[b, h, rows]))
+        ref["dq"].append(a)
+        keys = sorted({0, w.S - 1, 128, *map(int, rng.integers(0, w.S, 5))})
+        dk_ref = np.zeros((len(keys), w.D))
+        dv_ref = np.zeros((len(keys), w.D))
+        for r0 in range(0, w.S, 1024):
+            rr = np.arange(r0, r0 + 1024)
+            m = oracle.element_mask(w.S, w.S, w.head_masks[0], rows=rr)
+            _, bk, bv = oracle.softmax_attention_bwd_rows(q64[rr], k64, v64, do64[rr], w.scale, m)
+            dk_ref += bk[keys]
+            dv_ref += bv[keys]
+        got["dk"].append(to64(dk[b, h, keys]))
+        ref["dk"].append(dk_ref)
+        got["dv"].append(to64(dv[b, h, keys]))
+        ref["dv"].append(dv_ref)
+    for n in ("dq", "dk", "dv"):
+        print(n, check_close(np.concatenate(got[n]), np.concatenate(ref[n]), "bf16", f"s3h {n}"))
