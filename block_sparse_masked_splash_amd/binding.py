@@ -195,6 +195,8 @@ class MaskInfo:
     # blocks, int32 [num_blocks, block_q, block_kv // 32] (bits, see splash.h)
     mask_next: torch.Tensor | None = None
     mask_blocks: torch.Tensor | None = None
+    # dK/dV metadata: block_mask and data_next are [meta_batch, meta_heads, nk, nq]
+    columns: bool = False
 
     @property
     def dense(self) -> bool:
@@ -214,6 +216,8 @@ class MaskInfo:
 
     def info_struct(self):
         Bm, Hm, nq, nk = self.block_mask.shape
+        if self.columns:
+            nq, nk = nk, nq
         return MaskInfoC(Bm, Hm, nq, nk, self.block_q, self.block_kv,
                          self.block_mask.data_ptr() if self.block_mask.numel() else None,
                          self.data_next.data_ptr() if self.data_next.numel() else None)
@@ -284,8 +288,9 @@ def mask_info_build(B: int, H: int, q_len: int, kv_len: int, head_masks, block_q
 def mask_info_build_dkv(B: int, H: int, q_len: int, kv_len: int, head_masks, block_q: int = 128,
                         block_kv: int = 128, q_segment_ids=None, kv_segment_ids=None,
                         device="cuda", out: MaskInfo | None = None) -> MaskInfo:
-    """Metadata of the backward's dK/dV pass: the same block classes, with
-    ``data_next`` walking each kv-block column over q blocks."""
+    """Metadata of the backward's dK/dV pass, stored by columns: block_mask
+    and data_next are [meta_batch, meta_heads, nk, nq]; the same block
+    classes, with ``data_next`` walking each kv-block column over q blocks."""
     return _mask_info(True, B, H, q_len, kv_len, head_masks, block_q, block_kv, q_segment_ids, kv_segment_ids,
                       device, out)
 
@@ -302,7 +307,7 @@ def _mask_info(dkv: bool, B, H, q_len, kv_len, head_masks, block_q, block_kv, q_
     Bm = B if q_segment_ids is not None else 1
     nq = -(-q_len // block_q) if block_q > 0 else 0
     nk = -(-kv_len // block_kv) if block_kv > 0 else 0
-    shape = (Bm, len(head_masks), nq, nk)
+    shape = (Bm, len(head_masks), nk, nq) if dkv else (Bm, len(head_masks), nq, nk)
     if out is not None and tuple(out.block_mask.shape) == shape:
         bmask, dnext = out.block_mask, out.data_next
     else:
@@ -311,7 +316,7 @@ def _mask_info(dkv: bool, B, H, q_len, kv_len, head_masks, block_q, block_kv, q_
         bmask = torch.empty((n + 3) // 4 * 4, dtype=torch.int8, device=device)[:n].view(shape)
         dnext = torch.empty(shape, dtype=torch.int32, device=device)
     info = MaskInfo(B, H, q_len, kv_len, block_q, block_kv, head_masks, q_segment_ids, kv_segment_ids,
-                    bmask, dnext)
+                    bmask, dnext, columns=dkv)
     desc, keep = info.mask_desc()
     cinfo = info.info_struct()
     fn = lib.splash_mask_info_build_dkv if dkv else lib.splash_mask_info_build
@@ -452,6 +457,8 @@ def _backward(softmax: bool, q, k, v, d_o, info, info_dkv, scale, out_dtype, lay
                               + (" (dense masks)" if m.dense else ""))
     if info.head_masks != info_dkv.head_masks:
         raise ValueError("info and info_dkv were built for different masks")
+    if info.columns or not info_dkv.columns:
+        raise ValueError("info must come from mask_info_build and info_dkv from mask_info_build_dkv")
     desc, keep = info.mask_desc()
     c1, c2 = info.info_struct(), info_dkv.info_struct()
     head = (_DT[q.dtype], _DT[out_dtype], B, H, Hk, Sq, Skv, D,

@@ -511,6 +511,7 @@ splash_status mask_info_common(bool dkv, int B, int H, int q_len, int kv_len, in
   p.kv_seg = mask->kv_segment_ids;
   p.block_mask = info->block_mask;
   p.data_next = info->data_next;
+  p.columns = dkv ? 1 : 0;
   return dkv ? hip_status(splash::launch_mask_info_dkv(p, stream), "splash_mask_info_build_dkv launch")
              : hip_status(splash::launch_mask_info(p, stream), "splash_mask_info_build launch");
 }

@@ -33,6 +33,10 @@ struct MaskInfoParams {
   const int32_t* kv_seg;  // [B, kv_len] or null
   int8_t* block_mask;
   int32_t* data_next;
+  // 0: [meta_batch, meta_heads, nq, nk] (rows of kv blocks, the forward's
+  // walk); 1: [meta_batch, meta_heads, nk, nq] (columns of q blocks, the
+  // dK/dV walk), data_next then running along q blocks
+  int columns;
   HeadBand band[SPLASH_MAX_MASK_HEADS];
 };
 
@@ -98,7 +102,7 @@ struct BwdParams {
   int block_q, block_kv, nq, nk, meta_heads;
   const int8_t* block_mask;
   const int32_t* data_next;
-  // column walk (dK, dV): [meta_batch, c_meta_heads, c_nq, c_nk]
+  // column walk (dK, dV): [meta_batch, c_meta_heads, c_nk, c_nq] (columns contiguous)
   int c_block_q, c_block_kv, c_nq, c_nk, c_meta_heads;
   const int8_t* c_block_mask;
   const int32_t* c_data_next;
@@ -126,7 +130,8 @@ struct DeltaParams {
 
 // Launchers; return the launch error (hipSuccess when enqueued).
 hipError_t launch_mask_info(const MaskInfoParams& p, hipStream_t stream);
-// Same classes, data_next along the q blocks of each kv-block column.
+// Same classes in the column layout (p.columns = 1), data_next along the q
+// blocks of each kv-block column.
 hipError_t launch_mask_info_dkv(const MaskInfoParams& p, hipStream_t stream);
 // bf16 inputs, matrix-core path. out_f32 selects an fp32 output.
 hipError_t launch_fwd_bf16(const FwdParams& p, bool pointwise, bool out_f32, hipStream_t stream);

@@ -23,8 +23,9 @@
 // The dK/dV pass of the pointwise backward walks columns instead ("hstu_ops.py",
 // _pointwise_splash_attention_bwd_kernel: grid over kv blocks, then heads,
 // then q steps; _next_nonzero(next_i=True) reads data_next[h, i, j] as the
-// q block to fetch). Its metadata has the same classes, and data_next[.., i, j]
-// is the first non-empty q block at or after i in column j (nq if none).
+// q block to fetch). Its metadata has the same classes, and data_next of
+// (i, j) is the first non-empty q block at or after i in column j (nq if
+// none); it is stored by columns, [meta_batch, meta_heads, nk, nq].
 
 #include "internal.h"
 
@@ -95,11 +96,13 @@ __global__ __launch_bounds__(kSegThreads) void segment_class_kernel(MaskInfoPara
   __shared__ int32_t red[4][kSegThreads / 64];  // per wave: q min, q max, k min, k max
   const int t = threadIdx.x;
   const int wv = t >> 6;
-  for (int64_t e = blockIdx.x; e < entries; e += gridDim.x) {
-    const int64_t row = e / p.nk;
-    const int j = (int)(e - row * p.nk);
+  for (int64_t e0 = blockIdx.x; e0 < entries; e0 += gridDim.x) {
+    const int64_t row = e0 / p.nk;
+    const int j = (int)(e0 - row * p.nk);
     int bm, hm, i;
     decode_row(p, row, bm, hm, i);
+    // where this entry's class goes: row layout e0, column layout its transpose
+    const int64_t e = p.columns ? (((int64_t)bm * p.meta_heads + hm) * p.nk + j) * p.nq + i : e0;
     const HeadBand hb = p.band[hm];
     const BlockSpan s = block_span(p, i, j);
     const int base = band_class(s, hb);
@@ -208,25 +211,38 @@ __global__ __launch_bounds__(256) void row_scan_kernel(MaskInfoParams p) {
   }
 }
 
-// Column walk of the dK/dV pass: one wavefront per (metadata batch, head,
-// kv block) column, the same back-to-front ballot scan over its q blocks.
+// Column walk of the dK/dV pass, in the column layout: one wavefront per
+// (metadata batch, head, kv block) column, with the classes (closed form, or
+// read back from the segment pass) and the same back-to-front ballot scan
+// over its q blocks. A column's entries are contiguous, so the dK/dV kernel's
+// walk reads consecutive metadata, as the forward's does along a row.
+template <bool kFromSegments>
 __global__ __launch_bounds__(256) void column_scan_kernel(MaskInfoParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t col = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t cols = (int64_t)p.meta_batch * p.meta_heads * p.nk;
   if (col >= cols) return;
   const int j = (int)(col % p.nk);
-  const int64_t plane = col / p.nk;  // (bm, hm)
-  const int8_t* bmask = p.block_mask + plane * p.nq * p.nk + j;
-  int32_t* dnext = p.data_next + plane * p.nq * p.nk + j;
+  const int hm = (int)((col / p.nk) % p.meta_heads);
+  const HeadBand hb = p.band[hm];
+  int8_t* bmask = p.block_mask + col * p.nq;
+  int32_t* dnext = p.data_next + col * p.nq;
   int carry = p.nq;
   const int nchunks = (p.nq + 63) / 64;
   for (int c = nchunks - 1; c >= 0; --c) {
     const int i = c * 64 + lane;
-    const int cls = i < p.nq ? bmask[(int64_t)i * p.nk] : 0;
+    int cls = 0;
+    if (i < p.nq) {
+      if constexpr (kFromSegments) {
+        cls = bmask[i];
+      } else {
+        cls = band_class(block_span(p, i, j), hb);
+        bmask[i] = (int8_t)cls;
+      }
+    }
     const uint64_t bits = __ballot(cls != 0);
     const uint64_t at_or_after = bits >> lane;
-    if (i < p.nq) dnext[(int64_t)i * p.nk] = at_or_after ? i + __builtin_ctzll(at_or_after) : carry;
+    if (i < p.nq) dnext[i] = at_or_after ? i + __builtin_ctzll(at_or_after) : carry;
     if (bits) carry = c * 64 + __builtin_ctzll(bits);
   }
 }
@@ -234,12 +250,19 @@ __global__ __launch_bounds__(256) void column_scan_kernel(MaskInfoParams p) {
 }  // namespace
 
 hipError_t launch_mask_info_dkv(const MaskInfoParams& p, hipStream_t stream) {
-  // classes (and a row scan whose data_next the column scan then replaces)
-  hipError_t e = launch_mask_info(p, stream);
-  if (e != hipSuccess) return e;
   const int64_t cols = (int64_t)p.meta_batch * p.meta_heads * p.nk;
   if (cols == 0 || p.nq == 0) return hipSuccess;
-  hipLaunchKernelGGL(column_scan_kernel, dim3((unsigned)((cols + 3) / 4)), dim3(256), 0, stream, p);
+  const int64_t blocks = (cols + 3) / 4;
+  if (p.q_seg != nullptr) {
+    const int64_t entries = cols * p.nq;
+    const int64_t grid = entries < (1 << 20) ? entries : (1 << 20);
+    hipLaunchKernelGGL(segment_class_kernel, dim3((unsigned)grid), dim3(kSegThreads), 0, stream, p, entries);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(column_scan_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(column_scan_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -167,10 +167,11 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
   tile_copy_offsets<D, NW>(lane, wave, do_rs, dsel);
 
   // ---- column walk over (query head of the group, q block, 32-query tile) ----
+  // the dK/dV metadata is stored by columns: column (g, j) is c_nq entries
   auto entry = [&](int g, int i) -> int64_t {
     const int h = hk * G + g;
     const int hm = p.c_meta_heads == 1 ? 0 : h;
-    return (((int64_t)bm * p.c_meta_heads + hm) * p.c_nq + i) * p.c_nk + j;
+    return (((int64_t)bm * p.c_meta_heads + hm) * p.c_nk + j) * p.c_nq + i;
   };
   // data_next is only followed forward and within [0, nq], so any metadata
   // content ends the walk in bounds.
@@ -192,7 +193,7 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
   };
   auto class_of = [&](int g, int i) {
     const int64_t e = entry(g, i);
-    return block_class(p.c_block_mask + (e - j), j);
+    return block_class(p.c_block_mask + (e - i), i);
   };
 
   auto issue_tile = [&](int stage, int g, int i, int t) {
@@ -398,6 +399,375 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
                      dk[db][4 * g + 3] * ck);
         store4<OutT>(dvr + col, dv[db][4 * g] * cv, dv[db][4 * g + 1] * cv, dv[db][4 * g + 2] * cv,
                      dv[db][4 * g + 3] * cv);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV with paired wavefronts
+// ---------------------------------------------------------------------------
+//
+// At D = 128 one wavefront holding K, V, dK and dV needs about 295 registers,
+// so only one fits a SIMD. Here each 32-key group is split over two
+// wavefronts:
+//   role 0 holds K, forms S = Q Kᵀ, the weights (P for dV and the factor g
+//          that turns dP into dS), and accumulates dVᵀ += dOᵀ P;
+//   role 1 holds V, forms dP = dO Vᵀ, takes g from role 0 through LDS, forms
+//          dS = dP g (pointwise) or g (dP - delta) (softmax, g = P), and
+//          accumulates dKᵀ += Qᵀ dS.
+// Same products as the single-wavefront kernel at about 190 registers per
+// wavefront. A workgroup has NG key groups (2 NG wavefronts, 32 NG keys);
+// kv blocks wider than that are split over several workgroups. With NG = 2
+// two workgroups share a CU, and the roles of a workgroup's wavefront pairs
+// swap with the parity of its id, so that each SIMD runs the exponentials of
+// one role beside the matrix work of the other. One extra workgroup barrier
+// per tile orders the exchange.
+
+template <int D, int NG>
+struct PairTiling {
+  static constexpr int NW = 2 * NG;               // wavefronts
+  static constexpr int KEYS = 32 * NG;            // keys per workgroup
+  static constexpr int QC = 32;                   // queries per LDS tile
+  static constexpr int ROWB = D * 2;
+  static constexpr int RPI = 64 / (D / 8);        // rows per direct-copy instruction
+  static constexpr int TILE = QC * ROWB;
+  static constexpr int CW = (QC / RPI) < NW ? (QC / RPI) : NW;  // wavefronts that copy tiles
+  static constexpr int LOADS = (QC / RPI) / CW;   // copies per copying wave per matrix per tile
+  static constexpr int SEG_ROWS = QC / NW;        // ids (and stats) copied per wave per tile
+  static constexpr int NS = D / 16;
+  static constexpr int ND = D / 32;
+  static constexpr int ST = 3;                    // LDS stages: two tiles in flight beside the one in use
+  static constexpr int SEG_OFF = ST * 2 * TILE;   // [stage][Q | dO][TILE], then [stage][QC] ids
+  static constexpr int STAT_OFF = SEG_OFF + ST * QC * 4;      // softmax: [stage][LSE | delta][QC]
+  static constexpr int X_OFF = STAT_OFF + ST * 2 * QC * 4;    // exchange: [NG][4][64 lanes][16 B]
+  static constexpr int LDS_BYTES = X_OFF + NG * 4096;
+  static_assert(LOADS >= 1 && SEG_ROWS >= 1, "tile too small for the workgroup");
+  static_assert(CW == NW, "every wavefront copies tile rows (fixed copies per wave and tile)");
+};
+
+template <int D, int NG, bool SM, typename OutT>
+__global__ __launch_bounds__(2 * NG * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
+  using T = PairTiling<D, NG>;
+  constexpr int NW = T::NW;
+  constexpr int NS = T::NS;
+  constexpr int ND = T::ND;
+  constexpr int QC = T::QC;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+
+  const int sub = p.c_block_kv / T::KEYS;  // workgroups per kv block
+  int unit, rest;
+  if (!work_item(p.c_nk * sub, total_work, work_per_xcd, units_interleaved, unit, rest)) return;
+  const int j = rest / sub;
+  const int part = rest - j * sub;
+  const int b = unit / p.kv_heads;
+  const int hk = unit - b * p.kv_heads;
+  const int bm = p.meta_batch == 1 ? 0 : b;
+  const int G = p.kv_group;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // 0: S, P, dV; 1: dP, dS, dK (wave-uniform). With NG = 4 the pair (w, w + 4)
+  // shares a SIMD; with NG = 2 the pairs alternate with the workgroup parity.
+  const int role = NG == 4 ? wave / NG : ((wave / NG) ^ (int)(blockIdx.x & 1));
+  const int kg = wave % NG;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int key = j * p.c_block_kv + part * T::KEYS + kg * 32 + l32;
+  const bool kvalid = key < p.kv_len;
+  const bool has_seg = p.q_seg != nullptr;
+
+  // ---- this lane's key row: K (role 0) or V (role 1) as the B operand ----
+  bf16x8 breg[NS];
+  {
+    const __bf16* src = role == 0
+        ? reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh + (int64_t)key * p.k_ss
+        : reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh + (int64_t)key * p.v_ss;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      i16x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (kvalid) a = *reinterpret_cast<const i16x8*>(src + 16 * s + 8 * hh);
+      breg[s] = __builtin_bit_cast(bf16x8, a);
+    }
+  }
+  const int32_t kseg = (has_seg && kvalid) ? p.kv_seg[(int64_t)b * p.kv_len + key] : 0;
+
+  // LDS offsets with the role's tile folded in: role 0 reads Q rows and dO
+  // transposed, role 1 dO rows and Q transposed (dO sits TILE bytes after Q)
+  int aoff[NS];
+  row_operand_offsets<D>(lane, aoff);
+  int toff[2][ND];
+  transpose_operand_offsets<D>(lane, toff);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) aoff[s] += role == 0 ? 0 : T::TILE;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int db = 0; db < ND; ++db) toff[hf][db] += role == 0 ? T::TILE : 0;
+  const int64_t q_rs = p.q_ss * 2, do_rs = p.do_ss * 2;
+  uint32_t qsel[T::LOADS], dsel[T::LOADS];
+  tile_copy_offsets<D, T::CW>(lane, wave, q_rs, qsel);
+  tile_copy_offsets<D, T::CW>(lane, wave, do_rs, dsel);
+
+  // the dK/dV metadata is stored by columns: column (g, j) is c_nq entries
+  auto entry = [&](int g, int i) -> int64_t {
+    const int h = hk * G + g;
+    const int hm = p.c_meta_heads == 1 ? 0 : h;
+    return (((int64_t)bm * p.c_meta_heads + hm) * p.c_nk + j) * p.c_nq + i;
+  };
+  auto first_i = [&](int g) {
+    if (p.c_nq == 0) return p.c_nq;
+    const int i = scalar_load_i32(p.c_data_next + entry(g, 0));
+    return (i >= 0 && i <= p.c_nq) ? i : p.c_nq;
+  };
+  auto next_i = [&](int g, int i) {
+    const int in = (i + 1 < p.c_nq) ? scalar_load_i32(p.c_data_next + entry(g, i + 1)) : p.c_nq;
+    return (in > i && in <= p.c_nq) ? in : p.c_nq;
+  };
+  auto settle = [&](int& g, int& i) {
+    while (i >= p.c_nq) {
+      if (++g >= G) return;
+      i = first_i(g);
+    }
+  };
+  auto class_of = [&](int g, int i) {
+    const int64_t e = entry(g, i);
+    return block_class(p.c_block_mask + (e - i), i);
+  };
+
+  // Per tile each wave issues 2 LOADS row copies, plus one id copy (segment
+  // ids) and two stat copies (softmax): the fixed count the pipeline waits by.
+  auto issue_tile = [&](int stage, int g, int i, int t) {
+    const int h = hk * G + g;
+    const int q0 = i * p.c_block_q + t;
+    const int rows = p.q_len - q0 < QC ? p.q_len - q0 : QC;  // rows past the end read as 0
+    {
+      const char* qg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh);
+      const char* dg =
+          reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.d_o) + b * p.do_sb + h * p.do_sh);
+      char* qdst = smem + stage * 2 * T::TILE;
+      char* ddst = qdst + T::TILE;
+      const u32x4 qrs = buffer_rsrc(qg + q0 * q_rs, (uint32_t)(rows * q_rs));
+      const u32x4 drs = buffer_rsrc(dg + q0 * do_rs, (uint32_t)(rows * do_rs));
+      lds_copy_rows<T::LOADS, T::CW * 1024>(qrs, qsel, (uint32_t)(wave * T::RPI * q_rs),
+                                            (uint32_t)(T::CW * T::RPI * q_rs), lds_addr(qdst + wave * T::RPI * T::ROWB));
+      lds_copy_rows<T::LOADS, T::CW * 1024>(drs, dsel, (uint32_t)(wave * T::RPI * do_rs),
+                                            (uint32_t)(T::CW * T::RPI * do_rs),
+                                            lds_addr(ddst + wave * T::RPI * T::ROWB));
+    }
+    if (has_seg) {
+      const uint32_t sdst =
+          lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * QC + wave * T::SEG_ROWS);
+      const u32x4 srs = buffer_rsrc(p.q_seg + (int64_t)b * p.q_len + q0, (uint32_t)(rows * 4));
+      if (lane < T::SEG_ROWS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), sdst);
+    }
+    if constexpr (SM) {
+      float* st = reinterpret_cast<float*>(smem + T::STAT_OFF) + stage * 2 * QC + wave * T::SEG_ROWS;
+      const int64_t off = b * p.st_sb + h * p.st_sh + q0;
+      const u32x4 lrs = buffer_rsrc(p.lse + off, (uint32_t)(rows * 4));
+      const u32x4 drs2 = buffer_rsrc(p.delta + off, (uint32_t)(rows * 4));
+      if (lane < T::SEG_ROWS) {
+        lds_copy4(lrs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st));
+        lds_copy4(drs2, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st + QC));
+      }
+    }
+  };
+
+  for (int o = tid * 16; o < T::SEG_OFF; o += NW * 64 * 16)
+    *reinterpret_cast<uint4*>(smem + o) = uint4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  f32x16 acc[ND];  // role 0: dVᵀ, role 1: dKᵀ
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  const float nl = -p.scale * 1.4426950408889634f;
+  const float cl = p.scale * 1.4426950408889634f;
+  constexpr float kMasked = SM ? -__builtin_inff() : kMaskedT;
+  f32x4* xg = reinterpret_cast<f32x4*>(smem + T::X_OFF + kg * 4096) + lane;  // this lane's exchange slots
+
+  auto advance = [&](int g, int i, int t, int& ng, int& ni, int& nt) {  // the tile after (g, i, t)
+    ng = g;
+    ni = i;
+    nt = t + QC;
+    if (nt >= p.c_block_q || ni * p.c_block_q + nt >= p.q_len) {
+      ni = next_i(ng, ni);
+      nt = 0;
+      settle(ng, ni);
+    }
+  };
+  // The pipeline: tile cur is used from LDS while tile nxt is in flight; the
+  // tile after it is issued at the start of each step.
+  int cur_g = 0, cur_i = first_i(0), cur_t = 0;
+  settle(cur_g, cur_i);
+  int nxt_g = G, nxt_i = 0, nxt_t = 0;
+  if (cur_g < G) {
+    issue_tile(0, cur_g, cur_i, 0);
+    advance(cur_g, cur_i, 0, nxt_g, nxt_i, nxt_t);
+    if (nxt_g < G) issue_tile(1, nxt_g, nxt_i, nxt_t);
+  }
+
+  auto step = [&](auto stage_tag) -> bool {
+    constexpr int stage = decltype(stage_tag)::value;
+    int nn_g = G, nn_i = 0, nn_t = 0;
+    if (nxt_g < G) advance(nxt_g, nxt_i, nxt_t, nn_g, nn_i, nn_t);
+    // this wave's copies of the current tile are in LDS; the next tile's
+    // (2 LOADS + segment ids + softmax stats) may still be in flight
+    if (nxt_g < G) {
+      if (has_seg)
+        wait_vmcnt<2 * T::LOADS + (SM ? 2 : 0) + 1>();
+      else
+        wait_vmcnt<2 * T::LOADS + (SM ? 2 : 0)>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_only();   // everyone's are; the stage two tiles back and the exchange are free again
+    if (nn_g < G) issue_tile((stage + 2) % 3, nn_g, nn_i, nn_t);
+
+    const char* tb = smem + stage * 2 * T::TILE;  // Q tile, then dO tile
+    const float* sst = reinterpret_cast<const float*>(smem + T::STAT_OFF) + stage * 2 * QC;
+
+    // S = Q Kᵀ (role 0) or dP = dO Vᵀ (role 1): 32 queries (rows) x 32 keys
+    f32x16 c;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(tb + aoff[s]);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, breg[s], c, 0, 0, 0);
+    }
+
+    bf16x8 wb[2];  // role 0: P, role 1: dS (B operands)
+    if (role == 0) {
+      // element r: query q0 + 8 (r / 4) + 4 hh + r % 4, key `key`
+      f32x16& t = c;
+      if constexpr (SM) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(sst + 8 * u + 4 * hh);
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) t[4 * u + v4] = __builtin_fmaf(c[4 * u + v4], cl, -kLog2e * l4[v4]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = c[r] * nl;
+      }
+      if (class_of(cur_g, cur_i) == 1) {
+        const int h = hk * G + cur_g;
+        const HeadBand band = p.band[p.band_heads == 1 ? 0 : h];
+        const int q0 = cur_i * p.c_block_q + cur_t;
+        int a = key - band.hi - q0;
+        int e = key - band.lo - q0;
+        a = a > 0 ? a : 0;
+        e = e < p.q_len - 1 - q0 ? e : p.q_len - 1 - q0;
+        e = e < QC - 1 ? e : QC - 1;
+        if (e < a || !kvalid) a = e = QC;
+        const uint32_t width = (uint32_t)(e - a);
+        const int base = 4 * hh - a;
+        if (has_seg) {
+          const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * QC;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int4 qs4 = *reinterpret_cast<const int4*>(sseg + 8 * u + 4 * hh);
+            const int ids[4] = {qs4.x, qs4.y, qs4.z, qs4.w};
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+              const bool ok = ((uint32_t)(base + 8 * u + v4) <= width) & (ids[v4] == kseg);
+              t[4 * u + v4] = ok ? t[4 * u + v4] : kMasked;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) t[r] = ((uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width) ? t[r] : kMasked;
+        }
+      }
+      // P for dV, g for role 1 (in place of t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr, g;
+        if constexpr (SM) {
+          pr = __builtin_amdgcn_exp2f(t[r]);
+          g = pr;
+        } else {
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t[r]));
+          pr = t[r] * sg;
+          g = __builtin_fmaf(pr, __builtin_fmaf(sg, kLn2, -kLn2), sg);
+        }
+        wb[r >> 3][r & 7] = (__bf16)pr;
+        t[r] = g;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) xg[64 * u] = f32x4{t[4 * u], t[4 * u + 1], t[4 * u + 2], t[4 * u + 3]};
+    }
+    barrier_only();  // g of every key group is in LDS (the next tile's copies stay in flight)
+    if (role == 1) {
+      if constexpr (SM) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 g4 = xg[64 * u];
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(sst + QC + 8 * u + 4 * hh);
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int r = 4 * u + v4;
+            wb[r >> 3][r & 7] = (__bf16)(g4[v4] * (c[r] - d4[v4]));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 g4 = xg[64 * u];
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int r = 4 * u + v4;
+            wb[r >> 3][r & 7] = (__bf16)(c[r] * g4[v4]);
+          }
+        }
+      }
+    }
+
+    // role 0: dVᵀ += dOᵀ P; role 1: dKᵀ += Qᵀ dS (toff carries the role's tile)
+#pragma unroll
+    for (int g2 = 0; g2 < 2; ++g2) {
+      const int rowbase = 16 * g2 * T::ROWB;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tb + rowbase + toff[0][db]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tb + rowbase + toff[1][db]));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wb[g2], acc[db], 0, 0, 0);
+      }
+    }
+
+    cur_g = nxt_g;
+    cur_i = nxt_i;
+    cur_t = nxt_t;
+    nxt_g = nn_g;
+    nxt_i = nn_i;
+    nxt_t = nn_t;
+    return cur_g < G;
+  };
+  while (cur_g < G) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
+    if (!step(std::integral_constant<int, 2>{})) break;
+  }
+
+  // role 0 stores dV, role 1 dK (factors as in the single-wavefront kernel)
+  if (kvalid) {
+    const float cf = role == 0 ? (SM ? 1.0f : -kLn2 * p.inv_q_len) : (SM ? p.scale : p.scale * p.inv_q_len);
+    OutT* dst = role == 0
+        ? reinterpret_cast<OutT*>(p.dv) + b * p.dv_sb + hk * p.dv_sh + (int64_t)key * p.dv_ss
+        : reinterpret_cast<OutT*>(p.dk) + b * p.dk_sb + hk * p.dk_sh + (int64_t)key * p.dk_ss;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * hh;
+        store4<OutT>(dst + col, acc[db][4 * g] * cf, acc[db][4 * g + 1] * cf, acc[db][4 * g + 2] * cf,
+                     acc[db][4 * g + 3] * cf);
       }
   }
 }
@@ -679,9 +1049,24 @@ hipError_t launch_dq(const BwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, int NG, bool SM, typename OutT>
+hipError_t launch_dkv_pair(const BwdParams& p, hipStream_t stream) {
+  const Order o = order_for((int64_t)p.B * p.kv_heads, (int64_t)p.c_nk * (p.c_block_kv / (32 * NG)));
+  if (o.total == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_dkv_pair_bf16_kernel<D, NG, SM, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(2 * NG * 64),
+                     0, stream, p, (int)o.total, (int)o.per_xcd, o.interleaved);
+  return hipGetLastError();
+}
+
 template <int D, bool SM, typename OutT>
 hipError_t launch_sm(const BwdParams& p, hipStream_t stream) {
-  hipError_t e = p.c_block_kv == 64 ? launch_dkv<D, 2, SM, OutT>(p, stream) : launch_dkv<D, 4, SM, OutT>(p, stream);
+  hipError_t e;
+  if constexpr (D == 128) {
+    // paired wavefronts: K, V, dK and dV do not fit one wavefront twice per SIMD
+    e = launch_dkv_pair<D, 2, SM, OutT>(p, stream);
+  } else {
+    e = p.c_block_kv == 64 ? launch_dkv<D, 2, SM, OutT>(p, stream) : launch_dkv<D, 4, SM, OutT>(p, stream);
+  }
   if (e != hipSuccess) return e;
   if (p.block_q == 64) return launch_dq<D, 2, SM, OutT>(p, stream);
   if (p.block_q == 256) return launch_dq<D, 8, SM, OutT>(p, stream);

@@ -68,14 +68,15 @@ __global__ __launch_bounds__(BKV*(D / 32)) void bwd_dkv_f32_kernel(BwdParams p) 
     const int h = hk * p.kv_group + g;
     const int hm = p.c_meta_heads == 1 ? 0 : h;
     const HeadBand band = p.band[p.band_heads == 1 ? 0 : h];
-    const int64_t plane = ((int64_t)bm * p.c_meta_heads + hm) * p.c_nq;
+    // the dK/dV metadata is stored by columns: this column's c_nq entries
+    const int64_t col = (((int64_t)bm * p.c_meta_heads + hm) * p.c_nk + j) * p.c_nq;
     const float* qg = reinterpret_cast<const float*>(p.q) + b * p.q_sb + h * p.q_sh;
     const float* og = reinterpret_cast<const float*>(p.d_o) + b * p.do_sb + h * p.do_sh;
     // data_next only moves forward within [0, nq]
-    int i = p.c_nq > 0 ? p.c_data_next[plane * p.c_nk + j] : p.c_nq;
+    int i = p.c_nq > 0 ? p.c_data_next[col] : p.c_nq;
     if (i < 0 || i > p.c_nq) i = p.c_nq;
     while (i < p.c_nq) {
-      const bool partial = p.c_block_mask[(plane + i) * p.c_nk + j] == 1;
+      const bool partial = p.c_block_mask[col + i] == 1;
       for (int t = 0; t < p.c_block_q; t += TT) {
         const int q0 = i * p.c_block_q + t;
         if (q0 >= p.q_len) break;
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(BKV*(D / 32)) void bwd_dkv_f32_kernel(BwdParams p) 
           }
         }
       }
-      const int in = (i + 1 < p.c_nq) ? p.c_data_next[(plane + i + 1) * p.c_nk + j] : p.c_nq;
+      const int in = (i + 1 < p.c_nq) ? p.c_data_next[col + i + 1] : p.c_nq;
       i = (in > i && in <= p.c_nq) ? in : p.c_nq;
     }
   }

@@ -259,12 +259,15 @@ splash_status splash_masked_fwd(int pointwise, splash_dtype in_dtype, splash_dty
  * and dV over the column walk that the page's dK/dV grid uses (metadata of
  * splash_mask_info_build_dkv, possibly with other block sizes). */
 
-/* Metadata of the dK/dV pass: block_mask exactly as splash_mask_info_build
- * gives it for the same arguments, and data_next[.., i, j] = the first q
- * block i' >= i of kv-block column j whose class is not 0, else nq
+/* Metadata of the dK/dV pass, stored by columns: both arrays are
+ * [meta_batch, meta_heads, nk, nq] (info's num_q_blocks and num_kv_blocks
+ * still give nq and nk). block_mask[.., j, i] is the class that
+ * splash_mask_info_build gives block (i, j), and data_next[.., j, i] = the
+ * first q block i' >= i of kv-block column j whose class is not 0, else nq
  * (_next_nonzero with next_i=True reads data_next[h, i, j] as the q block to
- * fetch). Same arguments, checks, shapes and errors as
- * splash_mask_info_build; enqueued on `stream`. */
+ * fetch; the column layout keeps each column's walk in consecutive memory).
+ * Same arguments, checks and errors as splash_mask_info_build; enqueued on
+ * `stream`. */
 splash_status splash_mask_info_build_dkv(int B, int H, int q_len, int kv_len, int block_q, int block_kv,
                                          const splash_mask_desc* mask, const splash_mask_info* info,
                                          hipStream_t stream);

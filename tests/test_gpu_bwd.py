@@ -66,8 +66,9 @@ def test_dkv_metadata_matches_oracle(gpu_device, case):
                                   device=gpu_device)
     torch.cuda.synchronize()
     bm, dn = oracle.mask_info_dkv(B, H, Sq, Skv, bq, bkv, heads, _seg(c, "q_segment_ids"), _seg(c, "kv_segment_ids"))
-    np.testing.assert_array_equal(info.block_mask.cpu().numpy(), bm)
-    np.testing.assert_array_equal(info.data_next.cpu().numpy(), dn)
+    # stored by columns: [Bm, Hm, nk, nq]
+    np.testing.assert_array_equal(info.block_mask.cpu().numpy(), bm.transpose(0, 1, 3, 2))
+    np.testing.assert_array_equal(info.data_next.cpu().numpy(), dn.transpose(0, 1, 3, 2))
 
 
 BWD_CASES = [
