@@ -39,10 +39,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"splash_fwd_{workload}_traffic.json")
+def traffic_for(workload: str, backward: bool = False):
+    """HBM bytes per timed call from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"splash_{'bwd' if backward else 'fwd'}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -277,7 +277,7 @@ def main():
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma" if not in_f32 else "alu", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_for(w.name), "kernel_source_sha256_16": kernel_source_hash()},
+                     "traffic": traffic_for(w.name, w.backward), "kernel_source_sha256_16": kernel_source_hash()},
     }
     if not args.no_gemm_reference and not in_f32:
         g = gemm_reference(dev)
