@@ -415,19 +415,22 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
 //   role 1 holds V, forms dP = dO Vᵀ, takes g from role 0 through LDS, forms
 //          dS = dP g (pointwise) or g (dP - delta) (softmax, g = P), and
 //          accumulates dKᵀ += Qᵀ dS.
-// Same products as the single-wavefront kernel at about 190 registers per
+// Same products as the single-wavefront kernel at about 200 registers per
 // wavefront. A workgroup has NG key groups (2 NG wavefronts, 32 NG keys);
 // kv blocks wider than that are split over several workgroups. With NG = 2
 // two workgroups share a CU, and the roles of a workgroup's wavefront pairs
 // swap with the parity of its id, so that each SIMD runs the exponentials of
-// one role beside the matrix work of the other. One extra workgroup barrier
-// per tile orders the exchange.
+// one role beside the matrix work of the other. A step takes 64 queries (two
+// 32-query parts per wavefront), so the walk's per-step scalar work and the
+// two workgroup barriers per step (the tile, then the exchange of g in bf16)
+// are spread over twice the matrix work.
 
 template <int D, int NG>
 struct PairTiling {
   static constexpr int NW = 2 * NG;               // wavefronts
   static constexpr int KEYS = 32 * NG;            // keys per workgroup
-  static constexpr int QC = 32;                   // queries per LDS tile
+  static constexpr int QC = 64;                   // queries per LDS tile (one step)
+  static constexpr int PARTS = QC / 32;           // 32-query parts per step
   static constexpr int ROWB = D * 2;
   static constexpr int RPI = 64 / (D / 8);        // rows per direct-copy instruction
   static constexpr int TILE = QC * ROWB;
@@ -436,13 +439,11 @@ struct PairTiling {
   static constexpr int SEG_ROWS = QC / NW;        // ids (and stats) copied per wave per tile
   static constexpr int NS = D / 16;
   static constexpr int ND = D / 32;
-  static constexpr int ST = 3;                    // LDS stages: two tiles in flight beside the one in use
-  static constexpr int SEG_OFF = ST * 2 * TILE;   // [stage][Q | dO][TILE], then [stage][QC] ids
-  static constexpr int STAT_OFF = SEG_OFF + ST * QC * 4;      // softmax: [stage][LSE | delta][QC]
-  static constexpr int X_OFF = STAT_OFF + ST * 2 * QC * 4;    // exchange: [NG][4][64 lanes][16 B]
-  static constexpr int LDS_BYTES = X_OFF + NG * 4096;
+  static constexpr int SEG_OFF = 2 * 2 * TILE;    // [stage][Q | dO][TILE], then [stage][QC] ids
+  static constexpr int STAT_OFF = SEG_OFF + 2 * QC * 4;      // softmax: [stage][LSE | delta][QC]
+  static constexpr int X_OFF = STAT_OFF + 2 * 2 * QC * 4;    // exchange: [NG][PARTS][2][64 lanes][16 B] bf16
+  static constexpr int LDS_BYTES = X_OFF + NG * PARTS * 2048;
   static_assert(LOADS >= 1 && SEG_ROWS >= 1, "tile too small for the workgroup");
-  static_assert(CW == NW, "every wavefront copies tile rows (fixed copies per wave and tile)");
 };
 
 template <int D, int NG, bool SM, typename OutT>
@@ -453,13 +454,14 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
   constexpr int NS = T::NS;
   constexpr int ND = T::ND;
   constexpr int QC = T::QC;
+  constexpr int PARTS = T::PARTS;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
   const int sub = p.c_block_kv / T::KEYS;  // workgroups per kv block
   int unit, rest;
   if (!work_item(p.c_nk * sub, total_work, work_per_xcd, units_interleaved, unit, rest)) return;
   const int j = rest / sub;
-  const int part = rest - j * sub;
+  const int part_of_block = rest - j * sub;
   const int b = unit / p.kv_heads;
   const int hk = unit - b * p.kv_heads;
   const int bm = p.meta_batch == 1 ? 0 : b;
@@ -475,7 +477,7 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  const int key = j * p.c_block_kv + part * T::KEYS + kg * 32 + l32;
+  const int key = j * p.c_block_kv + part_of_block * T::KEYS + kg * 32 + l32;
   const bool kvalid = key < p.kv_len;
   const bool has_seg = p.q_seg != nullptr;
 
@@ -537,13 +539,13 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
     return block_class(p.c_block_mask + (e - i), i);
   };
 
-  // Per tile each wave issues 2 LOADS row copies, plus one id copy (segment
-  // ids) and two stat copies (softmax): the fixed count the pipeline waits by.
   auto issue_tile = [&](int stage, int g, int i, int t) {
     const int h = hk * G + g;
     const int q0 = i * p.c_block_q + t;
-    const int rows = p.q_len - q0 < QC ? p.q_len - q0 : QC;  // rows past the end read as 0
-    {
+    // rows past the end of the sequence or of the q block read as 0 (no contribution)
+    int rows = p.q_len - q0 < QC ? p.q_len - q0 : QC;
+    rows = p.c_block_q - t < rows ? p.c_block_q - t : rows;
+    if (wave < T::CW) {
       const char* qg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh);
       const char* dg =
           reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.d_o) + b * p.do_sb + h * p.do_sh);
@@ -587,142 +589,124 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
   const float nl = -p.scale * 1.4426950408889634f;
   const float cl = p.scale * 1.4426950408889634f;
   constexpr float kMasked = SM ? -__builtin_inff() : kMaskedT;
-  f32x4* xg = reinterpret_cast<f32x4*>(smem + T::X_OFF + kg * 4096) + lane;  // this lane's exchange slots
+  // this lane's exchange slots: part u, chunk c at xg + (u * 2 + c) * 64
+  bf16x8* xg = reinterpret_cast<bf16x8*>(smem + T::X_OFF + kg * PARTS * 2048) + lane;
 
-  auto advance = [&](int g, int i, int t, int& ng, int& ni, int& nt) {  // the tile after (g, i, t)
-    ng = g;
-    ni = i;
-    nt = t + QC;
+  int cur_g = 0, cur_i = first_i(0), cur_t = 0;
+  settle(cur_g, cur_i);
+  if (cur_g < G) issue_tile(0, cur_g, cur_i, 0);
+
+  auto step = [&](auto stage_tag) -> bool {
+    constexpr int stage = decltype(stage_tag)::value;
+    int ng = cur_g, ni = cur_i, nt = cur_t + QC;
     if (nt >= p.c_block_q || ni * p.c_block_q + nt >= p.q_len) {
       ni = next_i(ng, ni);
       nt = 0;
       settle(ng, ni);
     }
-  };
-  // The pipeline: tile cur is used from LDS while tile nxt is in flight; the
-  // tile after it is issued at the start of each step.
-  int cur_g = 0, cur_i = first_i(0), cur_t = 0;
-  settle(cur_g, cur_i);
-  int nxt_g = G, nxt_i = 0, nxt_t = 0;
-  if (cur_g < G) {
-    issue_tile(0, cur_g, cur_i, 0);
-    advance(cur_g, cur_i, 0, nxt_g, nxt_i, nxt_t);
-    if (nxt_g < G) issue_tile(1, nxt_g, nxt_i, nxt_t);
-  }
-
-  auto step = [&](auto stage_tag) -> bool {
-    constexpr int stage = decltype(stage_tag)::value;
-    int nn_g = G, nn_i = 0, nn_t = 0;
-    if (nxt_g < G) advance(nxt_g, nxt_i, nxt_t, nn_g, nn_i, nn_t);
-    // this wave's copies of the current tile are in LDS; the next tile's
-    // (2 LOADS + segment ids + softmax stats) may still be in flight
-    if (nxt_g < G) {
-      if (has_seg)
-        wait_vmcnt<2 * T::LOADS + (SM ? 2 : 0) + 1>();
-      else
-        wait_vmcnt<2 * T::LOADS + (SM ? 2 : 0)>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    barrier_only();   // everyone's are; the stage two tiles back and the exchange are free again
-    if (nn_g < G) issue_tile((stage + 2) % 3, nn_g, nn_i, nn_t);
+    const bool partial = class_of(cur_g, cur_i) == 1;
+    wait_vmcnt<0>();  // this wave's copies of the current tile are in LDS
+    barrier_only();   // everyone's are; the other stage and the exchange are free again
+    if (ng < G) issue_tile(stage ^ 1, ng, ni, nt);
 
     const char* tb = smem + stage * 2 * T::TILE;  // Q tile, then dO tile
     const float* sst = reinterpret_cast<const float*>(smem + T::STAT_OFF) + stage * 2 * QC;
 
-    // S = Q Kᵀ (role 0) or dP = dO Vᵀ (role 1): 32 queries (rows) x 32 keys
-    f32x16 c;
+    // S = Q Kᵀ (role 0) or dP = dO Vᵀ (role 1): per part, 32 queries (rows) x 32 keys
+    f32x16 c[PARTS];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) c[r] = 0.0f;
+    for (int u = 0; u < PARTS; ++u) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(tb + aoff[s]);
-      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, breg[s], c, 0, 0, 0);
+      for (int r = 0; r < 16; ++r) c[u][r] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(tb + 32 * u * T::ROWB + aoff[s]);
+        c[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, breg[s], c[u], 0, 0, 0);
+      }
     }
 
-    bf16x8 wb[2];  // role 0: P, role 1: dS (B operands)
+    bf16x8 wb[PARTS][2];  // role 0: P, role 1: dS (B operands)
     if (role == 0) {
-      // element r: query q0 + 8 (r / 4) + 4 hh + r % 4, key `key`
-      f32x16& t = c;
-      if constexpr (SM) {
+      const int h = hk * G + cur_g;
+      const HeadBand band = p.band[p.band_heads == 1 ? 0 : h];
+      const int q0 = cur_i * p.c_block_q + cur_t;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(sst + 8 * u + 4 * hh);
+      for (int u = 0; u < PARTS; ++u) {
+        // element r: query q0 + 32 u + 8 (r / 4) + 4 hh + r % 4, key `key`
+        f32x16& t = c[u];
+        if constexpr (SM) {
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) t[4 * u + v4] = __builtin_fmaf(c[4 * u + v4], cl, -kLog2e * l4[v4]);
-        }
-      } else {
+          for (int w4 = 0; w4 < 4; ++w4) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(sst + 32 * u + 8 * w4 + 4 * hh);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) t[r] = c[r] * nl;
-      }
-      if (class_of(cur_g, cur_i) == 1) {
-        const int h = hk * G + cur_g;
-        const HeadBand band = p.band[p.band_heads == 1 ? 0 : h];
-        const int q0 = cur_i * p.c_block_q + cur_t;
-        int a = key - band.hi - q0;
-        int e = key - band.lo - q0;
-        a = a > 0 ? a : 0;
-        e = e < p.q_len - 1 - q0 ? e : p.q_len - 1 - q0;
-        e = e < QC - 1 ? e : QC - 1;
-        if (e < a || !kvalid) a = e = QC;
-        const uint32_t width = (uint32_t)(e - a);
-        const int base = 4 * hh - a;
-        if (has_seg) {
-          const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * QC;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int4 qs4 = *reinterpret_cast<const int4*>(sseg + 8 * u + 4 * hh);
-            const int ids[4] = {qs4.x, qs4.y, qs4.z, qs4.w};
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-              const bool ok = ((uint32_t)(base + 8 * u + v4) <= width) & (ids[v4] == kseg);
-              t[4 * u + v4] = ok ? t[4 * u + v4] : kMasked;
-            }
+            for (int v4 = 0; v4 < 4; ++v4) t[4 * w4 + v4] = __builtin_fmaf(t[4 * w4 + v4], cl, -kLog2e * l4[v4]);
           }
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) t[r] = ((uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width) ? t[r] : kMasked;
+          for (int r = 0; r < 16; ++r) t[r] = t[r] * nl;
         }
-      }
-      // P for dV, g for role 1 (in place of t)
+        if (partial) {
+          const int qp = q0 + 32 * u;
+          int a = key - band.hi - qp;
+          int e = key - band.lo - qp;
+          a = a > 0 ? a : 0;
+          e = e < p.q_len - 1 - qp ? e : p.q_len - 1 - qp;
+          e = e < 31 ? e : 31;
+          if (e < a || !kvalid) a = e = 32;
+          const uint32_t width = (uint32_t)(e - a);
+          const int base = 4 * hh - a;
+          if (has_seg) {
+            const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * QC + 32 * u;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr, g;
-        if constexpr (SM) {
-          pr = __builtin_amdgcn_exp2f(t[r]);
-          g = pr;
-        } else {
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t[r]));
-          pr = t[r] * sg;
-          g = __builtin_fmaf(pr, __builtin_fmaf(sg, kLn2, -kLn2), sg);
+            for (int w4 = 0; w4 < 4; ++w4) {
+              const int4 qs4 = *reinterpret_cast<const int4*>(sseg + 8 * w4 + 4 * hh);
+              const int ids[4] = {qs4.x, qs4.y, qs4.z, qs4.w};
+#pragma unroll
+              for (int v4 = 0; v4 < 4; ++v4) {
+                const bool ok = ((uint32_t)(base + 8 * w4 + v4) <= width) & (ids[v4] == kseg);
+                t[4 * w4 + v4] = ok ? t[4 * w4 + v4] : kMasked;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              t[r] = ((uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width) ? t[r] : kMasked;
+          }
         }
-        wb[r >> 3][r & 7] = (__bf16)pr;
-        t[r] = g;
-      }
+        // P for dV, g for role 1 (bf16, through LDS)
+        bf16x8 gp[2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) xg[64 * u] = f32x4{t[4 * u], t[4 * u + 1], t[4 * u + 2], t[4 * u + 3]};
+        for (int r = 0; r < 16; ++r) {
+          float pr, g;
+          if constexpr (SM) {
+            pr = __builtin_amdgcn_exp2f(t[r]);
+            g = pr;
+          } else {
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t[r]));
+            pr = t[r] * sg;
+            g = __builtin_fmaf(pr, __builtin_fmaf(sg, kLn2, -kLn2), sg);
+          }
+          wb[u][r >> 3][r & 7] = (__bf16)pr;
+          gp[r >> 3][r & 7] = (__bf16)g;
+        }
+        xg[(2 * u) * 64] = gp[0];
+        xg[(2 * u + 1) * 64] = gp[1];
+      }
     }
     barrier_only();  // g of every key group is in LDS (the next tile's copies stay in flight)
     if (role == 1) {
-      if constexpr (SM) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const f32x4 g4 = xg[64 * u];
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(sst + QC + 8 * u + 4 * hh);
+      for (int u = 0; u < PARTS; ++u) {
+        const bf16x8 g0 = xg[(2 * u) * 64], g1 = xg[(2 * u + 1) * 64];
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            const int r = 4 * u + v4;
-            wb[r >> 3][r & 7] = (__bf16)(g4[v4] * (c[r] - d4[v4]));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const f32x4 g4 = xg[64 * u];
+        for (int w4 = 0; w4 < 4; ++w4) {
+          f32x4 d4 = {0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (SM) d4 = *reinterpret_cast<const f32x4*>(sst + QC + 32 * u + 8 * w4 + 4 * hh);
 #pragma unroll
           for (int v4 = 0; v4 < 4; ++v4) {
-            const int r = 4 * u + v4;
-            wb[r >> 3][r & 7] = (__bf16)(c[r] * g4[v4]);
+            const int r = 4 * w4 + v4;
+            const float g = (float)(r < 8 ? g0[r] : g1[r - 8]);
+            wb[u][r >> 3][r & 7] = (__bf16)(SM ? g * (c[u][r] - d4[v4]) : c[u][r] * g);
           }
         }
       }
@@ -730,29 +714,27 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
 
     // role 0: dVᵀ += dOᵀ P; role 1: dKᵀ += Qᵀ dS (toff carries the role's tile)
 #pragma unroll
-    for (int g2 = 0; g2 < 2; ++g2) {
-      const int rowbase = 16 * g2 * T::ROWB;
+    for (int u = 0; u < PARTS; ++u)
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tb + rowbase + toff[0][db]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tb + rowbase + toff[1][db]));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wb[g2], acc[db], 0, 0, 0);
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int rowbase = (32 * u + 16 * g2) * T::ROWB;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tb + rowbase + toff[0][db]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tb + rowbase + toff[1][db]));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wb[u][g2], acc[db], 0, 0, 0);
+        }
       }
-    }
 
-    cur_g = nxt_g;
-    cur_i = nxt_i;
-    cur_t = nxt_t;
-    nxt_g = nn_g;
-    nxt_i = nn_i;
-    nxt_t = nn_t;
+    cur_g = ng;
+    cur_i = ni;
+    cur_t = nt;
     return cur_g < G;
   };
   while (cur_g < G) {
     if (!step(std::integral_constant<int, 0>{})) break;
     if (!step(std::integral_constant<int, 1>{})) break;
-    if (!step(std::integral_constant<int, 2>{})) break;
   }
 
   // role 0 stores dV, role 1 dK (factors as in the single-wavefront kernel)
