@@ -27,13 +27,17 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak
 METRIC = "splash fwd TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, causal S=8192"
-KERNEL_SOURCES = ["splash_fwd_bf16.hip", "splash_fwd_f32.hip", "splash_bwd_bf16.hip", "splash_bwd_f32.hip",
-                  "softmax_delta.hip", "cdna4.h", "internal.h"]
+# the sources each direction's kernels are built from: a counter summary stays
+# valid while these are unchanged
+KERNEL_SOURCES = {
+    False: ["splash_fwd_bf16.hip", "splash_fwd_f32.hip", "cdna4.h", "internal.h"],
+    True: ["splash_bwd_bf16.hip", "splash_bwd_f32.hip", "softmax_delta.hip", "cdna4.h", "internal.h"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(backward: bool = False) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[backward]:
         with open(os.path.join(ROOT, "block_sparse_masked_splash_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -47,7 +51,7 @@ def traffic_for(workload: str, backward: bool = False):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(backward):
         return None
     return t.get("bytes_per_launch")
 
@@ -277,7 +281,7 @@ def main():
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma" if not in_f32 else "alu", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_for(w.name, w.backward), "kernel_source_sha256_16": kernel_source_hash()},
+                     "traffic": traffic_for(w.name, w.backward), "kernel_source_sha256_16": kernel_source_hash(w.backward)},
     }
     if not args.no_gemm_reference and not in_f32:
         g = gemm_reference(dev)

@@ -134,6 +134,17 @@ typedef __attribute__((address_space(4))) const uint32_t* const_u32_ptr;
 __device__ inline int scalar_load_i32(const int32_t* p) {
   return (int)*(const_u32_ptr)(uintptr_t)p;
 }
+// The kernel's parameter block read in place in the kernarg segment (P must
+// be the kernel's first argument). The pointer is opaque to the optimizer,
+// so fields read through it are loaded where they are used instead of being
+// held in scalar registers for the kernel's lifetime: for values that only a
+// rare path needs.
+template <typename P>
+__device__ inline const __attribute__((address_space(4))) P* kernarg_params() {
+  auto ptr = (const __attribute__((address_space(4))) P*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(ptr));
+  return ptr;
+}
 // Class of kv block j in a metadata row, read as part of its aligned 32-bit
 // word (block_mask buffers are padded to whole words).
 __device__ inline int block_class(const int8_t* row, int j) {

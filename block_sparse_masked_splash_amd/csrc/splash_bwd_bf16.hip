@@ -508,68 +508,84 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int db = 0; db < ND; ++db) toff[hf][db] += role == 0 ? T::TILE : 0;
-  const int64_t q_rs = p.q_ss * 2, do_rs = p.do_ss * 2;
+  // each copying wavefront's first row group folded into its lane offsets
+  const uint32_t q_rs = (uint32_t)(p.q_ss * 2), do_rs = (uint32_t)(p.do_ss * 2);
   uint32_t qsel[T::LOADS], dsel[T::LOADS];
   tile_copy_offsets<D, T::CW>(lane, wave, q_rs, qsel);
   tile_copy_offsets<D, T::CW>(lane, wave, do_rs, dsel);
+#pragma unroll
+  for (int n = 0; n < T::LOADS; ++n) {
+    qsel[n] += wave * T::RPI * q_rs;
+    dsel[n] += wave * T::RPI * do_rs;
+  }
+  const int32_t* qseg_b = p.q_seg + (int64_t)b * p.q_len;
 
-  // the dK/dV metadata is stored by columns: column (g, j) is c_nq entries
-  auto entry = [&](int g, int i) -> int64_t {
+  // Walk state of one query head of the group: its Q, dO and statistics rows
+  // and its metadata column (stored by columns: c_nq consecutive entries).
+  // It always describes the head of the most recently issued tile.
+  // (The parameters it is made from are read from the kernarg segment on a
+  // head change only, which keeps them out of the loop's scalar registers.)
+  const char* q_h;
+  const char* do_h;
+  const float* lse_h;
+  const float* delta_h;
+  const int32_t* dn_col;
+  const int8_t* cls_col;
+  auto set_head = [&](int g) {
+    const auto* kp = kernarg_params<BwdParams>();
     const int h = hk * G + g;
-    const int hm = p.c_meta_heads == 1 ? 0 : h;
-    return (((int64_t)bm * p.c_meta_heads + hm) * p.c_nk + j) * p.c_nq + i;
+    const int hm = kp->c_meta_heads == 1 ? 0 : h;
+    const int64_t col = (((int64_t)bm * kp->c_meta_heads + hm) * kp->c_nk + j) * kp->c_nq;
+    dn_col = kp->c_data_next + col;
+    cls_col = kp->c_block_mask + col;
+    q_h = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(kp->q) + b * kp->q_sb + h * kp->q_sh);
+    do_h = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(kp->d_o) + b * kp->do_sb + h * kp->do_sh);
+    const int64_t st = b * kp->st_sb + h * kp->st_sh;
+    lse_h = kp->lse + st;
+    delta_h = kp->delta + st;
   };
-  auto first_i = [&](int g) {
+  auto first_i = [&]() {
     if (p.c_nq == 0) return p.c_nq;
-    const int i = scalar_load_i32(p.c_data_next + entry(g, 0));
+    const int i = scalar_load_i32(dn_col);
     return (i >= 0 && i <= p.c_nq) ? i : p.c_nq;
   };
-  auto next_i = [&](int g, int i) {
-    const int in = (i + 1 < p.c_nq) ? scalar_load_i32(p.c_data_next + entry(g, i + 1)) : p.c_nq;
+  auto next_i = [&](int i) {
+    const int in = (i + 1 < p.c_nq) ? scalar_load_i32(dn_col + i + 1) : p.c_nq;
     return (in > i && in <= p.c_nq) ? in : p.c_nq;
   };
   auto settle = [&](int& g, int& i) {
     while (i >= p.c_nq) {
       if (++g >= G) return;
-      i = first_i(g);
+      set_head(g);
+      i = first_i();
     }
   };
-  auto class_of = [&](int g, int i) {
-    const int64_t e = entry(g, i);
-    return block_class(p.c_block_mask + (e - i), i);
-  };
 
-  auto issue_tile = [&](int stage, int g, int i, int t) {
-    const int h = hk * G + g;
+  auto issue_tile = [&](int stage, int i, int t) {
     const int q0 = i * p.c_block_q + t;
     // rows past the end of the sequence or of the q block read as 0 (no contribution)
     int rows = p.q_len - q0 < QC ? p.q_len - q0 : QC;
     rows = p.c_block_q - t < rows ? p.c_block_q - t : rows;
     if (wave < T::CW) {
-      const char* qg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh);
-      const char* dg =
-          reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.d_o) + b * p.do_sb + h * p.do_sh);
       char* qdst = smem + stage * 2 * T::TILE;
       char* ddst = qdst + T::TILE;
-      const u32x4 qrs = buffer_rsrc(qg + q0 * q_rs, (uint32_t)(rows * q_rs));
-      const u32x4 drs = buffer_rsrc(dg + q0 * do_rs, (uint32_t)(rows * do_rs));
-      lds_copy_rows<T::LOADS, T::CW * 1024>(qrs, qsel, (uint32_t)(wave * T::RPI * q_rs),
-                                            (uint32_t)(T::CW * T::RPI * q_rs), lds_addr(qdst + wave * T::RPI * T::ROWB));
-      lds_copy_rows<T::LOADS, T::CW * 1024>(drs, dsel, (uint32_t)(wave * T::RPI * do_rs),
-                                            (uint32_t)(T::CW * T::RPI * do_rs),
+      const u32x4 qrs = buffer_rsrc(q_h + (int64_t)q0 * q_rs, (uint32_t)rows * q_rs);
+      const u32x4 drs = buffer_rsrc(do_h + (int64_t)q0 * do_rs, (uint32_t)rows * do_rs);
+      lds_copy_rows<T::LOADS, T::CW * 1024>(qrs, qsel, 0u, T::CW * T::RPI * q_rs,
+                                            lds_addr(qdst + wave * T::RPI * T::ROWB));
+      lds_copy_rows<T::LOADS, T::CW * 1024>(drs, dsel, 0u, T::CW * T::RPI * do_rs,
                                             lds_addr(ddst + wave * T::RPI * T::ROWB));
     }
     if (has_seg) {
       const uint32_t sdst =
           lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * QC + wave * T::SEG_ROWS);
-      const u32x4 srs = buffer_rsrc(p.q_seg + (int64_t)b * p.q_len + q0, (uint32_t)(rows * 4));
+      const u32x4 srs = buffer_rsrc(qseg_b + q0, (uint32_t)(rows * 4));
       if (lane < T::SEG_ROWS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), sdst);
     }
     if constexpr (SM) {
       float* st = reinterpret_cast<float*>(smem + T::STAT_OFF) + stage * 2 * QC + wave * T::SEG_ROWS;
-      const int64_t off = b * p.st_sb + h * p.st_sh + q0;
-      const u32x4 lrs = buffer_rsrc(p.lse + off, (uint32_t)(rows * 4));
-      const u32x4 drs2 = buffer_rsrc(p.delta + off, (uint32_t)(rows * 4));
+      const u32x4 lrs = buffer_rsrc(lse_h + q0, (uint32_t)(rows * 4));
+      const u32x4 drs2 = buffer_rsrc(delta_h + q0, (uint32_t)(rows * 4));
       if (lane < T::SEG_ROWS) {
         lds_copy4(lrs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st));
         lds_copy4(drs2, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st + QC));
@@ -592,22 +608,24 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
   // this lane's exchange slots: part u, chunk c at xg + (u * 2 + c) * 64
   bf16x8* xg = reinterpret_cast<bf16x8*>(smem + T::X_OFF + kg * PARTS * 2048) + lane;
 
-  int cur_g = 0, cur_i = first_i(0), cur_t = 0;
+  int cur_g = 0, cur_t = 0;
+  set_head(0);
+  int cur_i = first_i();
   settle(cur_g, cur_i);
-  if (cur_g < G) issue_tile(0, cur_g, cur_i, 0);
+  if (cur_g < G) issue_tile(0, cur_i, 0);
 
   auto step = [&](auto stage_tag) -> bool {
     constexpr int stage = decltype(stage_tag)::value;
+    const bool partial = block_class(cls_col, cur_i) == 1;
     int ng = cur_g, ni = cur_i, nt = cur_t + QC;
     if (nt >= p.c_block_q || ni * p.c_block_q + nt >= p.q_len) {
-      ni = next_i(ng, ni);
+      ni = next_i(ni);
       nt = 0;
       settle(ng, ni);
     }
-    const bool partial = class_of(cur_g, cur_i) == 1;
     wait_vmcnt<0>();  // this wave's copies of the current tile are in LDS
     barrier_only();   // everyone's are; the other stage and the exchange are free again
-    if (ng < G) issue_tile(stage ^ 1, ng, ni, nt);
+    if (ng < G) issue_tile(stage ^ 1, ni, nt);
 
     const char* tb = smem + stage * 2 * T::TILE;  // Q tile, then dO tile
     const float* sst = reinterpret_cast<const float*>(smem + T::STAT_OFF) + stage * 2 * QC;
@@ -627,8 +645,6 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
 
     bf16x8 wb[PARTS][2];  // role 0: P, role 1: dS (B operands)
     if (role == 0) {
-      const int h = hk * G + cur_g;
-      const HeadBand band = p.band[p.band_heads == 1 ? 0 : h];
       const int q0 = cur_i * p.c_block_q + cur_t;
 #pragma unroll
       for (int u = 0; u < PARTS; ++u) {
@@ -646,9 +662,12 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
           for (int r = 0; r < 16; ++r) t[r] = t[r] * nl;
         }
         if (partial) {
+          const auto* kp = kernarg_params<BwdParams>();
+          const int bi = kp->band_heads == 1 ? 0 : hk * G + cur_g;
+          const int band_lo = kp->band[bi].lo, band_hi = kp->band[bi].hi;
           const int qp = q0 + 32 * u;
-          int a = key - band.hi - qp;
-          int e = key - band.lo - qp;
+          int a = key - band_hi - qp;
+          int e = key - band_lo - qp;
           a = a > 0 ? a : 0;
           e = e < p.q_len - 1 - qp ? e : p.q_len - 1 - qp;
           e = e < 31 ? e : 31;
