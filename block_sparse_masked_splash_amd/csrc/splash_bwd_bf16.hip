@@ -161,67 +161,82 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
   row_operand_offsets<D>(lane, aoff);
   int toff[2][ND];
   transpose_operand_offsets<D>(lane, toff);
-  const int64_t q_rs = p.q_ss * 2, do_rs = p.do_ss * 2;
+  // each wavefront's first row group folded into its lane offsets
+  const uint32_t q_rs = (uint32_t)(p.q_ss * 2), do_rs = (uint32_t)(p.do_ss * 2);
   uint32_t qsel[T::LOADS], dsel[T::LOADS];
   tile_copy_offsets<D, NW>(lane, wave, q_rs, qsel);
   tile_copy_offsets<D, NW>(lane, wave, do_rs, dsel);
+#pragma unroll
+  for (int n = 0; n < T::LOADS; ++n) {
+    qsel[n] += wave * T::RPI * q_rs;
+    dsel[n] += wave * T::RPI * do_rs;
+  }
+  const int32_t* qseg_b = p.q_seg + (int64_t)b * p.q_len;
 
   // ---- column walk over (query head of the group, q block, 32-query tile) ----
-  // the dK/dV metadata is stored by columns: column (g, j) is c_nq entries
-  auto entry = [&](int g, int i) -> int64_t {
+  // Walk state of one query head: its Q, dO and statistics rows and its
+  // metadata column (stored by columns: c_nq consecutive entries), for the
+  // head of the most recently issued tile. The parameters it is made from
+  // are read from the kernarg segment on a head change only, which keeps
+  // them out of the loop's scalar registers.
+  const char* q_h;
+  const char* do_h;
+  const float* lse_h;
+  const float* delta_h;
+  const int32_t* dn_col;
+  const int8_t* cls_col;
+  auto set_head = [&](int g) {
+    const auto* kp = kernarg_params<BwdParams>();
     const int h = hk * G + g;
-    const int hm = p.c_meta_heads == 1 ? 0 : h;
-    return (((int64_t)bm * p.c_meta_heads + hm) * p.c_nk + j) * p.c_nq + i;
+    const int hm = kp->c_meta_heads == 1 ? 0 : h;
+    const int64_t col = (((int64_t)bm * kp->c_meta_heads + hm) * kp->c_nk + j) * kp->c_nq;
+    dn_col = kp->c_data_next + col;
+    cls_col = kp->c_block_mask + col;
+    q_h = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(kp->q) + b * kp->q_sb + h * kp->q_sh);
+    do_h = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(kp->d_o) + b * kp->do_sb + h * kp->do_sh);
+    const int64_t st = b * kp->st_sb + h * kp->st_sh;
+    lse_h = kp->lse + st;
+    delta_h = kp->delta + st;
   };
   // data_next is only followed forward and within [0, nq], so any metadata
   // content ends the walk in bounds.
-  auto first_i = [&](int g) {
+  auto first_i = [&]() {
     if (p.c_nq == 0) return p.c_nq;
-    const int i = scalar_load_i32(p.c_data_next + entry(g, 0));
+    const int i = scalar_load_i32(dn_col);
     return (i >= 0 && i <= p.c_nq) ? i : p.c_nq;
   };
-  auto next_i = [&](int g, int i) {
-    const int in = (i + 1 < p.c_nq) ? scalar_load_i32(p.c_data_next + entry(g, i + 1)) : p.c_nq;
+  auto next_i = [&](int i) {
+    const int in = (i + 1 < p.c_nq) ? scalar_load_i32(dn_col + i + 1) : p.c_nq;
     return (in > i && in <= p.c_nq) ? in : p.c_nq;
   };
   // the first (g, i) at or after head g with a non-empty block (g == G: none)
   auto settle = [&](int& g, int& i) {
     while (i >= p.c_nq) {
       if (++g >= G) return;
-      i = first_i(g);
+      set_head(g);
+      i = first_i();
     }
   };
-  auto class_of = [&](int g, int i) {
-    const int64_t e = entry(g, i);
-    return block_class(p.c_block_mask + (e - i), i);
-  };
 
-  auto issue_tile = [&](int stage, int g, int i, int t) {
-    const int h = hk * G + g;
+  auto issue_tile = [&](int stage, int i, int t) {
     const int q0 = i * p.c_block_q + t;
     const int rows = p.q_len - q0 < QC ? p.q_len - q0 : QC;  // rows past the end read as 0
-    const char* qg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh);
-    const char* dg =
-        reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.d_o) + b * p.do_sb + h * p.do_sh);
     char* qdst = smem + stage * 2 * T::TILE;
     char* ddst = qdst + T::TILE;
-    const u32x4 qrs = buffer_rsrc(qg + q0 * q_rs, (uint32_t)(rows * q_rs));
-    const u32x4 drs = buffer_rsrc(dg + q0 * do_rs, (uint32_t)(rows * do_rs));
-    lds_copy_rows<T::LOADS, NW * 1024>(qrs, qsel, (uint32_t)(wave * T::RPI * q_rs), (uint32_t)(NW * T::RPI * q_rs),
-                                       lds_addr(qdst + wave * T::RPI * T::ROWB));
-    lds_copy_rows<T::LOADS, NW * 1024>(drs, dsel, (uint32_t)(wave * T::RPI * do_rs), (uint32_t)(NW * T::RPI * do_rs),
-                                       lds_addr(ddst + wave * T::RPI * T::ROWB));
+    const u32x4 qrs = buffer_rsrc(q_h + (int64_t)q0 * q_rs, (uint32_t)rows * q_rs);
+    const u32x4 drs = buffer_rsrc(do_h + (int64_t)q0 * do_rs, (uint32_t)rows * do_rs);
+    lds_copy_rows<T::LOADS, NW * 1024>(qrs, qsel, 0u, NW * T::RPI * q_rs, lds_addr(qdst + wave * T::RPI * T::ROWB));
+    lds_copy_rows<T::LOADS, NW * 1024>(drs, dsel, 0u, NW * T::RPI * do_rs, lds_addr(ddst + wave * T::RPI * T::ROWB));
     if (has_seg) {
       const uint32_t sdst =
           lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * QC + wave * T::SEG_ROWS);
-      const u32x4 srs = buffer_rsrc(p.q_seg + (int64_t)b * p.q_len + q0, (uint32_t)(rows * 4));
+      const u32x4 srs = buffer_rsrc(qseg_b + q0, (uint32_t)(rows * 4));
       if (lane < T::SEG_ROWS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), sdst);
     }
     if constexpr (SM) {
       float* st = reinterpret_cast<float*>(smem + T::STAT_OFF) + stage * 2 * QC + wave * T::SEG_ROWS;
-      const int64_t off = b * p.st_sb + h * p.st_sh + q0;
-      const u32x4 lrs = buffer_rsrc(p.lse + off, (uint32_t)(rows * 4));
-      const u32x4 drs2 = buffer_rsrc(p.delta + off, (uint32_t)(rows * 4));
+      const u32x4 lrs = buffer_rsrc(lse_h + q0, (uint32_t)(rows * 4));
+      const u32x4 drs2 = buffer_rsrc(delta_h + q0, (uint32_t)(rows * 4));
       if (lane < T::SEG_ROWS) {
         lds_copy4(lrs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st));
         lds_copy4(drs2, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st + QC));
@@ -246,25 +261,25 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
   const float cl = p.scale * 1.4426950408889634f;  // softmax: x log2(e) = cl q·k
   constexpr float kMasked = SM ? -__builtin_inff() : kMaskedT;
 
-  int cur_g = 0, cur_i = first_i(0), cur_t = 0;
+  int cur_g = 0, cur_t = 0;
+  set_head(0);
+  int cur_i = first_i();
   settle(cur_g, cur_i);
-  if (cur_g < G) issue_tile(0, cur_g, cur_i, 0);
+  if (cur_g < G) issue_tile(0, cur_i, 0);
 
   auto step = [&](auto stage_tag) -> bool {
     constexpr int stage = decltype(stage_tag)::value;
+    const bool partial = block_class(cls_col, cur_i) == 1;
     int ng = cur_g, ni = cur_i, nt = cur_t + QC;
     if (nt >= p.c_block_q || ni * p.c_block_q + nt >= p.q_len) {
-      ni = next_i(ng, ni);
+      ni = next_i(ni);
       nt = 0;
       settle(ng, ni);
     }
     wait_vmcnt<0>();  // this wave's copies of the current tile are in LDS
     barrier_only();   // everyone's are, and the other stage is free again
-    if (ng < G) issue_tile(stage ^ 1, ng, ni, nt);
+    if (ng < G) issue_tile(stage ^ 1, ni, nt);
 
-    const int h = hk * G + cur_g;
-    const HeadBand band = p.band[p.band_heads == 1 ? 0 : h];
-    const bool partial = class_of(cur_g, cur_i) == 1;
     const int q0 = cur_i * p.c_block_q + cur_t;
     const char* qt = smem + stage * 2 * T::TILE;
     const char* dt = qt + T::TILE;
@@ -307,8 +322,11 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
       for (int r = 0; r < 16; ++r) t[r] = sacc[r] * nl;
     }
     if (partial) {
-      int a = key - band.hi - q0;
-      int e = key - band.lo - q0;
+      const auto* kp = kernarg_params<BwdParams>();
+      const int bi = kp->band_heads == 1 ? 0 : hk * G + cur_g;
+      const int band_lo = kp->band[bi].lo, band_hi = kp->band[bi].hi;
+      int a = key - band_hi - q0;
+      int e = key - band_lo - q0;
       a = a > 0 ? a : 0;
       e = e < p.q_len - 1 - q0 ? e : p.q_len - 1 - q0;
       e = e < QC - 1 ? e : QC - 1;
