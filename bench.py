@@ -27,6 +27,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak
 METRIC = "splash fwd TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, causal S=8192"
+# the backward workloads report the same kind of figure for the backward pass
+BWD_METRIC = "splash bwd TFLOP/s (unmasked FLOPs, 5 products per block) + % bf16 MFMA peak"
 # the sources each direction's kernels are built from: a counter summary stays
 # valid while these are unchanged
 KERNEL_SOURCES = {
@@ -257,7 +259,7 @@ def main():
     fwd_name = (("pointwise_bwd" if w.pointwise else "softmax_bwd_preprocess + softmax_bwd") if w.backward
                 else ("pointwise_fwd" if w.pointwise else "splash_fwd"))
     line = {
-        "metric": METRIC,
+        "metric": BWD_METRIC if w.backward else METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
