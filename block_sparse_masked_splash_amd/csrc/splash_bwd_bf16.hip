@@ -1081,8 +1081,12 @@ template <int D, bool SM, typename OutT>
 hipError_t launch_sm(const BwdParams& p, hipStream_t stream) {
   hipError_t e;
   if constexpr (D == 128) {
-    // paired wavefronts: K, V, dK and dV do not fit one wavefront twice per SIMD
-    e = launch_dkv_pair<D, 2, SM, OutT>(p, stream);
+    // paired wavefronts: K, V, dK and dV do not fit one wavefront twice per
+    // SIMD. 128-key blocks: one eight-wavefront workgroup per CU (each tile
+    // copy serves 128 keys, and a SIMD's two wavefronts work in step);
+    // 64-key blocks: two four-wavefront workgroups per CU.
+    e = p.c_block_kv % 128 == 0 ? launch_dkv_pair<D, 4, SM, OutT>(p, stream)
+                                : launch_dkv_pair<D, 2, SM, OutT>(p, stream);
   } else {
     e = p.c_block_kv == 64 ? launch_dkv<D, 2, SM, OutT>(p, stream) : launch_dkv<D, 4, SM, OutT>(p, stream);
   }
