@@ -195,7 +195,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
 
   // Copy of tile (block j, offset t): K and V rows, their segment ids, and for
   // a partial block of a dense mask the block's bits of this tile's keys.
-  auto issue_tile = [&](int stage, int j, int t) {
+  auto issue_tile = [&](int stage, int j, int t, bool j_partial) {
     const int key0 = j * p.block_kv + t;
     char* kdst = smem + stage * 2 * T::TILE;
     char* vdst = kdst + T::TILE;
@@ -211,7 +211,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
       const u32x4 srs = buffer_rsrc(kvseg_g + key0, (uint32_t)(rows * 4));
       if (lane < T::SEG_KEYS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_KEYS * 4), sdst);
     }
-    if (dense && block_class(bmask, j) == 1) {
+    if (dense && j_partial) {
       int m = scalar_load_i32(p.mask_next + mrow + j);
       m = m < 0 ? 0 : (m >= p.num_mask_blocks ? (int)p.num_mask_blocks - 1 : m);  // any content stays in the store
       const int wpr = p.block_kv / 32;
@@ -251,7 +251,9 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
   int cur_j = p.nk > 0 ? scalar_load_i32(dnext) : p.nk;
   if (cur_j < 0 || cur_j > p.nk) cur_j = p.nk;
   int cur_t = 0;
-  if (cur_j < p.nk) issue_tile(0, cur_j, 0);
+  // class of the block being walked, read once per block (off the tile's math)
+  bool cur_partial = cur_j < p.nk && block_class(bmask, cur_j) == 1;
+  if (cur_j < p.nk) issue_tile(0, cur_j, 0, cur_partial);
 
   // One tile in LDS stage STAGE (a compile-time constant, so every tile
   // address is a per-lane offset plus an immediate). Returns whether another
@@ -259,18 +261,24 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
   auto step = [&](auto stage_tag) -> bool {
     constexpr int stage = decltype(stage_tag)::value;
     int nxt_j = cur_j, nxt_t = cur_t + KC;
+    bool nxt_partial = cur_partial;
     if (nxt_t >= p.block_kv || cur_j * p.block_kv + nxt_t >= p.kv_len) {
       nxt_j = next_block(cur_j);
       nxt_t = 0;
+      nxt_partial = nxt_j < p.nk && block_class(bmask, nxt_j) == 1;
     }
     wait_vmcnt<0>();  // this wave's copies of the current tile are in LDS
     // After this barrier every wave's copies of the current tile are in LDS and
     // every wave is done with the previous tile, whose stage is refilled now.
     barrier_only();
-    if (nxt_j < p.nk) issue_tile(stage ^ 1, nxt_j, nxt_t);
+    // The wavefront issues at raised priority while it reads K and forms S,
+    // and drops back before P V: a wavefront entering its matrix phase is then
+    // picked ahead of the others' vector work on the SIMD.
+    __builtin_amdgcn_s_setprio(1);
+    if (nxt_j < p.nk) issue_tile(stage ^ 1, nxt_j, nxt_t, nxt_partial);
 
     const int k0 = cur_j * p.block_kv + cur_t;
-    const bool partial = block_class(bmask, cur_j) == 1;
+    const bool partial = cur_partial;
     const char* kt = smem + stage * 2 * T::TILE;
     const char* vt = kt + T::TILE;
 
@@ -346,8 +354,10 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
           }
           return rs;
         };
+        // (a row with no reference yet gets the offset +inf: its sum is inf
+        // or NaN, so it fails the test as well)
         float rs = probs(-mref);
-        const bool fast = (mref != kNegInf) & (rs <= kFastLimit);  // false for NaN / inf too
+        const bool fast = rs <= kFastLimit;  // false for NaN / inf too
         if (__builtin_amdgcn_ballot_w64(!fast) != 0) {
           float mx = kNegInf;
 #pragma unroll
@@ -379,6 +389,8 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
         }
       }
 
+      __builtin_amdgcn_s_setprio(0);
+
       // ---- Oᵀ += Vᵀ Pᵀ over these 32 keys ----
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
@@ -395,6 +407,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
 
     cur_j = nxt_j;
     cur_t = nxt_t;
+    cur_partial = nxt_partial;
     return cur_j < p.nk;
   };
   while (cur_j < p.nk) {
