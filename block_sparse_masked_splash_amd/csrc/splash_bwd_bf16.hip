@@ -278,6 +278,9 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
     }
     wait_vmcnt<0>();  // this wave's copies of the current tile are in LDS
     barrier_only();   // everyone's are, and the other stage is free again
+    // raised issue priority while the wavefront forms S, dP and the weights;
+    // back to normal for the dV/dK products
+    __builtin_amdgcn_s_setprio(1);
     if (ng < G) issue_tile(stage ^ 1, ni, nt);
 
     const int q0 = cur_i * p.c_block_q + cur_t;
@@ -371,6 +374,8 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
         sb[r >> 3][r & 7] = (__bf16)w.ds;
       }
     }
+
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- dVᵀ += dOᵀ P', dKᵀ += Qᵀ dS' over the 32 queries ----
 #pragma unroll
@@ -926,21 +931,30 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
   int cur_j = p.nk > 0 ? scalar_load_i32(dnext) : p.nk;
   if (cur_j < 0 || cur_j > p.nk) cur_j = p.nk;
   int cur_t = 0;
+  // class of the block being walked, read once per block (off the tile's math)
+  bool cur_partial = cur_j < p.nk && block_class(bmask, cur_j) == 1;
   if (cur_j < p.nk) issue_tile(0, cur_j, 0);
 
   auto step = [&](auto stage_tag) -> bool {
     constexpr int stage = decltype(stage_tag)::value;
     int nxt_j = cur_j, nxt_t = cur_t + KC;
+    bool nxt_partial = cur_partial;
     if (nxt_t >= p.block_kv || cur_j * p.block_kv + nxt_t >= p.kv_len) {
       nxt_j = next_block(cur_j);
       nxt_t = 0;
+      nxt_partial = nxt_j < p.nk && block_class(bmask, nxt_j) == 1;
     }
     wait_vmcnt<0>();
     barrier_only();
     if (nxt_j < p.nk) issue_tile(stage ^ 1, nxt_j, nxt_t);
+    // raised issue priority while the wavefront forms S, dP and dS (measured
+    // faster at D = 64 and for the softmax gradient, slower for the pointwise
+    // one at D = 128)
+    constexpr bool kPrio = D == 64 || SM;
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
 
     const int k0 = cur_j * p.block_kv + cur_t;
-    const bool partial = block_class(bmask, cur_j) == 1;
+    const bool partial = cur_partial;
     const char* kt = smem + stage * 2 * T::TILE;
     const char* vt = kt + T::TILE;
     const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * KC;
@@ -1000,6 +1014,8 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
         sb[r >> 3][r & 7] = SM ? (__bf16)(__builtin_amdgcn_exp2f(t[r]) * (pacc[r] - dlt))
                                : (__bf16)pointwise_weights(t[r], pacc[r]).ds;
 
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+
       // ---- dQᵀ += Kᵀ dSᵀ over these 32 keys ----
 #pragma unroll
       for (int g2 = 0; g2 < 2; ++g2) {
@@ -1015,6 +1031,7 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
     }
     cur_j = nxt_j;
     cur_t = nxt_t;
+    cur_partial = nxt_partial;
     return cur_j < p.nk;
   };
   while (cur_j < p.nk) {
