@@ -303,15 +303,16 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
       // Element mask, only on blocks of class 1: the band and the sequence end
       // leave row q one run of keys [a, e] of the tile (offsets from k0),
       // tested per score as one unsigned compare; straight-line code.
-      auto apply_mask = [&](auto seg_tag) {
+      auto apply_mask = [&](auto seg_tag, auto dense_tag) {
         constexpr bool kSeg = decltype(seg_tag)::value;
+        constexpr bool kDense = decltype(dense_tag)::value;
         int4 kseg4[4];
         if constexpr (kSeg) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) kseg4[u] = *reinterpret_cast<const int4*>(sseg + 32 * kb + 8 * u + 4 * hh);
         }
-        // dense mask: bit 8 (r / 4) + r % 4 of this word for score r (all ones without one)
-        const uint32_t dbits = dense ? dmw[kb] >> (4 * hh) : 0xffffffffu;
+        // dense mask: bit 8 (r / 4) + r % 4 of this word for score r
+        const uint32_t dbits = kDense ? dmw[kb] >> (4 * hh) : 0u;
         int a = qrow + band.lo - k0;
         int e = qrow + band.hi - k0;
         a = a > 0 ? a : 0;
@@ -323,16 +324,21 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kc = 32 * kb + 8 * (r >> 2) + (r & 3);
-          bool ok = ((uint32_t)(base + kc) <= width) & ((dbits >> (8 * (r >> 2) + (r & 3))) & 1u);
+          bool ok = (uint32_t)(base + kc) <= width;
+          if constexpr (kDense) ok &= (bool)((dbits >> (8 * (r >> 2) + (r & 3))) & 1u);
           if constexpr (kSeg) ok &= kseg4[r >> 2][r & 3] == myseg;
           sacc[r] = ok ? sacc[r] : (PW ? 0.0f : kNegInf);
         }
       };
+      // one straight-line variant per kind of mask (dense-mask metadata is
+      // never combined with segment ids)
       if (partial) {
-        if (has_seg)
-          apply_mask(std::true_type{});
+        if (dense)
+          apply_mask(std::false_type{}, std::true_type{});
+        else if (has_seg)
+          apply_mask(std::true_type{}, std::false_type{});
         else
-          apply_mask(std::false_type{});
+          apply_mask(std::false_type{}, std::false_type{});
       }
 
       bf16x8 pb[2];  // [g]: B operand of Oᵀ += Vᵀ Pᵀ for keys 32 kb + 16 g + ...
