@@ -53,6 +53,9 @@ DKV_META_CASES = [
     (3, 2, 517, 517, [CAUSAL, wl.local_causal(40)], 96, 128, "docs"),
     (2, 2, 200, 180, [(1, 30, 30), FULL], 64, 128, "random"),
     (1, 1, 4100, 300, [CAUSAL], 32, 64, None),   # more than 64 q blocks per column
+    (2, 1, 90, 100, [CAUSAL], 64, 64, "random"),  # too small to hold the blocks' id ranges
+    (2, 2, 263, 301, [CAUSAL, (0, 40, 10)], 96, 160, "random"),
+    (1, 1, 4100, 700, [CAUSAL], 32, 64, "docs"),  # more than 64 q blocks per column, with segments
 ]
 
 

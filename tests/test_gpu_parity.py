@@ -48,6 +48,11 @@ META_CASES = [
     (2, 2, 200, 180, [(1, 30, 30), FULL], 64, 128, "random"),
     (1, 2, 1000, 1000, [CAUSAL, wl.local_causal(100)], 48, 100, None),
     (2, 1, 4100, 4100, [CAUSAL], 64, 64, "docs"),   # more than 64 kv blocks per row
+    # segment ids with metadata smaller than the blocks' id ranges (the
+    # one-workgroup-per-entry classification), and random ids in ragged blocks
+    # of uneven sizes (pair tests on most entries, several 64-query rounds)
+    (2, 1, 100, 90, [CAUSAL], 64, 64, "random"),
+    (2, 2, 301, 263, [CAUSAL, (0, 40, 10)], 160, 96, "random"),
     (1, 1, 1, 1, [CAUSAL], 64, 64, None),
     (1, 1, 70, 0, [FULL], 64, 64, None),
 ]
