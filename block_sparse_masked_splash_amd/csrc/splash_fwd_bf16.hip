@@ -100,7 +100,7 @@ struct Tiling {
 template <int D, int NW, bool PW, typename OutT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW>(),
                                                                       waves_per_simd<D, NW>())))
-void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
+void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int units_grouped) {
   using T = Tiling<D, NW>;
   constexpr int KC = T::KC;
   constexpr int NS = T::NS;
@@ -108,22 +108,30 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
   // XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
-  // id -> (x, k) = (id % 8, id / 8) is the k-th workgroup XCD x runs. The
-  // unit an XCD works through in one go is a K/V head together with the
-  // kv_group query heads that read it (one head without grouping), so that
-  // K/V head stays in the XCD's L2; within a unit the heaviest query blocks
-  // (most kv blocks under causal masks) go first, the unit's heads side by
-  // side. When the number of units is a multiple of 8, XCD x takes units
-  // x, x + 8, ...: units with different masks (say causal and local heads)
-  // are then spread evenly over the XCDs. Otherwise each XCD takes a
-  // contiguous eighth of the work list.
+  // id -> (x, k) = (id % 8, id / 8) is the k-th workgroup XCD x runs. A unit
+  // is a K/V head together with the kv_group query heads that read it (one
+  // head without grouping). When the number of units is a multiple of 8, XCD
+  // x takes units x, x + 8, ... (units with different masks, say causal and
+  // local heads, are then spread evenly over the XCDs), in groups of
+  // `units_grouped` units: within a group the query blocks go heaviest first
+  // (most kv blocks under causal masks) across all the group's units and
+  // heads, so the group's tail is made of its lightest blocks, while the
+  // K/V heads in flight stay few enough to be served from cache. Otherwise
+  // (units_grouped = 0) each XCD takes a contiguous eighth of the work list.
   const int xcd = (int)(blockIdx.x & 7), k_in_xcd = (int)(blockIdx.x >> 3);
   const int per_unit = p.nq * p.kv_group;
   int unit, rest;
-  if (units_interleaved) {
-    const int uk = k_in_xcd / per_unit;
-    unit = xcd + 8 * uk;
-    rest = k_in_xcd - uk * per_unit;
+  if (units_grouped) {
+    const int G = units_grouped;
+    const int units_xcd = (p.B * p.kv_heads) / 8;
+    const int gi = k_in_xcd / (G * per_unit);
+    const int g_units = units_xcd - gi * G < G ? units_xcd - gi * G : G;  // the last group may be smaller
+    const int r = k_in_xcd - gi * G * per_unit;
+    const int ri0 = r / (g_units * p.kv_group);  // rank of the query block, heaviest first
+    const int rem = r - ri0 * g_units * p.kv_group;
+    const int ug = rem / p.kv_group;
+    unit = xcd + 8 * (gi * G + ug);
+    rest = ri0 * p.kv_group + (rem - ug * p.kv_group);
   } else {
     const int wid = xcd * work_per_xcd + k_in_xcd;
     if (wid >= total_work) return;
@@ -450,9 +458,22 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   const int64_t total = (int64_t)p.nq * p.B * p.H;
   if (total == 0) return hipSuccess;
   const int64_t per_xcd = (total + 7) / 8;
-  const int interleaved = (p.B * p.kv_heads) % 8 == 0 ? 1 : 0;  // then total == 8 * per_xcd
+  // units per group on an XCD (0: no round-robin of units, when their count
+  // is not a multiple of 8; then total != 8 * per_xcd): the largest power of
+  // two up to 8 whose K/V heads, over all 8 XCDs at once, stay within about
+  // half of the 256 MB last-level cache (16 MiB per XCD). Measured at
+  // B x H x S x D = 2 x 32 x 8192 x 128 (4 MiB of K/V per head): groups of 4
+  // beat 1 by 4% and 8 by 2%; at 1 MiB per head groups of 8 beat 1 by 15-20%;
+  // at 16 MiB per head groups of 2 were 37% slower than 1.
+  int grouped = 0;
+  const int units = p.B * p.kv_heads;
+  if (units % 8 == 0) {
+    const double kv_unit = 4.0 * p.kv_len * p.head_dim;  // bf16 K and V rows of one K/V head
+    grouped = 1;
+    while (grouped < 8 && 2 * grouped <= units / 8 && 2 * grouped * kv_unit <= 16.0 * 1024 * 1024) grouped *= 2;
+  }
   hipLaunchKernelGGL((splash_fwd_bf16_kernel<D, NW, PW, OutT>), dim3((unsigned)(per_xcd * 8)), dim3(NW * 64), 0,
-                     stream, p, (int)total, (int)per_xcd, interleaved);
+                     stream, p, (int)total, (int)per_xcd, grouped);
   return hipGetLastError();
 }
 
