@@ -65,16 +65,26 @@ __device__ inline Weights pointwise_weights(float t, float dp) {
 }
 
 // XCD-aware work order shared by both passes: workgroup ids are dealt
-// round-robin to the 8 XCDs; XCD x takes units x, x + 8, ... when the number
-// of units is a multiple of 8, else a contiguous eighth of the work list.
-// Returns false for an id past the end of the list.
-__device__ inline bool work_item(int per_unit, int total_work, int work_per_xcd, int units_interleaved, int& unit,
-                                 int& rest) {
+// round-robin to the 8 XCDs. When the number of units is a multiple of 8, XCD
+// x takes units x, x + 8, ... in groups of `units_grouped` units, and within a
+// group the work items go heaviest first across all the group's units (a
+// unit's items are listed heaviest first, `inner` consecutive items at a time
+// being of equal weight); else (units_grouped = 0) each XCD takes a
+// contiguous eighth of the work list. Returns false for an id past the end.
+__device__ inline bool work_item(int per_unit, int inner, int total_work, int work_per_xcd, int units_grouped,
+                                 int& unit, int& rest) {
   const int xcd = (int)(blockIdx.x & 7), k_in_xcd = (int)(blockIdx.x >> 3);
-  if (units_interleaved) {
-    const int uk = k_in_xcd / per_unit;
-    unit = xcd + 8 * uk;
-    rest = k_in_xcd - uk * per_unit;
+  if (units_grouped) {
+    const int G = units_grouped;
+    const int units_xcd = total_work / (8 * per_unit);
+    const int gi = k_in_xcd / (G * per_unit);
+    const int g_units = units_xcd - gi * G < G ? units_xcd - gi * G : G;  // the last group may be smaller
+    const int r = k_in_xcd - gi * G * per_unit;
+    const int rank = r / (g_units * inner);
+    const int rem = r - rank * g_units * inner;
+    const int ug = rem / inner;
+    unit = xcd + 8 * (gi * G + ug);
+    rest = rank * inner + (rem - ug * inner);
     return true;
   }
   const int wid = xcd * work_per_xcd + k_in_xcd;
@@ -114,7 +124,7 @@ constexpr int dkv_waves() {
 
 template <int D, int NW, bool SM, typename OutT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dkv_waves<D>(), dkv_waves<D>())))
-void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
+void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_grouped) {
   using T = DkvTiling<D, NW>;
   constexpr int NS = T::NS;
   constexpr int ND = T::ND;
@@ -122,7 +132,7 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
   int unit, j;
-  if (!work_item(p.c_nk, total_work, work_per_xcd, units_interleaved, unit, j)) return;
+  if (!work_item(p.c_nk, 1, total_work, work_per_xcd, units_grouped, unit, j)) return;
   // j ascending: under causal masks the first kv blocks have the longest columns
   const int b = unit / p.kv_heads;
   const int hk = unit - b * p.kv_heads;
@@ -471,7 +481,7 @@ struct PairTiling {
 
 template <int D, int NG, bool SM, typename OutT>
 __global__ __launch_bounds__(2 * NG * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
+void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_grouped) {
   using T = PairTiling<D, NG>;
   constexpr int NW = T::NW;
   constexpr int NS = T::NS;
@@ -482,7 +492,7 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
 
   const int sub = p.c_block_kv / T::KEYS;  // workgroups per kv block
   int unit, rest;
-  if (!work_item(p.c_nk * sub, total_work, work_per_xcd, units_interleaved, unit, rest)) return;
+  if (!work_item(p.c_nk * sub, sub, total_work, work_per_xcd, units_grouped, unit, rest)) return;
   const int j = rest / sub;
   const int part_of_block = rest - j * sub;
   const int b = unit / p.kv_heads;
@@ -823,7 +833,7 @@ constexpr int dq_waves() {
 
 template <int D, int NW, bool SM, typename OutT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_waves<D>(), dq_waves<D>())))
-void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_interleaved) {
+void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_grouped) {
   using T = DqTiling<D, NW>;
   constexpr int KC = T::KC;
   constexpr int NS = T::NS;
@@ -832,7 +842,7 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
 
   // unit = (b, K/V head) with its query heads; heaviest q blocks first
   int unit, rest;
-  if (!work_item(p.nq * p.kv_group, total_work, work_per_xcd, units_interleaved, unit, rest)) return;
+  if (!work_item(p.nq * p.kv_group, p.kv_group, total_work, work_per_xcd, units_grouped, unit, rest)) return;
   const int ri = rest / p.kv_group;
   const int i = p.nq - 1 - ri;
   const int b = unit / p.kv_heads;
@@ -1059,38 +1069,49 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
 
 struct Order {
   int64_t total, per_xcd;
-  int interleaved;
+  int grouped;
 };
-// Units: (b, K/V head); a grid of 8 * ceil(work / 8) ids.
-Order order_for(int64_t units, int64_t per_unit) {
+// Units: (b, K/V head); a grid of 8 * ceil(work / 8) ids. Units per group on
+// an XCD: the largest power of two up to 8 whose streamed tiles (unit_bytes
+// per unit), over all 8 XCDs at once, stay within about half of the 256 MB
+// last-level cache, as in the forward.
+Order order_for(int64_t units, int64_t per_unit, double unit_bytes) {
   const int64_t total = units * per_unit;
-  return {total, (total + 7) / 8, units % 8 == 0 ? 1 : 0};
+  int g = 0;
+  if (units % 8 == 0) {
+    g = 1;
+    while (g < 8 && 2 * g <= units / 8 && 2 * g * unit_bytes <= 16.0 * 1024 * 1024) g *= 2;
+  }
+  return {total, (total + 7) / 8, g};
 }
 
 template <int D, int NW, bool SM, typename OutT>
 hipError_t launch_dkv(const BwdParams& p, hipStream_t stream) {
-  const Order o = order_for((int64_t)p.B * p.kv_heads, p.c_nk);
+  // a dK/dV unit streams Q and dO of its kv_group query heads
+  const Order o = order_for((int64_t)p.B * p.kv_heads, p.c_nk, 4.0 * p.q_len * p.head_dim * p.kv_group);
   if (o.total == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dkv_bf16_kernel<D, NW, SM, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
-                     stream, p, (int)o.total, (int)o.per_xcd, o.interleaved);
+                     stream, p, (int)o.total, (int)o.per_xcd, o.grouped);
   return hipGetLastError();
 }
 
 template <int D, int NW, bool SM, typename OutT>
 hipError_t launch_dq(const BwdParams& p, hipStream_t stream) {
-  const Order o = order_for((int64_t)p.B * p.kv_heads, (int64_t)p.nq * p.kv_group);
+  // a dQ unit streams K and V of its K/V head
+  const Order o = order_for((int64_t)p.B * p.kv_heads, (int64_t)p.nq * p.kv_group, 4.0 * p.kv_len * p.head_dim);
   if (o.total == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NW, SM, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
-                     stream, p, (int)o.total, (int)o.per_xcd, o.interleaved);
+                     stream, p, (int)o.total, (int)o.per_xcd, o.grouped);
   return hipGetLastError();
 }
 
 template <int D, int NG, bool SM, typename OutT>
 hipError_t launch_dkv_pair(const BwdParams& p, hipStream_t stream) {
-  const Order o = order_for((int64_t)p.B * p.kv_heads, (int64_t)p.c_nk * (p.c_block_kv / (32 * NG)));
+  const Order o = order_for((int64_t)p.B * p.kv_heads, (int64_t)p.c_nk * (p.c_block_kv / (32 * NG)),
+                            4.0 * p.q_len * p.head_dim * p.kv_group);
   if (o.total == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dkv_pair_bf16_kernel<D, NG, SM, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(2 * NG * 64),
-                     0, stream, p, (int)o.total, (int)o.per_xcd, o.interleaved);
+                     0, stream, p, (int)o.total, (int)o.per_xcd, o.grouped);
   return hipGetLastError();
 }
 
