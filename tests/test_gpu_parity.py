@@ -252,6 +252,10 @@ GQA_CASES = [
     (1, 8, 2, 517, 517, 128, [CAUSAL], 128, 64, "docs", "bf16", "bshd"),
     (1, 6, 3, 290, 290, 128, [wl.local_causal(70)], 256, 128, None, "bf16", "bhsd"),
     (2, 4, 2, 200, 200, 64, [CAUSAL], 64, 64, "docs", "f32", "bhsd"),
+    # units (batch x K/V head) a multiple of 8, three and five per XCD: the
+    # XCD work order in groups of 2 and of 4 units, each with a smaller last group
+    (3, 8, 8, 200, 200, 64, [CAUSAL], 64, 64, None, "bf16", "bhsd"),
+    (1, 80, 40, 130, 130, 128, [CAUSAL, wl.local_causal(30)] * 40, 64, 64, None, "bf16", "bhsd"),
 ]
 
 
