@@ -656,6 +656,7 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
       nt = 0;
       settle(ng, ni);
     }
+    __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<0>();  // this wave's copies of the current tile are in LDS
     barrier_only();   // everyone's are; the other stage and the exchange are free again
     if (ng < G) issue_tile(stage ^ 1, ni, nt);
@@ -746,6 +747,10 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
       }
     }
     barrier_only();  // g of every key group is in LDS (the next tile's copies stay in flight)
+    // role 1 (dS, then dK) issues at raised priority until the next tile
+    // barrier, ahead of its role-0 partner on the SIMD (measured 1.8% faster
+    // at s3h; raising role 0 before the exchange instead was not faster)
+    if (role == 1) __builtin_amdgcn_s_setprio(1);
     if (role == 1) {
 #pragma unroll
       for (int u = 0; u < PARTS; ++u) {
