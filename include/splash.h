@@ -113,7 +113,10 @@ size_t splash_mask_info_entries(int B, int H, int q_len, int kv_len, int block_q
  * study notes section 21, data_next).
  * block_q, block_kv: positive, at most 1024. `info` must describe buffers of
  * the shape given above; its integer fields are checked against the call.
- * Segment ids are read on the device. Errors: INVALID_ARGUMENT (bad sizes,
+ * Segment ids are read on the device; with segment ids the build first uses
+ * data_next as its own scratch (per-block runs of equal ids) and then
+ * overwrites it with the result, so data_next must not be read by other work
+ * until the call's kernels have finished on `stream`. Errors: INVALID_ARGUMENT (bad sizes,
  * null pointers, one segment array without the other, info shape wrong),
  * HIP (launch failure / no device). */
 splash_status splash_mask_info_build(int B, int H, int q_len, int kv_len, int block_q,
