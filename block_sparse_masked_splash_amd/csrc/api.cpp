@@ -307,7 +307,8 @@ splash_status bwd_common(bool softmax, splash_dtype in_dtype, splash_dtype out_d
   if (!work) return ok();
   const int64_t nq = ceil_div(q_len, bq), nk = ceil_div(kv_len, bkv);
   const int64_t cnq = ceil_div(q_len, cbq), cnk = ceil_div(kv_len, cbkv);
-  if (nq * B * H >= (int64_t)1 << 31 || cnk * B * kv_heads >= (int64_t)1 << 31)
+  // (the dK/dV pass may split a kv block over up to block_kv / 32 workgroups)
+  if (nq * B * H >= (int64_t)1 << 31 || cnk * (cbkv / 32 > 1 ? cbkv / 32 : 1) * B * kv_heads >= (int64_t)1 << 31)
     return record_error(SPLASH_ERR_UNSUPPORTED, "too many workgroups for one launch");
 
   p.B = B;
@@ -493,8 +494,17 @@ splash_status mask_info_common(bool dkv, int B, int H, int q_len, int kv_len, in
                 info->block_kv);
   const int64_t entries = (int64_t)info->meta_batch * info->meta_heads * nq * nk;
   if (entries == 0) return ok();
-  if ((int64_t)info->meta_batch * info->meta_heads * nq / 4 >= ((int64_t)1 << 31))
+  if ((int64_t)info->meta_batch * info->meta_heads * nq / 4 >= ((int64_t)1 << 31) ||
+      (int64_t)info->meta_batch * info->meta_heads * nk / 4 >= ((int64_t)1 << 31))
     return record_error(SPLASH_ERR_UNSUPPORTED, "too many metadata rows for one launch");
+  // the segment-id classification runs one wavefront per 64 entries of a row
+  // (or column), four wavefronts per workgroup
+  if (seg) {
+    const int64_t lines = (int64_t)info->meta_batch * info->meta_heads * (dkv ? nk : nq);
+    const int64_t waves = lines * ceil_div(dkv ? nq : nk, 64);
+    if (waves / 4 >= ((int64_t)1 << 31))
+      return record_error(SPLASH_ERR_UNSUPPORTED, "too many metadata entries for one launch");
+  }
   if (info->block_mask == nullptr || info->data_next == nullptr)
     return record_error(SPLASH_ERR_INVALID_ARGUMENT, "info arrays are null");
   p.B = B;

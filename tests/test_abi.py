@@ -217,6 +217,24 @@ def test_mask_info_build_dkv_validation_errors():
                                           None) == bd.SPLASH_OK
 
 
+def test_mask_info_build_too_large_for_one_launch():
+    """Metadata whose build would need more workgroups than one launch takes
+    is refused on the host: columns of the dK/dV layout, and the segment-id
+    classification (one wavefront per 64 entries)."""
+    lib = bd.load_library()
+    heads = [(1, -1, -1)] * 256
+    d, keep = _desc(heads=heads)
+    big = 1 << 30
+    info = _info(Hm=256, nq=1, nk=big, bq=64, bkv=1)
+    assert lib.splash_mask_info_build_dkv(1, 256, 64, big, 64, 1, ctypes.byref(d), ctypes.byref(info), None) == \
+        bd.SPLASH_ERR_UNSUPPORTED
+    ds, keep_s = _desc(qseg=0x1000, kvseg=0x2000)
+    info = _info(nq=big, nk=big, bq=1, bkv=1)
+    assert lib.splash_mask_info_build(1, 1, big, big, 1, 1, ctypes.byref(ds), ctypes.byref(info), None) == \
+        bd.SPLASH_ERR_UNSUPPORTED
+    assert b"too many metadata entries" in lib.splash_last_error()
+
+
 def test_softmax_entry_points_validation_errors():
     """splash_fwd_lse, splash_softmax_bwd_preprocess and splash_softmax_bwd
     reject bad arguments on the host (nothing is launched)."""
