@@ -105,6 +105,11 @@ splash_status check_tensor(const char* name, const void* ptr, const int64_t* str
       return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s stride %d (%lld elements) breaks 16-byte row alignment", name, a,
                   (long long)strides[a]);
   }
+  // tiles of up to 64 rows are copied through buffer resources whose offsets
+  // and sizes are 32-bit: rows must lie less than 64 MiB apart
+  if (strides[2] * elem_bytes >= ((int64_t)1 << 26))
+    return record_error(SPLASH_ERR_UNSUPPORTED, "%s rows are %lld bytes apart (at most 64 MiB - 16 supported)", name,
+                        (long long)(strides[2] * elem_bytes));
   return SPLASH_OK;
 }
 

@@ -135,7 +135,10 @@ splash_status splash_mask_info_build(int B, int H, int q_len, int kv_len, int bl
  * batch, head and sequence axes (int64, HOST arrays of 3); head_dim is
  * contiguous. This covers both [B,H,S,D] and the [B,S,H,D] layout of
  * "hstu_ops.py" pointwise_splash_attention without copies. Every row must
- * start 16-byte aligned (base pointers and strides accordingly).
+ * start 16-byte aligned (base pointers and strides accordingly), and
+ * consecutive rows of a tensor must lie less than 64 MiB apart
+ * (UNSUPPORTED otherwise; the same holds for every tensor of the backward
+ * entry points).
  *
  * Supported: in_dtype/out_dtype F32/F32, BF16/BF16 or BF16/F32; head_dim 64 or
  * 128; block_q in {64, 128, 256} and block_kv in {64, 128}. Arithmetic: F32 inputs are computed

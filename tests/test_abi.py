@@ -94,6 +94,10 @@ def test_forward_validation_errors(fn):
     assert _fwd(lib, fn, k=0x200002, desc=d, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
     bad = [bd._I64x3(256 * 128, 256 * 128, 130)] * 4
     assert _fwd(lib, fn, strides=bad, desc=d, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
+    # rows 64 MiB or more apart (tile copies use 32-bit buffer offsets)
+    far = [bd._I64x3(256 * 128, 256 * 128, 128)] * 3 + [bd._I64x3(0, 0, 1 << 25)]
+    assert _fwd(lib, fn, strides=far, desc=d, info=inf) == E.SPLASH_ERR_UNSUPPORTED
+    assert b"apart" in lib.splash_last_error()
     # segment ids: both or neither
     d1, keep1 = _desc(qseg=0x5000)
     assert _fwd(lib, fn, desc=d1, info=inf) == E.SPLASH_ERR_INVALID_ARGUMENT
