@@ -12,9 +12,11 @@
 //
 // The causal / window part of a head's mask is a band k - q in [lo, hi] with
 // lo <= 0 <= hi, so its class has a closed form per block. Segment ids are
-// arbitrary integers: where they are given, every block the band leaves
-// non-empty is classified by one workgroup, from the id ranges when they
-// decide it, else by comparing all its pairs.
+// arbitrary integers: where they are given, each q block and kv block is first
+// reduced to its runs of equal ids, and an entry whose two blocks have few
+// runs is classified from the rectangles those runs form, each with one id on
+// either side, by the band's closed form; other entries compare all their
+// pairs (the segment path below).
 // data_next is then a suffix scan of each metadata row, one wavefront per
 // row: the row is walked back to front in chunks of 64 kv blocks, a ballot
 // marks the non-empty ones, and each lane takes the lowest marked block at or
