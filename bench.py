@@ -149,7 +149,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the work shards by (batch, head) with no exchange; see the design notes)", file=sys.stderr)
+              "(the work shards by (batch, head) with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -306,9 +306,9 @@ splash_status splash_pointwise_bwd(splash_dtype in_dtype, splash_dtype out_dtype
 
 /* ---- Softmax log-sum-exp and backward ----
  *
- * The pages give the softmax forward (study notes "JAX 到 VLIW ...", sections
- * 12 and 15) and, for the pointwise variant, the custom_vjp pattern in which
- * the forward hands the backward its residuals ("hstu_ops.py"). The softmax
+ * The study notes "JAX 到 VLIW ..." give the softmax forward (sections 12 and
+ * 15); "hstu_ops.py" gives, for the pointwise variant, the custom_vjp pattern
+ * in which the forward hands the backward its residuals. The softmax
  * backward here is the gradient of the softmax definition with the
  * forward's per-row log-sum-exp as the residual: with x = scale q·k,
  *   LSE_q = log sum_k e^{x_qk} (allowed keys; -inf for a row with none),
