@@ -133,3 +133,49 @@ def test_random_backward_matches_oracle(gpu_device, seed):
               _seg(g["q_segment_ids"]), _seg(g["kv_segment_ids"]))
     for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
         print(name, check_close_grad(to64(got), want, f"fuzz backward {seed} {name}"))
+
+
+N_DENSE = 8
+
+
+@pytest.mark.parametrize("seed", range(N_DENSE))
+def test_random_dense_mask_forward_matches_oracle(gpu_device, seed):
+    """Arbitrary boolean masks (per head or shared, of random density, with
+    runs of allowed keys) ANDed with random head masks, block sizes, head
+    counts and dtypes."""
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.choice([1, 2]))
+    Hk = int(rng.choice([1, 2]))
+    H = Hk * int(rng.choice([1, 2]))
+    Sq, Skv = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+    D = int(rng.choice([64, 128]))
+    bq, bkv = int(rng.choice([64, 128, 256])), int(rng.choice([64, 128]))
+    heads = [_head_mask(rng) for _ in range(1 if rng.random() < 0.5 else H)]
+    dt = "f32" if rng.random() < 0.2 else "bf16"
+    pointwise = seed % 2 == 1
+    # per-head or shared mask: random bits, or runs of allowed keys around a random diagonal
+    nh = H if rng.random() < 0.5 else 1
+    if rng.random() < 0.5:
+        dense = rng.random((nh, Sq, Skv)) < rng.uniform(0.05, 0.9)
+    else:
+        qi = np.arange(Sq)[:, None]
+        ki = np.arange(Skv)[None, :]
+        dense = np.stack([np.abs(ki - qi - int(rng.integers(-50, 50))) < int(rng.integers(1, 80)) for _ in range(nh)])
+    if nh == 1:
+        dense = dense[0]
+    print(f"fuzz dense seed {seed}: B={B} H={H} Hk={Hk} Sq={Sq} Skv={Skv} D={D} blocks {bq}x{bkv} heads={heads} "
+          f"{dt} pointwise={pointwise} mask heads={nh}", flush=True)
+    sigma = 0.5 if pointwise else 1.0
+    c = wl.random_case(77 * seed + 3, B, H, Sq, Skv, D, dt, sigma=sigma)
+    kv = wl.random_case(77 * seed + 4, B, Hk, Sq, Skv, D, dt, sigma=sigma)
+    q, k, v = c["q"].to(gpu_device), kv["k"].to(gpu_device), kv["v"].to(gpu_device)
+    info = sp.dense_mask_info_build(B, H, torch.from_numpy(dense), heads, bq, bkv, device=gpu_device)
+    bm, dn = oracle.mask_info(B, H, Sq, Skv, bq, bkv, heads, dense=dense)
+    assert np.array_equal(info.block_mask.cpu().numpy(), bm)
+    assert np.array_equal(info.data_next.cpu().numpy(), dn)
+    fn = sp.pointwise_fwd if pointwise else sp.splash_fwd
+    out = fn(q, k, v, info)
+    torch.cuda.synchronize()
+    ofn = oracle.pointwise_attention if pointwise else oracle.softmax_attention
+    ref = ofn(to64(c["q"]), to64(kv["k"]), to64(kv["v"]), 1 / math.sqrt(D), heads, dense=dense)
+    print(check_close(to64(out), ref, dt, f"fuzz dense {seed}"))
