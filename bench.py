@@ -9,7 +9,9 @@ S=8192, D=128, bf16, 128x128 blocks. Prints one JSON line.
   python bench.py [--steps K] [--warmup W] [--workload c3h] [--no-cpu-baseline]
 
 Throughput counts 4*bq*bkv*D FLOPs per non-empty (b, h, i, j) block (the
-QKᵀ and P·V products of every block that is not skipped).
+QKᵀ and P·V products of every block that is not skipped). The element-exact
+count, 4*D per allowed (q, k) pair, is reported beside it
+(config.element_flops, config.element_tflops).
 """
 
 from __future__ import annotations
@@ -25,7 +27,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix peak: 256 CU x 4096 FLOP/clk x 2.4 GHz
-PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector peak
+# fp32 vector peak for the instructions the fp32 kernel can issue: packed
+# fp32 (two FMAs per lane) is disabled in this build, so one FMA per lane per
+# clock: 256 CU x 4 SIMD x 16 lanes x 2 FLOP x 2.4 GHz (AMD's 157.3 counts
+# packed FMAs)
+PEAK_F32_TFLOPS = 78.6
 METRIC = "splash fwd TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, causal S=8192"
 # the backward workloads report the same kind of figure for the backward pass
 BWD_METRIC = "splash bwd TFLOP/s (unmasked FLOPs, 5 products per block) + % bf16 MFMA peak"
@@ -58,57 +64,183 @@ def traffic_for(workload: str, backward: bool = False):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, gen, budget_s: float = 12.0):
-    """The oracle, as it is, on a bounded sample of the same workload: whole
-    query blocks of several (b, h), timed on the host cores."""
+def allowed_pairs(w, gen) -> int:
+    """Allowed (query, key) pairs summed over every (batch, head), counted row
+    by row, for the element-exact FLOP count (4 * D per pair).
+
+    A head mask is a band lo <= k - q <= hi (causal: hi <= 0), so query q
+    keeps the keys [max(0, q + lo), min(S - 1, q + hi)]; packed documents
+    (segment ids that are runs of equal values, as the workloads draw them)
+    clip that interval to q's document. A dense mask is counted from its bits,
+    ANDed with the band."""
     import numpy as np
-    import torch
+
+    S = w.S
+    q = np.arange(S, dtype=np.int64)
+    big = 1 << 40
+
+    def band(head):
+        causal, wl_, wr = (int(x) for x in head)
+        lo = -wl_ if wl_ >= 0 else -big
+        hi = wr if wr >= 0 else big
+        return lo, (min(hi, 0) if causal else hi)
+
+    heads = [w.head_masks[0] if len(w.head_masks) == 1 else w.head_masks[h] for h in range(w.H)]
+    if gen.get("dense") is not None:
+        d = gen["dense"].numpy().astype(bool)
+        k = np.arange(S, dtype=np.int64)[None, :]
+        total = 0
+        for head in heads:
+            lo, hi = band(head)
+            dd = (k - q[:, None] >= lo) & (k - q[:, None] <= hi)
+            total += int((d & dd).sum())
+        return w.B * total
+    seg = gen.get("q_segment_ids")
+    total = 0
+    for b in range(w.B if seg is not None else 1):
+        a0, e0 = np.zeros(S, dtype=np.int64), np.full(S, S - 1, dtype=np.int64)
+        if seg is not None:
+            ids = seg[b].numpy()
+            change = np.flatnonzero(np.diff(ids)) + 1
+            starts = np.concatenate([[0], change])
+            ends = np.concatenate([change - 1, [S - 1]])
+            run = np.repeat(np.arange(starts.size), ends - starts + 1)
+            a0, e0 = starts[run], ends[run]
+        for head in heads:
+            lo, hi = band(head)
+            a = np.maximum(a0, q + lo)
+            e = np.minimum(e0, q + hi)
+            total += int(np.maximum(e - a + 1, 0).sum())
+    return total * (1 if seg is not None else w.B)
+
+
+_BLAS_LIMIT = None
+
+
+def _cpu_worker_init():
+    # one BLAS thread per worker process (the pool's processes are the
+    # cores); set before numpy loads its BLAS, and enforced once it has
+    global _BLAS_LIMIT
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        os.environ[var] = "1"
+    import numpy  # noqa: F401  (imported before timing starts)
+    import oracle  # noqa: F401
+    try:
+        from threadpoolctl import threadpool_limits
+        _BLAS_LIMIT = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        pass
+
+
+def _cpu_ready(_):
+    return os.getpid()
+
+
+def _cpu_task(task):
+    """One oracle task of the CPU baseline: some query blocks of one (batch,
+    head), forward (or backward) rows formed by the fp64 oracle. Returns the
+    block FLOPs it covered."""
+    import numpy as np
     import oracle
 
+    (S, bq, bkv, D, scale, head, pointwise, backward, blocks, q, k, v, do, qs, dense) = task
+    k64, v64 = k.astype(np.float64), v.astype(np.float64)
+    flops = 0
+    for n, i in enumerate(blocks):
+        rows = np.arange(i * bq, min(S, (i + 1) * bq))
+        m = oracle.element_mask(S, S, head, qs, qs, rows=rows, dense=dense)
+        q64 = q[n].astype(np.float64)
+        if backward:
+            do64 = do[n].astype(np.float64)
+            if pointwise:
+                oracle.pointwise_attention_bwd_rows(q64, k64, v64, do64, scale, m, S)
+            else:
+                oracle.softmax_attention_bwd_rows(q64, k64, v64, do64, scale, m)
+        elif pointwise:
+            oracle.pointwise_attention_rows(q64, k64, v64, scale, m, S)
+        else:
+            oracle.softmax_attention_rows(q64, k64, v64, scale, m)
+        cls, _ = oracle.mask_info_row(S, S, bq, bkv, head, i, qs, qs, dense=dense)
+        flops += int(np.count_nonzero(cls)) * (10 if backward else 4) * bq * bkv * D
+    return flops
+
+
+def _cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, gen, budget_s: float = 12.0, single_s: float = 5.0):
+    """The oracle, as it is, on a bounded sample of the same workload: tasks of
+    a few whole query blocks of one random (b, h), run by a process pool with
+    one worker per core of this process's CPU share (at most 16) and one BLAS
+    thread per worker, for about ``budget_s`` seconds; then the same kind of
+    sample in one process on one core for about ``single_s`` seconds. Runs
+    before anything touches the GPU (the pool's processes are started fresh,
+    not forked)."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    try:
+        share = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        share = os.cpu_count() or 1
+    workers = max(1, min(share, os.cpu_count() or 1, 16))
     rng = np.random.default_rng(12345)
     S, bq, bkv, D = w.S, w.block_q, w.block_kv, w.D
     nq = -(-S // bq)
-    qs = gen["q_segment_ids"]
-    qs = None if qs is None else qs.numpy()
+    per_task = 1 if w.backward else 4
+    qs_all = gen["q_segment_ids"]
     dense = None if gen["dense"] is None else gen["dense"].numpy()
-    flops = 0
-    done = 0
-    t0 = time.perf_counter()
-    cache = {}
-    while time.perf_counter() - t0 < budget_s or done < 4:
-        b, h, i = int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(nq))
-        hk = oracle.kv_head_of(h, w.H, w.n_kv_heads)
-        if (b, hk) not in cache:
-            cache.clear()
-            cache[(b, hk)] = (gen["k"][b, hk].to(torch.float64).numpy(), gen["v"][b, hk].to(torch.float64).numpy())
-        k64, v64 = cache[(b, hk)]
-        rows = np.arange(i * bq, min(S, (i + 1) * bq))
-        head = w.head_masks[0] if len(w.head_masks) == 1 else w.head_masks[h]
-        m = oracle.element_mask(S, S, head, None if qs is None else qs[b], None if qs is None else qs[b], rows=rows,
-                                dense=dense)
-        q64 = gen["q"][b, h, rows[0]:rows[-1] + 1].to(torch.float64).numpy()
-        if w.backward:
-            do64 = gen["d_o"][b, h, rows[0]:rows[-1] + 1].to(torch.float64).numpy()
-            if w.pointwise:
-                oracle.pointwise_attention_bwd_rows(q64, k64, v64, do64, w.scale, m, S)
-            else:
-                oracle.softmax_attention_bwd_rows(q64, k64, v64, do64, w.scale, m)
-        elif w.pointwise:
-            oracle.pointwise_attention_rows(q64, k64, v64, w.scale, m, S)
-        else:
-            oracle.softmax_attention_rows(q64, k64, v64, w.scale, m)
-        cls, _ = oracle.mask_info_row(S, S, bq, bkv, head, i, None if qs is None else qs[b],
-                                      None if qs is None else qs[b], dense=dense)
-        flops += int(np.count_nonzero(cls)) * (10 if w.backward else 4) * bq * bkv * D
-        done += 1
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} query blocks of {bq} rows on random (b, h), fp64 numpy, {dt:.1f} s"}
+
+    def tasks():
+        while True:
+            b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
+            hk = h // (w.H // w.n_kv_heads)
+            blocks = sorted(int(x) for x in rng.integers(nq, size=per_task))
+            head = w.head_masks[0] if len(w.head_masks) == 1 else w.head_masks[h]
+            q = [gen["q"][b, h, i * bq:min(S, (i + 1) * bq)].float().numpy() for i in blocks]
+            do = None
+            if w.backward:
+                do = [gen["d_o"][b, h, i * bq:min(S, (i + 1) * bq)].float().numpy() for i in blocks]
+            yield (S, bq, bkv, D, w.scale, head, w.pointwise, w.backward, blocks, q,
+                   gen["k"][b, hk].float().numpy(), gen["v"][b, hk].float().numpy(), do,
+                   None if qs_all is None else qs_all[b].numpy(), dense)
+
+    def run(pool, n_workers, budget):
+        # every worker started and initialised before the clock starts
+        pool.map(_cpu_ready, range(4 * n_workers), chunksize=1)
+        it = tasks()
+        pending, flops, done = [], 0, 0
+        t0 = time.perf_counter()
+        while True:
+            while len(pending) < 2 * n_workers and (time.perf_counter() - t0 < budget or done + len(pending) < 2):
+                pending.append(pool.apply_async(_cpu_task, (next(it),)))
+            if not pending:
+                break
+            flops += pending.pop(0).get()
+            done += 1
+        return flops, done, time.perf_counter() - t0
+
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
+        flops, done, dt = run(pool, workers, budget_s)
+    with ctx.Pool(1, initializer=_cpu_worker_init) as pool:
+        f1, d1, t1 = run(pool, 1, single_s)
+    blocks_desc = "one query block" if per_task == 1 else f"{per_task} query blocks"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": (f"{done} tasks ({blocks_desc} of {bq} rows of one random (b, h) each), fp64 numpy oracle, "
+                       f"{workers} worker processes x 1 BLAS thread, {dt:.1f} s wall"),
+            "single_core": {"value": f1 / t1 / 1e12, "tasks": d1, "seconds": round(t1, 1)},
+            "cpu_count": os.cpu_count(), "cpu_share": share, "cpu_model": _cpu_model(),
+            "blas_threads_per_worker": 1}
 
 
 def gemm_reference(dev, n: int = 8192, reps: int = 10) -> float:
@@ -157,8 +289,11 @@ def main():
     from block_sparse_masked_splash_amd import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
     gen = wl.generate(w)
+    pairs = allowed_pairs(w, gen)
+    # the oracle's CPU baseline runs first, before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, gen)
+    dev = torch.device("cuda:0")
     q, k, v = (gen[n].to(dev) for n in ("q", "k", "v"))
     seg = None if gen["q_segment_ids"] is None else gen["q_segment_ids"].to(dev)
     fwd = sp.pointwise_fwd if w.pointwise else sp.splash_fwd
@@ -278,6 +413,8 @@ def main():
                    "seq_len": w.S,
                    "head_dim": w.D, "block_q": w.block_q, "block_kv": w.block_kv,
                    "nonempty_blocks": blocks, "flops_per_step": flops,
+                   "allowed_pairs": pairs, "element_flops": pairs * (10 if w.backward else 4) * w.D,
+                   "element_tflops": round(pairs * (10 if w.backward else 4) * w.D / (ms_per_step * 1e-3) / 1e12, 3),
                    "step": (f"{fwd_name} (dense-mask metadata built once on the host, before timing)"
                             if dense is not None else
                             "mask_info_build + mask_info_build_dkv + " + fwd_name if w.backward else
@@ -292,8 +429,8 @@ def main():
         g = gemm_reference(dev)
         line["bf16_gemm_reference"] = {"tflops": round(g, 1), "what": "torch bf16 GEMM 8192^3 on N(0,1) operands",
                                        "fwd_fraction_of_it": round(achieved / g, 4)}
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, gen)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

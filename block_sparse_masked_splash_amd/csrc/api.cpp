@@ -65,6 +65,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool len_ok(int x) { return x >= 0 && x <= splash::kMaxLen; }
 
+// Metadata, segment ids and row statistics are read as aligned 32-bit words.
+bool misaligned4(const void* p) { return p != nullptr && reinterpret_cast<uintptr_t>(p) % 4 != 0; }
+
 // Checks the mask description against B and H; fills the head bands.
 splash_status check_mask(int H, const splash_mask_desc* mask, splash::HeadBand* band) {
   if (mask == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "mask is null");
@@ -76,6 +79,8 @@ splash_status check_mask(int H, const splash_mask_desc* mask, splash::HeadBand* 
   if (mask->heads == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "mask->heads is null");
   if ((mask->q_segment_ids == nullptr) != (mask->kv_segment_ids == nullptr))
     return record_error(SPLASH_ERR_INVALID_ARGUMENT, "both or neither of q_segment_ids and kv_segment_ids must be given");
+  if (misaligned4(mask->q_segment_ids) || misaligned4(mask->kv_segment_ids))
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "segment ids must be 4-byte aligned");
   for (int h = 0; h < nm; ++h)
     if (!splash::head_band(mask->heads[h], h, &band[h])) return SPLASH_ERR_INVALID_ARGUMENT;
   return SPLASH_OK;
@@ -148,6 +153,7 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
   if (lse_strides != nullptr) {  // log-sum-exp requested (softmax only)
     if (pointwise) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "log-sum-exp is defined for softmax only");
     if (work && lse == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse is null");
+    if (misaligned4(lse)) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
     if (lse_strides[0] < 0 || lse_strides[1] < 0)
       return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse strides must be >= 0");
   }
@@ -174,11 +180,15 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
                 bq, bkv);
   if (work && nk > 0 && (info->block_mask == nullptr || info->data_next == nullptr))
     return record_error(SPLASH_ERR_INVALID_ARGUMENT, "info arrays are null");
+  if (misaligned4(info->block_mask) || misaligned4(info->data_next))
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "info arrays must be 4-byte aligned");
   if (partial != nullptr) {
     if (partial->num_blocks < 0 || partial->num_blocks > ((int64_t)1 << 31))
       return record_error(SPLASH_ERR_INVALID_ARGUMENT, "num_blocks=%lld", (long long)partial->num_blocks);
     if (work && nk > 0 && (partial->mask_next == nullptr || (partial->num_blocks > 0 && partial->mask_blocks == nullptr)))
       return record_error(SPLASH_ERR_INVALID_ARGUMENT, "dense mask arrays are null");
+    if (misaligned4(partial->mask_next) || misaligned4(partial->mask_blocks))
+      return record_error(SPLASH_ERR_INVALID_ARGUMENT, "dense mask arrays must be 4-byte aligned");
   }
   if (!work) return ok();
   if (nq * B * H >= (int64_t)1 << 31)
@@ -246,6 +256,8 @@ splash_status check_info(const char* what, const splash_mask_info* info, int B, 
   (void)H;
   if (work && nq > 0 && nk > 0 && (info->block_mask == nullptr || info->data_next == nullptr))
     return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s arrays are null", what);
+  if (misaligned4(info->block_mask) || misaligned4(info->data_next))
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s arrays must be 4-byte aligned", what);
   return SPLASH_OK;
 }
 
@@ -512,6 +524,8 @@ splash_status mask_info_common(bool dkv, int B, int H, int q_len, int kv_len, in
   }
   if (info->block_mask == nullptr || info->data_next == nullptr)
     return record_error(SPLASH_ERR_INVALID_ARGUMENT, "info arrays are null");
+  if (misaligned4(info->block_mask) || misaligned4(info->data_next))
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "info arrays must be 4-byte aligned");
   p.B = B;
   p.H = H;
   p.q_len = q_len;

@@ -46,12 +46,15 @@ __device__ inline void wait_vmcnt() {
 }
 
 // Direct HBM -> LDS copies through a buffer resource: every active lane
-// fetches 16 (or 4) bytes at byte offset voff + soff of the buffer, and lane
-// L's bytes land at LDS byte address lds + 16 L (4 L). Offsets at or past the
+// fetches 16 (or 4) bytes at byte offset voff of the buffer, and lane L's
+// bytes land at LDS byte address lds + 16 L (4 L). Offsets at or past the
 // buffer's size read as zero, which clips a tile at the end of the sequence
-// with no per-lane arithmetic. Issued through asm so that the compiler does
-// not treat the tile being filled as a pending write to every LDS read that
-// follows; completion is awaited explicitly with wait_vmcnt.
+// with no per-lane arithmetic. The hardware range check covers the VGPR
+// offset (plus the instruction offset) only, not the SGPR offset, so every
+// part of a lane's offset travels in voff and the SGPR offset is 0. Issued
+// through asm so that the compiler does not treat the tile being filled as a
+// pending write to every LDS read that follows; completion is awaited
+// explicitly with wait_vmcnt.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // 32-bit data format, no swizzle, no stride
 
@@ -64,50 +67,48 @@ __device__ inline u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
   r[3] = kRawBufferWord3;
   return r;
 }
-__device__ inline void lds_copy4(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
-               "s"(soff), "s"(lds)
+__device__ inline void lds_copy4(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(lds)
                : "memory", "m0");
 }
-// N 16-byte-per-lane copies of row groups: copy n reads at byte offset
-// vo_n + soff0 + n * gstep of the buffer and writes LDS lds0 + n * LSTEP
-// (64 lanes x 16 bytes each). The offsets advance in SGPRs inside one asm
-// block, so no per-copy constant is kept live and no per-copy setup is spent.
+// N 16-byte-per-lane copies of row groups: copy n reads the buffer at the
+// lane's byte offset vo[n] (its whole offset, range-checked) and writes LDS
+// lds0 + n * LSTEP (64 lanes x 16 bytes each). m0 advances inside one asm
+// block, so no per-copy LDS address is kept live.
 #define SPLASH_COPY1(V)                                         \
   "s_nop 0\n\t"                                                 \
-  "buffer_load_dwordx4 " V ", %[rs], %[so] offen lds\n\t"       \
-  "s_add_u32 m0, m0, %[ls]\n\t"                                 \
-  "s_add_u32 %[so], %[so], %[gs]\n\t"
+  "buffer_load_dwordx4 " V ", %[rs], 0 offen lds\n\t"          \
+  "s_add_u32 m0, m0, %[ls]\n\t"
 template <int N, int LSTEP>
-__device__ inline void lds_copy_rows(u32x4 rsrc, const uint32_t (&vo)[N], uint32_t soff0, uint32_t gstep,
-                                     uint32_t lds0) {
+__device__ inline void lds_copy_rows(u32x4 rsrc, const uint32_t (&vo)[N], uint32_t lds0) {
   static_assert(N == 1 || N == 2 || N == 4 || N == 8, "copy count");
-  uint32_t so = soff0;
   if constexpr (N == 1) {
-    asm volatile("s_mov_b32 m0, %[lds]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[v0], %[rs], %[so] offen lds"
-                 : [so] "+s"(so)
+    asm volatile("s_mov_b32 m0, %[lds]\n\ts_nop 0\n\tbuffer_load_dwordx4 %[v0], %[rs], 0 offen lds"
+                 :
                  : [lds] "s"(lds0), [rs] "s"(rsrc), [v0] "v"(vo[0])
                  : "memory", "m0");
   } else if constexpr (N == 2) {
     asm volatile("s_mov_b32 m0, %[lds]\n\t" SPLASH_COPY1("%[v0]") SPLASH_COPY1("%[v1]")
-                 : [so] "+s"(so)
-                 : [lds] "s"(lds0), [rs] "s"(rsrc), [gs] "s"(gstep), [ls] "i"(LSTEP), [v0] "v"(vo[0]), [v1] "v"(vo[1])
+                 :
+                 : [lds] "s"(lds0), [rs] "s"(rsrc), [ls] "i"(LSTEP), [v0] "v"(vo[0]), [v1] "v"(vo[1])
                  : "memory", "m0", "scc");
   } else if constexpr (N == 4) {
     asm volatile("s_mov_b32 m0, %[lds]\n\t" SPLASH_COPY1("%[v0]") SPLASH_COPY1("%[v1]")
                      SPLASH_COPY1("%[v2]") SPLASH_COPY1("%[v3]")
-                 : [so] "+s"(so)
-                 : [lds] "s"(lds0), [rs] "s"(rsrc), [gs] "s"(gstep), [ls] "i"(LSTEP), [v0] "v"(vo[0]), [v1] "v"(vo[1]), [v2] "v"(vo[2]),
-                   [v3] "v"(vo[3])
+                 :
+                 : [lds] "s"(lds0), [rs] "s"(rsrc), [ls] "i"(LSTEP), [v0] "v"(vo[0]), [v1] "v"(vo[1]),
+                   [v2] "v"(vo[2]), [v3] "v"(vo[3])
                  : "memory", "m0", "scc");
   } else {
     asm volatile("s_mov_b32 m0, %[lds]\n\t" SPLASH_COPY1("%[v0]") SPLASH_COPY1("%[v1]")
                      SPLASH_COPY1("%[v2]") SPLASH_COPY1("%[v3]")
                          SPLASH_COPY1("%[v4]") SPLASH_COPY1("%[v5]")
                              SPLASH_COPY1("%[v6]") SPLASH_COPY1("%[v7]")
-                 : [so] "+s"(so)
-                 : [lds] "s"(lds0), [rs] "s"(rsrc), [gs] "s"(gstep), [ls] "i"(LSTEP), [v0] "v"(vo[0]), [v1] "v"(vo[1]), [v2] "v"(vo[2]),
-                   [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5]), [v6] "v"(vo[6]), [v7] "v"(vo[7])
+                 :
+                 : [lds] "s"(lds0), [rs] "s"(rsrc), [ls] "i"(LSTEP), [v0] "v"(vo[0]), [v1] "v"(vo[1]),
+                   [v2] "v"(vo[2]), [v3] "v"(vo[3]), [v4] "v"(vo[4]), [v5] "v"(vo[5]), [v6] "v"(vo[6]),
+                   [v7] "v"(vo[7])
                  : "memory", "m0", "scc");
   }
 }
@@ -232,7 +233,9 @@ __device__ inline void transpose_operand_offsets(int lane, int (&off)[2][D / 32]
 // of wave w covers rows (n NW + w) RPI .. + RPI - 1 (RPI = 64 / (D / 8) rows
 // per copy instruction); lane L writes row RPI (n NW + w) + L / CPR at chunk
 // position L % CPR, so it fetches the logical chunk stored there. The swizzle
-// only sees row & 15, so the offset only depends on (n NW + w) & 3.
+// only sees row & 15, so the chunk choice only depends on (n NW + w) & 3.
+// Each offset is the lane's whole byte offset from the tile's first row, so
+// the buffer's range check clips every row past the end of the sequence.
 template <int D, int NW, int LOADS>
 __device__ inline void tile_copy_offsets(int lane, int wave, int64_t row_bytes, uint32_t (&sel)[LOADS]) {
   constexpr int CPR = D / 8, RPI = 64 / CPR;
@@ -247,7 +250,8 @@ __device__ inline void tile_copy_offsets(int lane, int wave, int64_t row_bytes, 
     vo[v4] = (uint32_t)(rr * row_bytes + chunk * 16);
   }
 #pragma unroll
-  for (int n = 0; n < LOADS; ++n) sel[n] = vo[(n * NW + wave) & 3];
+  for (int n = 0; n < LOADS; ++n)
+    sel[n] = vo[(n * NW + wave) & 3] + (uint32_t)((n * NW + wave) * RPI * row_bytes);
 }
 
 }  // namespace

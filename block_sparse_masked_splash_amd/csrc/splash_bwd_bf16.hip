@@ -171,16 +171,10 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
   row_operand_offsets<D>(lane, aoff);
   int toff[2][ND];
   transpose_operand_offsets<D>(lane, toff);
-  // each wavefront's first row group folded into its lane offsets
   const uint32_t q_rs = (uint32_t)(p.q_ss * 2), do_rs = (uint32_t)(p.do_ss * 2);
   uint32_t qsel[T::LOADS], dsel[T::LOADS];
   tile_copy_offsets<D, NW>(lane, wave, q_rs, qsel);
   tile_copy_offsets<D, NW>(lane, wave, do_rs, dsel);
-#pragma unroll
-  for (int n = 0; n < T::LOADS; ++n) {
-    qsel[n] += wave * T::RPI * q_rs;
-    dsel[n] += wave * T::RPI * do_rs;
-  }
   const int32_t* qseg_b = p.q_seg + (int64_t)b * p.q_len;
 
   // ---- column walk over (query head of the group, q block, 32-query tile) ----
@@ -235,21 +229,21 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
     char* ddst = qdst + T::TILE;
     const u32x4 qrs = buffer_rsrc(q_h + (int64_t)q0 * q_rs, (uint32_t)rows * q_rs);
     const u32x4 drs = buffer_rsrc(do_h + (int64_t)q0 * do_rs, (uint32_t)rows * do_rs);
-    lds_copy_rows<T::LOADS, NW * 1024>(qrs, qsel, 0u, NW * T::RPI * q_rs, lds_addr(qdst + wave * T::RPI * T::ROWB));
-    lds_copy_rows<T::LOADS, NW * 1024>(drs, dsel, 0u, NW * T::RPI * do_rs, lds_addr(ddst + wave * T::RPI * T::ROWB));
+    lds_copy_rows<T::LOADS, NW * 1024>(qrs, qsel, lds_addr(qdst + wave * T::RPI * T::ROWB));
+    lds_copy_rows<T::LOADS, NW * 1024>(drs, dsel, lds_addr(ddst + wave * T::RPI * T::ROWB));
     if (has_seg) {
       const uint32_t sdst =
           lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * QC + wave * T::SEG_ROWS);
       const u32x4 srs = buffer_rsrc(qseg_b + q0, (uint32_t)(rows * 4));
-      if (lane < T::SEG_ROWS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), sdst);
+      if (lane < T::SEG_ROWS) lds_copy4(srs, (uint32_t)((wave * T::SEG_ROWS + lane) * 4), sdst);
     }
     if constexpr (SM) {
       float* st = reinterpret_cast<float*>(smem + T::STAT_OFF) + stage * 2 * QC + wave * T::SEG_ROWS;
       const u32x4 lrs = buffer_rsrc(lse_h + q0, (uint32_t)(rows * 4));
       const u32x4 drs2 = buffer_rsrc(delta_h + q0, (uint32_t)(rows * 4));
       if (lane < T::SEG_ROWS) {
-        lds_copy4(lrs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st));
-        lds_copy4(drs2, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st + QC));
+        lds_copy4(lrs, (uint32_t)((wave * T::SEG_ROWS + lane) * 4), lds_addr(st));
+        lds_copy4(drs2, (uint32_t)((wave * T::SEG_ROWS + lane) * 4), lds_addr(st + QC));
       }
     }
   };
@@ -541,16 +535,10 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int db = 0; db < ND; ++db) toff[hf][db] += role == 0 ? T::TILE : 0;
-  // each copying wavefront's first row group folded into its lane offsets
   const uint32_t q_rs = (uint32_t)(p.q_ss * 2), do_rs = (uint32_t)(p.do_ss * 2);
   uint32_t qsel[T::LOADS], dsel[T::LOADS];
   tile_copy_offsets<D, T::CW>(lane, wave, q_rs, qsel);
   tile_copy_offsets<D, T::CW>(lane, wave, do_rs, dsel);
-#pragma unroll
-  for (int n = 0; n < T::LOADS; ++n) {
-    qsel[n] += wave * T::RPI * q_rs;
-    dsel[n] += wave * T::RPI * do_rs;
-  }
   const int32_t* qseg_b = p.q_seg + (int64_t)b * p.q_len;
 
   // Walk state of one query head of the group: its Q, dO and statistics rows
@@ -604,24 +592,22 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
       char* ddst = qdst + T::TILE;
       const u32x4 qrs = buffer_rsrc(q_h + (int64_t)q0 * q_rs, (uint32_t)rows * q_rs);
       const u32x4 drs = buffer_rsrc(do_h + (int64_t)q0 * do_rs, (uint32_t)rows * do_rs);
-      lds_copy_rows<T::LOADS, T::CW * 1024>(qrs, qsel, 0u, T::CW * T::RPI * q_rs,
-                                            lds_addr(qdst + wave * T::RPI * T::ROWB));
-      lds_copy_rows<T::LOADS, T::CW * 1024>(drs, dsel, 0u, T::CW * T::RPI * do_rs,
-                                            lds_addr(ddst + wave * T::RPI * T::ROWB));
+      lds_copy_rows<T::LOADS, T::CW * 1024>(qrs, qsel, lds_addr(qdst + wave * T::RPI * T::ROWB));
+      lds_copy_rows<T::LOADS, T::CW * 1024>(drs, dsel, lds_addr(ddst + wave * T::RPI * T::ROWB));
     }
     if (has_seg) {
       const uint32_t sdst =
           lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * QC + wave * T::SEG_ROWS);
       const u32x4 srs = buffer_rsrc(qseg_b + q0, (uint32_t)(rows * 4));
-      if (lane < T::SEG_ROWS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), sdst);
+      if (lane < T::SEG_ROWS) lds_copy4(srs, (uint32_t)((wave * T::SEG_ROWS + lane) * 4), sdst);
     }
     if constexpr (SM) {
       float* st = reinterpret_cast<float*>(smem + T::STAT_OFF) + stage * 2 * QC + wave * T::SEG_ROWS;
       const u32x4 lrs = buffer_rsrc(lse_h + q0, (uint32_t)(rows * 4));
       const u32x4 drs2 = buffer_rsrc(delta_h + q0, (uint32_t)(rows * 4));
       if (lane < T::SEG_ROWS) {
-        lds_copy4(lrs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st));
-        lds_copy4(drs2, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_ROWS * 4), lds_addr(st + QC));
+        lds_copy4(lrs, (uint32_t)((wave * T::SEG_ROWS + lane) * 4), lds_addr(st));
+        lds_copy4(drs2, (uint32_t)((wave * T::SEG_ROWS + lane) * 4), lds_addr(st + QC));
       }
     }
   };
@@ -915,14 +901,12 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
     const int rows = p.kv_len - key0 < KC ? p.kv_len - key0 : KC;
     const u32x4 krs = buffer_rsrc(kg + key0 * k_rs, (uint32_t)(rows * k_rs));
     const u32x4 vrs = buffer_rsrc(vg + key0 * v_rs, (uint32_t)(rows * v_rs));
-    lds_copy_rows<T::LOADS, NW * 1024>(krs, ksel, (uint32_t)(wave * T::RPI * k_rs), (uint32_t)(NW * T::RPI * k_rs),
-                                       lds_addr(kdst + wave * T::RPI * T::ROWB));
-    lds_copy_rows<T::LOADS, NW * 1024>(vrs, vsel, (uint32_t)(wave * T::RPI * v_rs), (uint32_t)(NW * T::RPI * v_rs),
-                                       lds_addr(vdst + wave * T::RPI * T::ROWB));
+    lds_copy_rows<T::LOADS, NW * 1024>(krs, ksel, lds_addr(kdst + wave * T::RPI * T::ROWB));
+    lds_copy_rows<T::LOADS, NW * 1024>(vrs, vsel, lds_addr(vdst + wave * T::RPI * T::ROWB));
     if (has_seg) {
       const uint32_t sdst = lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * KC + wave * T::SEG_KEYS);
       const u32x4 srs = buffer_rsrc(kvseg_g + key0, (uint32_t)(rows * 4));
-      if (lane < T::SEG_KEYS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_KEYS * 4), sdst);
+      if (lane < T::SEG_KEYS) lds_copy4(srs, (uint32_t)((wave * T::SEG_KEYS + lane) * 4), sdst);
     }
   };
 

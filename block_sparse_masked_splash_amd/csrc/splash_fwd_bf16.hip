@@ -210,14 +210,12 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
     const int rows = p.kv_len - key0 < KC ? p.kv_len - key0 : KC;  // rows past the end read as 0
     const u32x4 krs = buffer_rsrc(kg + key0 * k_rs, (uint32_t)(rows * k_rs));
     const u32x4 vrs = buffer_rsrc(vg + key0 * v_rs, (uint32_t)(rows * v_rs));
-    lds_copy_rows<T::LOADS, NW * 1024>(krs, kvsel, (uint32_t)(wave * T::RPI * k_rs), (uint32_t)(NW * T::RPI * k_rs),
-                                       lds_addr(kdst + wave * T::RPI * T::ROWB));
-    lds_copy_rows<T::LOADS, NW * 1024>(vrs, vvsel, (uint32_t)(wave * T::RPI * v_rs), (uint32_t)(NW * T::RPI * v_rs),
-                                       lds_addr(vdst + wave * T::RPI * T::ROWB));
+    lds_copy_rows<T::LOADS, NW * 1024>(krs, kvsel, lds_addr(kdst + wave * T::RPI * T::ROWB));
+    lds_copy_rows<T::LOADS, NW * 1024>(vrs, vvsel, lds_addr(vdst + wave * T::RPI * T::ROWB));
     if (has_seg) {
       const uint32_t sdst = lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * KC + wave * T::SEG_KEYS);
       const u32x4 srs = buffer_rsrc(kvseg_g + key0, (uint32_t)(rows * 4));
-      if (lane < T::SEG_KEYS) lds_copy4(srs, (uint32_t)(lane * 4), (uint32_t)(wave * T::SEG_KEYS * 4), sdst);
+      if (lane < T::SEG_KEYS) lds_copy4(srs, (uint32_t)((wave * T::SEG_KEYS + lane) * 4), sdst);
     }
     if (dense && j_partial) {
       int m = scalar_load_i32(p.mask_next + mrow + j);
@@ -229,7 +227,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
       for (int e0 = wave * 64; e0 < T::DM_WORDS; e0 += NW * 64) {
         const int e = e0 + lane;
         const uint32_t voff = (uint32_t)(((e / T::WPT) * wpr + t / 32 + e % T::WPT) * 4);
-        if (e < T::DM_WORDS) lds_copy4(drs, voff, 0u, lds_addr(ddst + e0));
+        if (e < T::DM_WORDS) lds_copy4(drs, voff, lds_addr(ddst + e0));
       }
     }
   };

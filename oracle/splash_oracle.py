@@ -270,16 +270,31 @@ def block_flops(block_mask: np.ndarray, B: int, H: int, bq: int, bkv: int, D: in
 
 
 def element_flops(B: int, H: int, q_len: int, kv_len: int, D: int, heads,
-                  q_seg=None, kv_seg=None) -> int:
-    """4*D per allowed (q, k) pair, summed over every (batch, head)."""
-    heads = [tuple(h) for h in heads]
+                  q_seg=None, kv_seg=None, dense=None) -> int:
+    """4*D per allowed (q, k) pair, summed over every (batch, head): the
+    element-exact count of the two products' FLOPs (2*D for q.k and 2*D for
+    p*v per allowed pair), as against ``block_flops``, which counts whole
+    non-empty blocks.
+
+    The allowed pairs of one (batch, head) are those of ``element_mask``;
+    (batch, head) pairs with the same head mask, segment ids and dense mask
+    have the same count, which is taken once.
+    """
+    heads = _heads_list(heads, H)
+    dh = _dense_heads(dense, H)
+    counts = {}
     total = 0
     for b in range(B):
+        qs = None if q_seg is None else np.asarray(q_seg)[b]
+        ks = None if kv_seg is None else np.asarray(kv_seg)[b]
         for h in range(H):
             hd = heads[0] if len(heads) == 1 else heads[h]
-            qs = None if q_seg is None else np.asarray(q_seg)[b]
-            ks = None if kv_seg is None else np.asarray(kv_seg)[b]
-            total += int(element_mask(q_len, kv_len, hd, qs, ks).sum())
+            hdn = None if dh is None else (0 if len(dh) == 1 else h)
+            key = (hd, b if q_seg is not None else None, hdn)
+            if key not in counts:
+                dm = None if dh is None else dh[hdn]
+                counts[key] = int(element_mask(q_len, kv_len, hd, qs, ks, dense=dm).sum())
+            total += counts[key]
     return 4 * D * total
 
 

@@ -277,3 +277,45 @@ def test_softmax_entry_points_validation_errors():
     assert bwd(lse=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
     assert bwd(delta=0xA00002) == bd.SPLASH_ERR_INVALID_ARGUMENT
     assert bwd(info_dkv=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+
+
+def test_misaligned_metadata_and_statistics_are_refused():
+    """block_mask and data_next are read as aligned 32-bit words, and so are
+    segment ids, dense-mask arrays and the log-sum-exp rows: a pointer that is
+    not 4-byte aligned is refused on the host before anything is launched."""
+    lib = bd.load_library()
+    E = bd
+    d, keep = _desc()
+    assert _fwd(lib, desc=d, info=_info(bm=0x10001)) == E.SPLASH_ERR_INVALID_ARGUMENT
+    assert b"aligned" in lib.splash_last_error()
+    assert _fwd(lib, desc=d, info=_info(dn=0x20002)) == E.SPLASH_ERR_INVALID_ARGUMENT
+    # the same through the metadata builds
+    for fn in (lib.splash_mask_info_build, lib.splash_mask_info_build_dkv):
+        assert fn(1, 1, 256, 256, 64, 64, ctypes.byref(d), ctypes.byref(_info(bm=0x10003)), None) == \
+            E.SPLASH_ERR_INVALID_ARGUMENT
+    # segment ids
+    ds, keep_s = _desc(qseg=0x5002, kvseg=0x6000)
+    assert _fwd(lib, desc=ds, info=_info()) == E.SPLASH_ERR_INVALID_ARGUMENT
+    assert b"segment ids must be 4-byte aligned" in lib.splash_last_error()
+    # the backward's two metadata structs
+    st = [bd._I64x3(4 * 256 * 128, 256 * 128, 128) for _ in range(7)]
+    args = []
+    for n, s in enumerate(st):
+        args += [0x100000 * (n + 1), s]
+    for row, col in ((_info(bm=0x10001), _info()), (_info(), _info(dn=0x20001))):
+        assert lib.splash_pointwise_bwd(1, 1, 1, 4, 2, 256, 256, 128, *args, 0.1, ctypes.byref(d),
+                                        ctypes.byref(row), ctypes.byref(col), None) == E.SPLASH_ERR_INVALID_ARGUMENT
+    # log-sum-exp output of the forward
+    ss = (ctypes.c_int64 * 2)(4 * 256, 256)
+    assert lib.splash_fwd_lse(1, 1, 1, 4, 2, 256, 256, 128, 0x100000, st[0], 0x200000, st[1], 0x300000, st[2],
+                              0x400000, st[3], 0x900002, ss, 0.1, ctypes.byref(d), ctypes.byref(_info()),
+                              None) == E.SPLASH_ERR_INVALID_ARGUMENT
+    assert b"lse" in lib.splash_last_error()
+    # dense-mask arrays
+    for mn, mb in ((0x30002, 0x40000), (0x30000, 0x40001)):
+        part = bd.PartialMasksC(mn, mb, 3)
+        stf = [bd._I64x3(256 * 128, 256 * 128, 128) for _ in range(4)]
+        assert lib.splash_masked_fwd(0, 1, 1, 1, 1, 1, 256, 256, 128, 0x100000, stf[0], 0x200000, stf[1],
+                                     0x300000, stf[2], 0x400000, stf[3], 0.1, ctypes.byref(d),
+                                     ctypes.byref(_info()), ctypes.byref(part), None) == E.SPLASH_ERR_INVALID_ARGUMENT
+        assert b"dense mask arrays must be 4-byte aligned" in lib.splash_last_error()

@@ -87,10 +87,16 @@ def test_mask_info_full_workloads(gpu_device, name):
     dn = info.data_next.cpu().numpy()
     Bm, Hm, nq, nk = bm.shape
     assert (Bm, Hm) == ((w.B if w.segments else 1), len(w.head_masks))
-    # sampled rows against the oracle, one row at a time
-    rows = {(0, 0, 0), (Bm - 1, Hm - 1, nq - 1)}
-    while len(rows) < min(Bm * Hm * nq, 40):
-        rows.add((int(rng.integers(Bm)), int(rng.integers(Hm)), int(rng.integers(nq))))
+    # every metadata row against the oracle, one row at a time (all rows of
+    # every workload with at most 128 of them, which covers the segment-id
+    # workload; 40 sampled rows of the 4096 of the mixed-head workload, whose
+    # whole arrays are checked against closed forms below)
+    if Bm * Hm * nq <= 128:
+        rows = {(b, h, i) for b in range(Bm) for h in range(Hm) for i in range(nq)}
+    else:
+        rows = {(0, 0, 0), (Bm - 1, Hm - 1, nq - 1)}
+        while len(rows) < 40:
+            rows.add((int(rng.integers(Bm)), int(rng.integers(Hm)), int(rng.integers(nq))))
     segn = None if seg is None else seg.numpy()
     for (b, h, i) in sorted(rows):
         cls, nxt = oracle.mask_info_row(w.S, w.S, w.block_q, w.block_kv, w.head_masks[h], i,
@@ -207,10 +213,23 @@ def test_full_workload_sampled_rows(gpu_device, name):
     rng = np.random.default_rng(1000 + w.seed)
     qs = _seg_np(c["q_segment_ids"])
     extra = [w.block_q - 1, w.block_q, w.S // 2]
-    if qs is not None:
-        starts = [t for t in range(1, w.S) if qs[0, t] != qs[0, t - 1]]
-        extra += starts[:3]
     rows = sample_rows(rng, w.B, w.H, w.S, 60, extra)
+    if qs is not None:
+        # document edges: in every batch row, the first token of each document
+        # (it attends to itself alone), the token before it (the end of the
+        # previous document), and a random row of each query block that holds
+        # a document edge (a block of partial kv blocks)
+        more = set()
+        for b in range(w.B):
+            starts = [t for t in range(1, w.S) if qs[b, t] != qs[b, t - 1]]
+            for t in starts:
+                h = int(rng.integers(w.H))
+                more.add((b, h, t))
+                more.add((b, h, t - 1))
+                i = t // w.block_q
+                more.add((b, int(rng.integers(w.H)), int(rng.integers(i * w.block_q, (i + 1) * w.block_q))))
+        assert len(more) >= 20
+        rows = sorted(set(rows) | more)
     got, ref = [], []
     cache = {}
     for (b, h, t) in rows:

@@ -100,6 +100,54 @@ def test_element_counts_closed_form():
     assert m.sum() == sum(min(q, w) + 1 + min(S - 1 - q, w) for q in range(S))
 
 
+def test_element_flops_closed_forms(monkeypatch):
+    """The element-exact FLOP count, 4*D per allowed (q, k) pair over every
+    (batch, head), against closed forms: causal S(S+1)/2 pairs per head (at
+    the S=8192 workload that is 1.0997e12 FLOPs), causal window w sum_q
+    min(q, w) + 1, full Sq*Skv, causal with Sq != Skv sum_q min(q + 1, Skv),
+    causal AND same document sum over documents L(L+1)/2, the causal pattern
+    as a dense array, and per-head masks summed head by head."""
+    import oracle.splash_oracle as so
+
+    D = 64
+    S, w = 300, 37
+    tri = S * (S + 1) // 2
+    win = sum(min(q, w) + 1 for q in range(S))
+    assert oracle.element_flops(2, 3, S, S, D, [CAUSAL]) == 4 * D * 2 * 3 * tri
+    assert oracle.element_flops(1, 3, S, S, D, [CAUSAL, wl.local_causal(w), FULL]) == 4 * D * (tri + win + S * S)
+    assert oracle.element_flops(1, 1, 200, 300, D, [CAUSAL]) == 4 * D * sum(min(q + 1, 300) for q in range(200))
+    assert oracle.element_flops(1, 1, 300, 200, D, [CAUSAL]) == 4 * D * sum(min(q + 1, 200) for q in range(300))
+    assert oracle.element_flops(1, 2, 120, 70, D, [FULL]) == 4 * D * 2 * 120 * 70
+    # packed documents: causal AND same document gives each document its own triangle
+    lens = [[50, 120, 30, 100], [300]]
+    ids = np.array([np.repeat(np.arange(len(L)), L) for L in lens], dtype=np.int32)
+    want = sum(L * (L + 1) // 2 for row in lens for L in row)
+    assert oracle.element_flops(2, 2, S, S, D, [CAUSAL], ids, ids) == 4 * D * 2 * want
+    assert oracle.element_flops(2, 1, S, S, D, [FULL], ids, ids) == 4 * D * sum(L * L for row in lens for L in row)
+    # the causal pattern written out as a dense array (shared, and per head)
+    assert oracle.element_flops(1, 2, S, S, D, [FULL], dense=np.tri(S, S, dtype=bool)) == 4 * D * 2 * tri
+    dh = np.stack([np.tri(S, S, dtype=bool), np.ones((S, S), dtype=bool)])
+    assert oracle.element_flops(1, 2, S, S, D, [FULL], dense=dh) == 4 * D * (tri + S * S)
+    # full-size workloads: causal B=2 H=32 S=8192 D=128, and the mixed-head S=32768 workload
+    n = 8192
+    f = oracle.element_flops(2, 32, n, n, 128, [CAUSAL])
+    assert f == 4 * 128 * 64 * n * (n + 1) // 2
+    assert abs(f - 1.0997e12) < 1e8
+    w4 = wl.WORKLOADS["c4"]
+    n, w = 32768, 1024
+    local = w * (w + 1) // 2 + (n - w) * (w + 1)
+    assert oracle.element_flops(1, 16, n, n, 128, w4.head_masks) == 4 * 128 * 8 * (n * (n + 1) // 2 + local)
+    # a count that drops the diagonal (S(S-1)/2 pairs) fails the causal pin
+    real = so.element_mask
+
+    def no_diagonal(q_len, kv_len, head, *a, **k):
+        m = real(q_len, kv_len, head, *a, **k)
+        return m & ~np.eye(q_len, kv_len, dtype=bool)
+
+    monkeypatch.setattr(so, "element_mask", no_diagonal)
+    assert so.element_flops(1, 1, S, S, D, [CAUSAL]) != 4 * D * tri
+
+
 def test_head_broadcast_and_per_head_metadata():
     heads = [CAUSAL, wl.local_causal(64), FULL]
     bm, dn = oracle.mask_info(1, 3, 512, 512, 64, 64, heads)
