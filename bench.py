@@ -17,6 +17,7 @@ count, 4*D per allowed (q, k) pair, is reported beside it
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -352,6 +353,10 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # no garbage-collection pass inside the timed steps (a full pass over the
+    # objects the setup left behind can stall one step's launches for tens of ms)
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -361,6 +366,7 @@ def main():
         ev[s][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
 
