@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     MaskInfo,
     SplashError,
     dense_mask_info_build,
+    dense_mask_info_build_dkv,
     load_library,
     mask_info_build,
     mask_info_build_dkv,

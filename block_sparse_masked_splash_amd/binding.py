@@ -41,6 +41,9 @@ SYMBOLS = (
     "splash_fwd_lse",
     "splash_softmax_bwd_preprocess",
     "splash_softmax_bwd",
+    "splash_dense_mask_info_host_ex",
+    "splash_masked_fwd_lse",
+    "splash_masked_bwd",
     "splash_status_string",
     "splash_last_error",
     "splash_abi_version",
@@ -96,6 +99,12 @@ _SM_BWD_ARGS = ([ctypes.c_int] * 8 + _T * 4 + [ctypes.c_void_p, ctypes.c_void_p,
                    ctypes.c_void_p])
 _LSE_ARGS = ([ctypes.c_int] * 8 + _T * 4 + [ctypes.c_void_p, _I64p]
              + [ctypes.c_float, ctypes.POINTER(MaskDescC), ctypes.POINTER(MaskInfoC), ctypes.c_void_p])
+# dense-mask forms: partial masks after the metadata they go with
+_MASKED_LSE_ARGS = _LSE_ARGS[:-1] + [ctypes.POINTER(PartialMasksC), ctypes.c_void_p]
+_MASKED_BWD_ARGS = ([ctypes.c_int] * 9 + _T * 4 + [ctypes.c_void_p, ctypes.c_void_p, _I64p] + _T * 3
+                    + [ctypes.c_float, ctypes.POINTER(MaskDescC), ctypes.POINTER(MaskInfoC),
+                       ctypes.POINTER(PartialMasksC), ctypes.POINTER(MaskInfoC), ctypes.POINTER(PartialMasksC),
+                       ctypes.c_void_p])
 _I64x2 = ctypes.c_int64 * 2
 
 _lib = None
@@ -140,6 +149,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.splash_dense_mask_info_host.argtypes = (
         [ctypes.c_int] * 5 + [ctypes.POINTER(HeadMaskC), ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
         + [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)])
+    lib.splash_dense_mask_info_host_ex.restype = ctypes.c_int
+    lib.splash_dense_mask_info_host_ex.argtypes = (
+        [ctypes.c_int] * 6 + [ctypes.POINTER(HeadMaskC), ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+        + [ctypes.c_void_p] * 2 + [ctypes.c_int] + [ctypes.c_void_p] * 4
+        + [ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)])
+    lib.splash_masked_fwd_lse.restype = ctypes.c_int
+    lib.splash_masked_fwd_lse.argtypes = _MASKED_LSE_ARGS
+    lib.splash_masked_bwd.restype = ctypes.c_int
+    lib.splash_masked_bwd.argtypes = _MASKED_BWD_ARGS
     lib.splash_status_string.restype = ctypes.c_char_p
     lib.splash_status_string.argtypes = [ctypes.c_int]
     lib.splash_last_error.restype = ctypes.c_char_p
@@ -228,13 +246,18 @@ def _stream(device) -> int:
 
 
 def dense_mask_info_build(B: int, H: int, dense, head_masks=((0, -1, -1),), block_q: int = 128,
-                          block_kv: int = 128, device="cuda") -> MaskInfo:
-    """Metadata of an arbitrary dense mask ANDed with head masks, built on the
-    host by the library and copied to ``device``.
+                          block_kv: int = 128, device="cuda", q_segment_ids=None, kv_segment_ids=None,
+                          columns: bool = False) -> MaskInfo:
+    """Metadata of an arbitrary dense mask ANDed with head masks (and, with
+    segment ids, with segment equality), built on the host by the library and
+    copied to ``device``.
 
     ``dense``: boolean [q_len, kv_len] (shared by all heads) or [H, q_len,
     kv_len]; ``head_masks``: 1 or H (causal, window_left, window_right)
-    triples. No segment ids."""
+    triples; segment ids: int32 [B, q_len] and [B, kv_len] (CPU or GPU),
+    folded into the metadata (one metadata batch row per batch row).
+    ``columns``: the layout of the backward's dK/dV walk (as
+    ``mask_info_build_dkv``) instead of the row walk."""
     lib = load_library()
     d = torch.as_tensor(dense).to("cpu")
     if d.dim() == 2:
@@ -246,31 +269,53 @@ def dense_mask_info_build(B: int, H: int, dense, head_masks=((0, -1, -1),), bloc
     head_masks = tuple(tuple(int(x) for x in m) for m in head_masks)
     if len(head_masks) not in (1, H) or len(head_masks) > MAX_MASK_HEADS:
         raise ValueError("head_masks must hold 1 or H entries")
+    if (q_segment_ids is None) != (kv_segment_ids is None):
+        raise ValueError("both or neither of q_segment_ids and kv_segment_ids must be given")
+    seg = q_segment_ids is not None
+    if seg:
+        qs_h = torch.as_tensor(q_segment_ids).to("cpu", torch.int32).contiguous()
+        ks_h = torch.as_tensor(kv_segment_ids).to("cpu", torch.int32).contiguous()
+        if tuple(qs_h.shape) != (B, q_len) or tuple(ks_h.shape) != (B, kv_len):
+            raise ValueError(f"segment ids must be [B, q_len] = {(B, q_len)} and [B, kv_len] = {(B, kv_len)}")
     Hm = max(Hd, len(head_masks))
+    Bm = B if seg else 1
     nq = -(-q_len // block_q) if block_q > 0 else 0
     nk = -(-kv_len // block_kv) if block_kv > 0 else 0
     arr, nmh = _head_array(head_masks)
     heads_p = ctypes.cast(arr, ctypes.POINTER(HeadMaskC))
+    qs_p = qs_h.data_ptr() if seg else None
+    ks_p = ks_h.data_ptr() if seg else None
     count = ctypes.c_int64(0)
-    st = lib.splash_dense_mask_info_host(q_len, kv_len, block_q, block_kv, nmh, heads_p, Hd, d.data_ptr(), Hm,
-                                         None, None, None, None, 0, ctypes.byref(count))
+    st = lib.splash_dense_mask_info_host_ex(B, q_len, kv_len, block_q, block_kv, nmh, heads_p, Hd, d.data_ptr(), Hm,
+                                            qs_p, ks_p, int(columns), None, None, None, None, 0, ctypes.byref(count))
     _check(st)
     n = count.value
-    shape = (1, Hm, nq, nk)
-    entries = Hm * nq * nk
+    shape = (Bm, Hm, nk, nq) if columns else (Bm, Hm, nq, nk)
+    entries = Bm * Hm * nq * nk
     bmask = torch.empty((entries + 3) // 4 * 4, dtype=torch.int8)
     dnext = torch.empty(shape, dtype=torch.int32)
     mnext = torch.empty(shape, dtype=torch.int32)
     wpr = block_kv // 32
     blocks = torch.empty((n, block_q, wpr), dtype=torch.int32)
-    st = lib.splash_dense_mask_info_host(q_len, kv_len, block_q, block_kv, nmh, heads_p, Hd, d.data_ptr(), Hm,
-                                         bmask.data_ptr(), dnext.data_ptr(), mnext.data_ptr(),
-                                         blocks.data_ptr() if n else None, n, ctypes.byref(count))
+    st = lib.splash_dense_mask_info_host_ex(B, q_len, kv_len, block_q, block_kv, nmh, heads_p, Hd, d.data_ptr(), Hm,
+                                            qs_p, ks_p, int(columns), bmask.data_ptr(), dnext.data_ptr(),
+                                            mnext.data_ptr(), blocks.data_ptr() if n else None, n,
+                                            ctypes.byref(count))
     _check(st)
     device = torch.device(device)
     bmask_dev = bmask.to(device)[:entries].view(shape)
-    return MaskInfo(B, H, q_len, kv_len, block_q, block_kv, head_masks, None, None, bmask_dev,
-                    dnext.to(device), mnext.to(device), blocks.to(device))
+    qs_d = qs_h.to(device) if seg else None
+    ks_d = ks_h.to(device) if seg else None
+    return MaskInfo(B, H, q_len, kv_len, block_q, block_kv, head_masks, qs_d, ks_d, bmask_dev,
+                    dnext.to(device), mnext.to(device), blocks.to(device), columns=bool(columns))
+
+
+def dense_mask_info_build_dkv(B: int, H: int, dense, head_masks=((0, -1, -1),), block_q: int = 128,
+                              block_kv: int = 128, device="cuda", q_segment_ids=None,
+                              kv_segment_ids=None) -> MaskInfo:
+    """``dense_mask_info_build`` in the layout of the backward's dK/dV walk."""
+    return dense_mask_info_build(B, H, dense, head_masks, block_q, block_kv, device, q_segment_ids,
+                                 kv_segment_ids, columns=True)
 
 
 def mask_info_build(B: int, H: int, q_len: int, kv_len: int, head_masks, block_q: int = 128,
@@ -451,11 +496,10 @@ def _backward(softmax: bool, q, k, v, d_o, info, info_dkv, scale, out_dtype, lay
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     for m in (info, info_dkv):
-        if (m.B, m.H, m.q_len, m.kv_len) != (B, H, Sq, Skv) or m.dense:
+        if (m.B, m.H, m.q_len, m.kv_len) != (B, H, Sq, Skv):
             raise SplashError(SPLASH_ERR_METADATA_MISMATCH,
-                              f"metadata built for B={m.B} H={m.H} q_len={m.q_len} kv_len={m.kv_len}"
-                              + (" (dense masks)" if m.dense else ""))
-    if info.head_masks != info_dkv.head_masks:
+                              f"metadata built for B={m.B} H={m.H} q_len={m.q_len} kv_len={m.kv_len}")
+    if info.head_masks != info_dkv.head_masks or info.dense != info_dkv.dense:
         raise ValueError("info and info_dkv were built for different masks")
     if info.columns or not info_dkv.columns:
         raise ValueError("info must come from mask_info_build and info_dkv from mask_info_build_dkv")
@@ -469,7 +513,15 @@ def _backward(softmax: bool, q, k, v, d_o, info, info_dkv, scale, out_dtype, lay
         ss = _stat_strides(lse, B, H, Sq)
         if tuple(_stat_strides(delta, B, H, Sq)) != tuple(ss):
             raise ValueError("lse and delta must share strides")
-        st = lib.splash_softmax_bwd(*head, lse.data_ptr(), delta.data_ptr(), ss, *tail)
+        stats = (lse.data_ptr(), delta.data_ptr(), ss)
+    else:
+        stats = (None, None, None)
+    if info.dense:
+        p1, p2 = info.partial_struct(), info_dkv.partial_struct()
+        st = lib.splash_masked_bwd(int(softmax), *head, *stats, *tail[:6], tail[6], tail[7], tail[8],
+                                   ctypes.byref(p1), tail[9], ctypes.byref(p2), tail[10])
+    elif softmax:
+        st = lib.splash_softmax_bwd(*head, *stats, *tail)
     else:
         st = lib.splash_pointwise_bwd(*head, *tail)
     del keep
@@ -497,8 +549,6 @@ def splash_fwd_lse(q, k, v, info: MaskInfo, scale: float | None = None, out=None
     """``splash_fwd`` that also returns the per-row log-sum-exp of the scores
     (fp32 [B, H, Sq]; -inf for rows with no allowed key): (out, lse)."""
     lib = load_library()
-    if info.dense:
-        raise ValueError("splash_fwd_lse takes head-mask metadata (no dense masks)")
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float32 or bfloat16")
     qs, (B, H, Sq, D) = _strides(q, layout)
@@ -524,9 +574,14 @@ def splash_fwd_lse(q, k, v, info: MaskInfo, scale: float | None = None, out=None
                           f"metadata built for B={info.B} H={info.H} q_len={info.q_len} kv_len={info.kv_len}")
     desc, keep = info.mask_desc()
     cinfo = info.info_struct()
-    st = lib.splash_fwd_lse(_DT[q.dtype], _DT[out_dtype], B, H, Hk, Sq, Skv, D, q.data_ptr(), qs, k.data_ptr(), ks,
-                            v.data_ptr(), vs, out.data_ptr(), os_, lse.data_ptr(), ls, float(scale),
-                            ctypes.byref(desc), ctypes.byref(cinfo), ctypes.c_void_p(_stream(q.device)))
+    args = (_DT[q.dtype], _DT[out_dtype], B, H, Hk, Sq, Skv, D, q.data_ptr(), qs, k.data_ptr(), ks,
+            v.data_ptr(), vs, out.data_ptr(), os_, lse.data_ptr(), ls, float(scale),
+            ctypes.byref(desc), ctypes.byref(cinfo))
+    if info.dense:
+        part = info.partial_struct()
+        st = lib.splash_masked_fwd_lse(*args, ctypes.byref(part), ctypes.c_void_p(_stream(q.device)))
+    else:
+        st = lib.splash_fwd_lse(*args, ctypes.c_void_p(_stream(q.device)))
     del keep
     _check(st)
     return out, lse

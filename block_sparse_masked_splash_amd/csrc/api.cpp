@@ -159,8 +159,6 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
   }
 
   const bool seg = mask->q_segment_ids != nullptr;
-  if (partial != nullptr && seg)
-    return record_error(SPLASH_ERR_UNSUPPORTED, "dense-mask metadata is built without segment ids");
   const int bq = info->block_q, bkv = info->block_kv;
   if (bq <= 0 || bkv <= 0) return record_error(SPLASH_ERR_METADATA_MISMATCH, "info block sizes %d x %d", bq, bkv);
   const int64_t nq = ceil_div(q_len, bq), nk = ceil_div(kv_len, bkv);
@@ -221,8 +219,10 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
   p.meta_batch = seg ? B : 1;
   p.block_mask = info->block_mask;
   p.data_next = info->data_next;
-  p.q_seg = mask->q_segment_ids;
-  p.kv_seg = mask->kv_segment_ids;
+  // with a dense mask, segment ids are folded into the host-built classes and
+  // partial-block bits (metadata per batch row), so the kernel does not read them
+  p.q_seg = partial != nullptr ? nullptr : mask->q_segment_ids;
+  p.kv_seg = partial != nullptr ? nullptr : mask->kv_segment_ids;
   if (lse_strides != nullptr) {
     p.lse = lse;
     p.lse_sb = lse_strides[0];
@@ -241,23 +241,36 @@ splash_status fwd_common(bool pointwise, splash_dtype in_dtype, splash_dtype out
 
 // Checks one metadata struct against the call; `what` names it in messages.
 splash_status check_info(const char* what, const splash_mask_info* info, int B, int H, int q_len, int kv_len,
-                         bool seg, int nm, bool work) {
+                         bool seg, int nm, bool work, bool dense = false) {
   if (info == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s is null", what);
   const int bq = info->block_q, bkv = info->block_kv;
   if (bq <= 0 || bkv <= 0)
     return record_error(SPLASH_ERR_METADATA_MISMATCH, "%s block sizes %d x %d", what, bq, bkv);
   const int64_t nq = ceil_div(q_len, bq), nk = ceil_div(kv_len, bkv);
-  if (info->meta_batch != (seg ? B : 1) || info->meta_heads != nm || info->num_q_blocks != nq ||
-      info->num_kv_blocks != nk)
+  // metadata heads: those of the head masks, or (dense masks) 1 or H with the
+  // head masks 1 or as many
+  const bool heads_ok = !dense ? info->meta_heads == nm
+                               : ((info->meta_heads == 1 || info->meta_heads == H) && (nm == 1 || nm == info->meta_heads));
+  if (info->meta_batch != (seg ? B : 1) || !heads_ok || info->num_q_blocks != nq || info->num_kv_blocks != nk)
     return record_error(SPLASH_ERR_METADATA_MISMATCH,
                         "%s [%d,%d,%d,%d] but this call needs [%d,%d,%lld,%lld] (segment ids %s)", what,
                         info->meta_batch, info->meta_heads, info->num_q_blocks, info->num_kv_blocks, seg ? B : 1, nm,
                         (long long)nq, (long long)nk, seg ? "given" : "absent");
-  (void)H;
   if (work && nq > 0 && nk > 0 && (info->block_mask == nullptr || info->data_next == nullptr))
     return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s arrays are null", what);
   if (misaligned4(info->block_mask) || misaligned4(info->data_next))
     return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s arrays must be 4-byte aligned", what);
+  return SPLASH_OK;
+}
+
+// Checks the dense-mask arrays of one walk (`what` names them in messages).
+splash_status check_partial(const char* what, const splash_partial_masks* partial, bool work) {
+  if (partial->num_blocks < 0 || partial->num_blocks > ((int64_t)1 << 31))
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s num_blocks=%lld", what, (long long)partial->num_blocks);
+  if (work && (partial->mask_next == nullptr || (partial->num_blocks > 0 && partial->mask_blocks == nullptr)))
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s dense mask arrays are null", what);
+  if (misaligned4(partial->mask_next) || misaligned4(partial->mask_blocks))
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "%s dense mask arrays must be 4-byte aligned", what);
   return SPLASH_OK;
 }
 
@@ -268,7 +281,9 @@ splash_status bwd_common(bool softmax, splash_dtype in_dtype, splash_dtype out_d
                          const int64_t* stat_strides, void* dq, const int64_t dq_strides[3], void* dk,
                          const int64_t dk_strides[3], void* dv, const int64_t dv_strides[3], float scale,
                          const splash_mask_desc* mask, const splash_mask_info* info,
-                         const splash_mask_info* info_dkv, hipStream_t stream) {
+                         const splash_mask_info* info_dkv, hipStream_t stream,
+                         const splash_partial_masks* partial = nullptr,
+                         const splash_partial_masks* partial_dkv = nullptr) {
   splash_status s = check_sizes(B, H, q_len, kv_len);
   if (s != SPLASH_OK) return s;
   if (kv_heads < 1 || kv_heads > H || H % kv_heads != 0)
@@ -291,8 +306,20 @@ splash_status bwd_common(bool softmax, splash_dtype in_dtype, splash_dtype out_d
   const bool qwork = (int64_t)B * H * q_len > 0;
   const bool kwork = (int64_t)B * kv_heads * kv_len > 0;
   const bool work = qwork || kwork;
-  if ((s = check_info("info", info, B, H, q_len, kv_len, seg, nm, work)) != SPLASH_OK) return s;
-  if ((s = check_info("info_dkv", info_dkv, B, H, q_len, kv_len, seg, nm, work)) != SPLASH_OK) return s;
+  if ((partial == nullptr) != (partial_dkv == nullptr))
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "both or neither of partial and partial_dkv must be given");
+  const bool dense = partial != nullptr;
+  if ((s = check_info("info", info, B, H, q_len, kv_len, seg, nm, work, dense)) != SPLASH_OK) return s;
+  if ((s = check_info("info_dkv", info_dkv, B, H, q_len, kv_len, seg, nm, work, dense)) != SPLASH_OK) return s;
+  if (dense) {
+    if (info->meta_heads != info_dkv->meta_heads)
+      return record_error(SPLASH_ERR_METADATA_MISMATCH, "info and info_dkv have %d and %d metadata heads",
+                          info->meta_heads, info_dkv->meta_heads);
+    if ((s = check_partial("partial", partial, work)) != SPLASH_OK) return s;
+    if ((s = check_partial("partial_dkv", partial_dkv, work)) != SPLASH_OK) return s;
+    if (info->block_kv % 32 != 0 || info_dkv->block_kv % 32 != 0)
+      return record_error(SPLASH_ERR_INVALID_ARGUMENT, "dense-mask metadata needs block_kv a multiple of 32");
+  }
   const int bq = info->block_q, bkv = info->block_kv;
   if ((bq != 64 && bq != 128 && bq != 256) || (bkv != 64 && bkv != 128))
     return record_error(SPLASH_ERR_UNSUPPORTED, "info block sizes %d x %d (supported: block_q 64, 128 or 256; "
@@ -367,8 +394,17 @@ splash_status bwd_common(bool softmax, splash_dtype in_dtype, splash_dtype out_d
   p.c_meta_heads = info_dkv->meta_heads;
   p.c_block_mask = info_dkv->block_mask;
   p.c_data_next = info_dkv->data_next;
-  p.q_seg = mask->q_segment_ids;
-  p.kv_seg = mask->kv_segment_ids;
+  // with a dense mask, segment ids are folded into the host-built metadata
+  p.q_seg = dense ? nullptr : mask->q_segment_ids;
+  p.kv_seg = dense ? nullptr : mask->kv_segment_ids;
+  if (dense) {
+    p.mask_next = partial->mask_next;
+    p.mask_blocks = partial->num_blocks > 0 ? partial->mask_blocks : nullptr;
+    p.num_mask_blocks = partial->num_blocks;
+    p.c_mask_next = partial_dkv->mask_next;
+    p.c_mask_blocks = partial_dkv->num_blocks > 0 ? partial_dkv->mask_blocks : nullptr;
+    p.c_num_mask_blocks = partial_dkv->num_blocks;
+  }
   p.softmax = softmax ? 1 : 0;
   if (softmax) {
     p.lse = lse;
@@ -595,6 +631,36 @@ splash_status splash_fwd_lse(splash_dtype in_dtype, splash_dtype out_dtype, int 
   if (lse_strides == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse strides are null");
   return fwd_common(false, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides,
                     v, v_strides, o, o_strides, scale, mask, info, nullptr, lse, lse_strides, stream);
+}
+
+splash_status splash_masked_fwd_lse(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
+                                    int q_len, int kv_len, int head_dim, const void* q, const int64_t q_strides[3],
+                                    const void* k, const int64_t k_strides[3], const void* v,
+                                    const int64_t v_strides[3], void* o, const int64_t o_strides[3], float* lse,
+                                    const int64_t lse_strides[2], float scale, const splash_mask_desc* mask,
+                                    const splash_mask_info* info, const splash_partial_masks* partial,
+                                    hipStream_t stream) {
+  if (lse_strides == nullptr) return record_error(SPLASH_ERR_INVALID_ARGUMENT, "lse strides are null");
+  return fwd_common(false, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k, k_strides,
+                    v, v_strides, o, o_strides, scale, mask, info, partial, lse, lse_strides, stream);
+}
+
+splash_status splash_masked_bwd(int softmax, splash_dtype in_dtype, splash_dtype out_dtype, int B, int H,
+                                int kv_heads, int q_len, int kv_len, int head_dim, const void* q,
+                                const int64_t q_strides[3], const void* k, const int64_t k_strides[3],
+                                const void* v, const int64_t v_strides[3], const void* d_o,
+                                const int64_t do_strides[3], const float* lse, const float* delta,
+                                const int64_t stat_strides[2], void* dq, const int64_t dq_strides[3], void* dk,
+                                const int64_t dk_strides[3], void* dv, const int64_t dv_strides[3], float scale,
+                                const splash_mask_desc* mask, const splash_mask_info* info,
+                                const splash_partial_masks* partial, const splash_mask_info* info_dkv,
+                                const splash_partial_masks* partial_dkv, hipStream_t stream) {
+  if (softmax != 0 && softmax != 1)
+    return record_error(SPLASH_ERR_INVALID_ARGUMENT, "softmax=%d must be 0 or 1", softmax);
+  return bwd_common(softmax == 1, in_dtype, out_dtype, B, H, kv_heads, q_len, kv_len, head_dim, q, q_strides, k,
+                    k_strides, v, v_strides, d_o, do_strides, softmax == 1 ? lse : nullptr,
+                    softmax == 1 ? delta : nullptr, softmax == 1 ? stat_strides : nullptr, dq, dq_strides, dk,
+                    dk_strides, dv, dv_strides, scale, mask, info, info_dkv, stream, partial, partial_dkv);
 }
 
 splash_status splash_masked_fwd(int pointwise, splash_dtype in_dtype, splash_dtype out_dtype, int B, int H,

@@ -108,6 +108,15 @@ struct BwdParams {
   const int32_t* c_data_next;
   const int32_t* q_seg;
   const int32_t* kv_seg;
+  // dense masks: for a partial block, mask_next (in its walk's metadata
+  // layout) names the block's entry of mask_blocks ([n][block_q][block_kv /
+  // 32] bits, the walk's block sizes); null without a dense mask
+  const int32_t* mask_next;
+  const uint32_t* mask_blocks;
+  int64_t num_mask_blocks;
+  const int32_t* c_mask_next;
+  const uint32_t* c_mask_blocks;
+  int64_t c_num_mask_blocks;
   // softmax backward: per-row log-sum-exp of the forward and
   // delta = rowsum(dO * O), both [B, H, q_len] fp32 (rows contiguous)
   int softmax;

@@ -110,7 +110,10 @@ struct DkvTiling {
   static constexpr int ND = D / 32;
   static constexpr int SEG_OFF = 2 * 2 * TILE;   // [stage][Q | dO][TILE], then [stage][QC] ids
   static constexpr int STAT_OFF = SEG_OFF + 2 * QC * 4;  // softmax: [stage][LSE | delta][QC] floats
-  static constexpr int LDS_BYTES = STAT_OFF + 2 * 2 * QC * 4;
+  // dense masks: [stage][NW key words][QC query rows] words of the block's entry
+  static constexpr int DM_WORDS = NW * QC;
+  static constexpr int DM_OFF = STAT_OFF + 2 * 2 * QC * 4;
+  static constexpr int LDS_BYTES = DM_OFF + 2 * DM_WORDS * 4;
   static_assert(LOADS >= 1, "tile too small for the workgroup");
 };
 
@@ -189,6 +192,7 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
   const float* delta_h;
   const int32_t* dn_col;
   const int8_t* cls_col;
+  const int32_t* mn_col;  // dense masks: the column's mask_next entries
   auto set_head = [&](int g) {
     const auto* kp = kernarg_params<BwdParams>();
     const int h = hk * G + g;
@@ -196,6 +200,7 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
     const int64_t col = (((int64_t)bm * kp->c_meta_heads + hm) * kp->c_nk + j) * kp->c_nq;
     dn_col = kp->c_data_next + col;
     cls_col = kp->c_block_mask + col;
+    mn_col = kp->c_mask_next + col;
     q_h = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(kp->q) + b * kp->q_sb + h * kp->q_sh);
     do_h = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(kp->d_o) + b * kp->do_sb + h * kp->do_sh);
     const int64_t st = b * kp->st_sb + h * kp->st_sh;
@@ -222,7 +227,11 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
     }
   };
 
-  auto issue_tile = [&](int stage, int i, int t) {
+  const bool dense = p.c_mask_blocks != nullptr;
+  // Copy of tile (q block i, offset t): Q and dO rows, their ids and
+  // statistics, and for a partial block of a dense mask the block's words of
+  // these rows, stored by key word ([NW][QC]).
+  auto issue_tile = [&](int stage, int i, int t, bool i_partial) {
     const int q0 = i * p.c_block_q + t;
     const int rows = p.q_len - q0 < QC ? p.q_len - q0 : QC;  // rows past the end read as 0
     char* qdst = smem + stage * 2 * T::TILE;
@@ -231,6 +240,18 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
     const u32x4 drs = buffer_rsrc(do_h + (int64_t)q0 * do_rs, (uint32_t)rows * do_rs);
     lds_copy_rows<T::LOADS, NW * 1024>(qrs, qsel, lds_addr(qdst + wave * T::RPI * T::ROWB));
     lds_copy_rows<T::LOADS, NW * 1024>(drs, dsel, lds_addr(ddst + wave * T::RPI * T::ROWB));
+    if (dense && i_partial) {
+      int m = scalar_load_i32(mn_col + i);
+      m = m < 0 ? 0 : (m >= p.c_num_mask_blocks ? (int)p.c_num_mask_blocks - 1 : m);  // stays in the store
+      const int wpr = p.c_block_kv / 32;  // = NW: the workgroup covers the whole kv block
+      const u32x4 mrs =
+          buffer_rsrc(p.c_mask_blocks + (int64_t)m * p.c_block_q * wpr, (uint32_t)(p.c_block_q * wpr * 4));
+      const uint32_t* mdst = reinterpret_cast<const uint32_t*>(smem + T::DM_OFF) + stage * T::DM_WORDS;
+      for (int e0 = wave * 64; e0 < T::DM_WORDS; e0 += NW * 64) {
+        const int e = e0 + lane;  // key word e / QC, tile row e % QC
+        if (e < T::DM_WORDS) lds_copy4(mrs, (uint32_t)(((t + e % QC) * wpr + e / QC) * 4), lds_addr(mdst + e0));
+      }
+    }
     if (has_seg) {
       const uint32_t sdst =
           lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * QC + wave * T::SEG_ROWS);
@@ -269,7 +290,7 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
   set_head(0);
   int cur_i = first_i();
   settle(cur_g, cur_i);
-  if (cur_g < G) issue_tile(0, cur_i, 0);
+  if (cur_g < G) issue_tile(0, cur_i, 0, dense && block_class(cls_col, cur_i) == 1);
 
   auto step = [&](auto stage_tag) -> bool {
     constexpr int stage = decltype(stage_tag)::value;
@@ -285,7 +306,7 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
     // raised issue priority while the wavefront forms S, dP and the weights;
     // back to normal for the dV/dK products
     __builtin_amdgcn_s_setprio(1);
-    if (ng < G) issue_tile(stage ^ 1, ni, nt);
+    if (ng < G) issue_tile(stage ^ 1, ni, nt, dense && block_class(cls_col, ni) == 1);
 
     const int q0 = cur_i * p.c_block_q + cur_t;
     const char* qt = smem + stage * 2 * T::TILE;
@@ -340,7 +361,20 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
       if (e < a || !kvalid) a = e = QC;  // no query of the tile
       const uint32_t width = (uint32_t)(e - a);
       const int base = 4 * hh - a;
-      if (has_seg) {
+      if (dense) {
+        // (dense-mask metadata is built with any segment ids folded in)
+        const uint32_t* sdm = reinterpret_cast<const uint32_t*>(smem + T::DM_OFF) + stage * T::DM_WORDS + wave * QC;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 w4 = *reinterpret_cast<const uint4*>(sdm + 8 * u + 4 * hh);
+          const uint32_t words[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const bool ok = ((uint32_t)(base + 8 * u + v4) <= width) & (bool)((words[v4] >> l32) & 1u);
+            t[4 * u + v4] = ok ? t[4 * u + v4] : kMasked;
+          }
+        }
+      } else if (has_seg) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int4 qs4 = *reinterpret_cast<const int4*>(sseg + 8 * u + 4 * hh);
@@ -469,7 +503,10 @@ struct PairTiling {
   static constexpr int SEG_OFF = 2 * 2 * TILE;    // [stage][Q | dO][TILE], then [stage][QC] ids
   static constexpr int STAT_OFF = SEG_OFF + 2 * QC * 4;      // softmax: [stage][LSE | delta][QC]
   static constexpr int X_OFF = STAT_OFF + 2 * 2 * QC * 4;    // exchange: [NG][PARTS][2][64 lanes][16 B] bf16
-  static constexpr int LDS_BYTES = X_OFF + NG * PARTS * 2048;
+  // dense masks: [stage][NG key words][QC query rows] words of the block's entry
+  static constexpr int DM_WORDS = NG * QC;
+  static constexpr int DM_OFF = X_OFF + NG * PARTS * 2048;
+  static constexpr int LDS_BYTES = DM_OFF + 2 * DM_WORDS * 4;
   static_assert(LOADS >= 1 && SEG_ROWS >= 1, "tile too small for the workgroup");
 };
 
@@ -552,6 +589,7 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
   const float* delta_h;
   const int32_t* dn_col;
   const int8_t* cls_col;
+  const int32_t* mn_col;  // dense masks: the column's mask_next entries
   auto set_head = [&](int g) {
     const auto* kp = kernarg_params<BwdParams>();
     const int h = hk * G + g;
@@ -559,6 +597,7 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
     const int64_t col = (((int64_t)bm * kp->c_meta_heads + hm) * kp->c_nk + j) * kp->c_nq;
     dn_col = kp->c_data_next + col;
     cls_col = kp->c_block_mask + col;
+    mn_col = kp->c_mask_next + col;
     q_h = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(kp->q) + b * kp->q_sb + h * kp->q_sh);
     do_h = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(kp->d_o) + b * kp->do_sb + h * kp->do_sh);
     const int64_t st = b * kp->st_sb + h * kp->st_sh;
@@ -582,11 +621,27 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
     }
   };
 
-  auto issue_tile = [&](int stage, int i, int t) {
+  const bool dense = p.c_mask_blocks != nullptr;
+  auto issue_tile = [&](int stage, int i, int t, bool i_partial) {
     const int q0 = i * p.c_block_q + t;
     // rows past the end of the sequence or of the q block read as 0 (no contribution)
     int rows = p.q_len - q0 < QC ? p.q_len - q0 : QC;
     rows = p.c_block_q - t < rows ? p.c_block_q - t : rows;
+    if (dense && i_partial) {
+      // the block's words of these rows for the workgroup's NG key words,
+      // stored by key word ([NG][QC]); rows past the block read as 0
+      int m = scalar_load_i32(mn_col + i);
+      m = m < 0 ? 0 : (m >= p.c_num_mask_blocks ? (int)p.c_num_mask_blocks - 1 : m);  // stays in the store
+      const int wpr = p.c_block_kv / 32;
+      const u32x4 mrs =
+          buffer_rsrc(p.c_mask_blocks + (int64_t)m * p.c_block_q * wpr, (uint32_t)(p.c_block_q * wpr * 4));
+      const uint32_t* mdst = reinterpret_cast<const uint32_t*>(smem + T::DM_OFF) + stage * T::DM_WORDS;
+      for (int e0 = wave * 64; e0 < T::DM_WORDS; e0 += NW * 64) {
+        const int e = e0 + lane;  // key word e / QC of the workgroup, tile row e % QC
+        const uint32_t voff = (uint32_t)(((t + e % QC) * wpr + part_of_block * NG + e / QC) * 4);
+        if (e < T::DM_WORDS) lds_copy4(mrs, voff, lds_addr(mdst + e0));
+      }
+    }
     if (wave < T::CW) {
       char* qdst = smem + stage * 2 * T::TILE;
       char* ddst = qdst + T::TILE;
@@ -631,7 +686,7 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
   set_head(0);
   int cur_i = first_i();
   settle(cur_g, cur_i);
-  if (cur_g < G) issue_tile(0, cur_i, 0);
+  if (cur_g < G) issue_tile(0, cur_i, 0, dense && block_class(cls_col, cur_i) == 1);
 
   auto step = [&](auto stage_tag) -> bool {
     constexpr int stage = decltype(stage_tag)::value;
@@ -645,7 +700,7 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
     __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<0>();  // this wave's copies of the current tile are in LDS
     barrier_only();   // everyone's are; the other stage and the exchange are free again
-    if (ng < G) issue_tile(stage ^ 1, ni, nt);
+    if (ng < G) issue_tile(stage ^ 1, ni, nt, dense && block_class(cls_col, ni) == 1);
 
     const char* tb = smem + stage * 2 * T::TILE;  // Q tile, then dO tile
     const float* sst = reinterpret_cast<const float*>(smem + T::STAT_OFF) + stage * 2 * QC;
@@ -694,7 +749,21 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
           if (e < a || !kvalid) a = e = 32;
           const uint32_t width = (uint32_t)(e - a);
           const int base = 4 * hh - a;
-          if (has_seg) {
+          if (dense) {
+            // (dense-mask metadata is built with any segment ids folded in)
+            const uint32_t* sdm =
+                reinterpret_cast<const uint32_t*>(smem + T::DM_OFF) + stage * T::DM_WORDS + kg * QC + 32 * u;
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {
+              const uint4 ww = *reinterpret_cast<const uint4*>(sdm + 8 * w4 + 4 * hh);
+              const uint32_t words[4] = {ww.x, ww.y, ww.z, ww.w};
+#pragma unroll
+              for (int v4 = 0; v4 < 4; ++v4) {
+                const bool ok = ((uint32_t)(base + 8 * w4 + v4) <= width) & (bool)((words[v4] >> l32) & 1u);
+                t[4 * w4 + v4] = ok ? t[4 * w4 + v4] : kMasked;
+              }
+            }
+          } else if (has_seg) {
             const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * QC + 32 * u;
 #pragma unroll
             for (int w4 = 0; w4 < 4; ++w4) {
@@ -811,8 +880,11 @@ struct DqTiling {
   static constexpr int SEG_KEYS = KC / NW;
   static constexpr int NS = D / 16;
   static constexpr int ND = D / 32;
-  static constexpr int SEG_OFF = 2 * 2 * TILE;   // [stage][K | V][TILE], then [stage][KC] ids
-  static constexpr int LDS_BYTES = SEG_OFF + 2 * KC * 4;
+  static constexpr int WPT = KC / 32;            // dense-mask words per query row per tile
+  static constexpr int DM_WORDS = NW * 32 * WPT; // dense-mask words per tile (every row of the block)
+  static constexpr int SEG_OFF = 2 * 2 * TILE;   // [stage][K | V][TILE], then [stage][KC] ids,
+  static constexpr int DM_OFF = SEG_OFF + 2 * KC * 4;  // then [stage][DM_WORDS] dense-mask words
+  static constexpr int LDS_BYTES = DM_OFF + 2 * DM_WORDS * 4;
   static_assert(LOADS >= 1, "tile too small for the workgroup");
 };
 
@@ -894,7 +966,10 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
   const int8_t* bmask = p.block_mask + mrow;
   const int32_t* dnext = p.data_next + mrow;
 
-  auto issue_tile = [&](int stage, int jj, int t) {
+  const bool dense = p.mask_blocks != nullptr;
+  // Copy of tile (block jj, offset t): K and V rows, their segment ids, and
+  // for a partial block of a dense mask the block's bits of this tile's keys.
+  auto issue_tile = [&](int stage, int jj, int t, bool j_partial) {
     const int key0 = jj * p.block_kv + t;
     char* kdst = smem + stage * 2 * T::TILE;
     char* vdst = kdst + T::TILE;
@@ -907,6 +982,19 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
       const uint32_t sdst = lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * KC + wave * T::SEG_KEYS);
       const u32x4 srs = buffer_rsrc(kvseg_g + key0, (uint32_t)(rows * 4));
       if (lane < T::SEG_KEYS) lds_copy4(srs, (uint32_t)((wave * T::SEG_KEYS + lane) * 4), sdst);
+    }
+    if (dense && j_partial) {
+      int m = scalar_load_i32(p.mask_next + mrow + jj);
+      m = m < 0 ? 0 : (m >= p.num_mask_blocks ? (int)p.num_mask_blocks - 1 : m);  // any content stays in the store
+      const int wpr = p.block_kv / 32;
+      const u32x4 drs = buffer_rsrc(p.mask_blocks + (int64_t)m * p.block_q * wpr, (uint32_t)(p.block_q * wpr * 4));
+      const uint32_t* ddst = reinterpret_cast<const uint32_t*>(smem + T::DM_OFF) + stage * T::DM_WORDS;
+      // word e of the tile: row e / WPT, word t / 32 + e % WPT of that row
+      for (int e0 = wave * 64; e0 < T::DM_WORDS; e0 += NW * 64) {
+        const int e = e0 + lane;
+        const uint32_t voff = (uint32_t)(((e / T::WPT) * wpr + t / 32 + e % T::WPT) * 4);
+        if (e < T::DM_WORDS) lds_copy4(drs, voff, lds_addr(ddst + e0));
+      }
     }
   };
 
@@ -932,7 +1020,7 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
   int cur_t = 0;
   // class of the block being walked, read once per block (off the tile's math)
   bool cur_partial = cur_j < p.nk && block_class(bmask, cur_j) == 1;
-  if (cur_j < p.nk) issue_tile(0, cur_j, 0);
+  if (cur_j < p.nk) issue_tile(0, cur_j, 0, cur_partial);
 
   auto step = [&](auto stage_tag) -> bool {
     constexpr int stage = decltype(stage_tag)::value;
@@ -945,7 +1033,7 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
     }
     wait_vmcnt<0>();
     barrier_only();
-    if (nxt_j < p.nk) issue_tile(stage ^ 1, nxt_j, nxt_t);
+    if (nxt_j < p.nk) issue_tile(stage ^ 1, nxt_j, nxt_t, nxt_partial);
     // raised issue priority while the wavefront forms S, dP and dS (measured
     // faster at D = 64 and for the softmax gradient, slower for the pointwise
     // one at D = 128)
@@ -957,6 +1045,8 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
     const char* kt = smem + stage * 2 * T::TILE;
     const char* vt = kt + T::TILE;
     const int32_t* sseg = reinterpret_cast<const int32_t*>(smem + T::SEG_OFF) + stage * KC;
+    const uint32_t* dmw = reinterpret_cast<const uint32_t*>(smem + T::DM_OFF) + stage * T::DM_WORDS +
+                          (wave * 32 + l32) * T::WPT;  // this row's dense-mask words of the tile
 #pragma unroll
     for (int kb = 0; kb < KC / 32; ++kb) {
       // ---- Sᵀ = K Qᵀ, dPᵀ = V dOᵀ: 32 keys (rows) x this wave's 32 queries ----
@@ -990,7 +1080,16 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
         if (e < a || !qvalid) a = e = KC;
         const uint32_t width = (uint32_t)(e - a);
         const int base = 4 * hh - a + 32 * kb;
-        if (has_seg) {
+        if (dense) {
+          // (dense-mask metadata is built with any segment ids folded in)
+          const uint32_t dbits = dmw[kb] >> (4 * hh);  // bit 8 (r / 4) + r % 4 for score r
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = ((uint32_t)(base + 8 * (r >> 2) + (r & 3)) <= width) &
+                            (bool)((dbits >> (8 * (r >> 2) + (r & 3))) & 1u);
+            t[r] = ok ? t[r] : kMasked;
+          }
+        } else if (has_seg) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int4 ks4 = *reinterpret_cast<const int4*>(sseg + 32 * kb + 8 * u + 4 * hh);

@@ -77,6 +77,13 @@ __global__ __launch_bounds__(BKV*(D / 32)) void bwd_dkv_f32_kernel(BwdParams p) 
     if (i < 0 || i > p.c_nq) i = p.c_nq;
     while (i < p.c_nq) {
       const bool partial = p.c_block_mask[col + i] == 1;
+      // dense mask: this key's bit column of the block's entry (0 if none)
+      const uint32_t* dcol = nullptr;
+      if (partial && p.c_mask_blocks != nullptr) {
+        int m = p.c_mask_next[col + i];
+        m = m < 0 ? 0 : (m >= p.c_num_mask_blocks ? (int)p.c_num_mask_blocks - 1 : m);  // stays in the store
+        dcol = p.c_mask_blocks + (int64_t)m * p.c_block_q * (p.c_block_kv / 32) + rl / 32;
+      }
       for (int t = 0; t < p.c_block_q; t += TT) {
         const int q0 = i * p.c_block_q + t;
         if (q0 >= p.q_len) break;
@@ -117,6 +124,7 @@ __global__ __launch_bounds__(BKV*(D / 32)) void bwd_dkv_f32_kernel(BwdParams p) 
             const int q = q0 + qq;
             const int dlt = key - q;
             ok = kvalid && q < p.q_len && dlt >= band.lo && dlt <= band.hi && (!has_seg || sQseg[qq] == kseg);
+            if (dcol != nullptr) ok = ok && ((dcol[(int64_t)(t + qq) * (p.c_block_kv / 32)] >> (rl & 31)) & 1u);
           }
           if (!ok) continue;
           const float x = s * p.scale;
@@ -199,6 +207,13 @@ __global__ __launch_bounds__(BQ*(D / 32)) void bwd_dq_f32_kernel(BwdParams p) {
   if (jb < 0 || jb > p.nk) jb = p.nk;
   while (jb < p.nk) {
     const bool partial = p.block_mask[mrow + jb] == 1;
+    // dense mask: this query's row of the block's entry (0 if none)
+    const uint32_t* drow = nullptr;
+    if (partial && p.mask_blocks != nullptr) {
+      int m = p.mask_next[mrow + jb];
+      m = m < 0 ? 0 : (m >= p.num_mask_blocks ? (int)p.num_mask_blocks - 1 : m);  // stays in the store
+      drow = p.mask_blocks + ((int64_t)m * BQ + rl) * (p.block_kv / 32);
+    }
     for (int t = 0; t < p.block_kv; t += TT) {
       const int k0 = jb * p.block_kv + t;
       if (k0 >= p.kv_len) break;
@@ -233,6 +248,7 @@ __global__ __launch_bounds__(BQ*(D / 32)) void bwd_dq_f32_kernel(BwdParams p) {
           const int key = k0 + kk;
           const int dlt = key - qrow;
           ok = qvalid && key < p.kv_len && dlt >= band.lo && dlt <= band.hi && (!has_seg || sKseg[kk] == qseg);
+          if (drow != nullptr) ok = ok && ((drow[(t + kk) >> 5] >> ((t + kk) & 31)) & 1u);
         }
         if (!ok) continue;
         const float x = s * p.scale;

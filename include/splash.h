@@ -227,10 +227,35 @@ splash_status splash_dense_mask_info_host(int q_len, int kv_len, int block_q, in
                                           int8_t* block_mask, int32_t* data_next, int32_t* mask_next,
                                           uint32_t* mask_blocks, int64_t capacity, int64_t* num_blocks);
 
+/* The same with segment ids and either metadata layout: for B batch rows,
+ *   allowed(b, h, q, k) = dense[h', q, k] != 0 AND the band of head mask h''
+ *                         AND q_segment_ids[b, q] == kv_segment_ids[b, k]
+ * ("hstu_ops.py", _apply_mask: the stored mask block, the mask function and
+ * segment equality, ANDed). q_segment_ids [B, q_len] and kv_segment_ids
+ * [B, kv_len] are HOST int32 arrays, both or neither. With them the metadata
+ * has meta_batch = B (every array gains a leading batch axis; the store is
+ * shared by all batch rows); without them meta_batch = 1 (B is then only
+ * range-checked). columns = 0 gives the row layout above (for the forward and the
+ * backward's dQ walk); columns = 1 the dK/dV walk's layout of
+ * splash_mask_info_build_dkv: block_mask, data_next and mask_next are
+ * [meta_batch, meta_heads, nk, nq], data_next running along q blocks ("hstu_ops.py"
+ * builds the backward's dK/dV mask blocks separately, bwd_mask_info). The
+ * store entries are [block_q, block_kv / 32] words either way. Everything
+ * else (sizing with a count-only call, capacity, errors) as
+ * splash_dense_mask_info_host, which is this call with B = 1, no segment ids
+ * and columns = 0. ALL POINTERS ARE HOST. */
+splash_status splash_dense_mask_info_host_ex(int B, int q_len, int kv_len, int block_q, int block_kv,
+                                             int num_mask_heads, const splash_head_mask* heads,
+                                             int dense_heads, const uint8_t* dense, int meta_heads,
+                                             const int32_t* q_segment_ids, const int32_t* kv_segment_ids,
+                                             int columns, int8_t* block_mask, int32_t* data_next,
+                                             int32_t* mask_next, uint32_t* mask_blocks, int64_t capacity,
+                                             int64_t* num_blocks);
+
 /* Device copies of a dense mask's partial blocks (see above). */
 typedef struct {
-  const int32_t* mask_next;     /* DEVICE [meta_heads, nq, nk]                    */
-  const uint32_t* mask_blocks;  /* DEVICE [num_blocks, block_q, block_kv / 32]    */
+  const int32_t* mask_next;     /* DEVICE, the layout of its metadata's block_mask */
+  const uint32_t* mask_blocks;  /* DEVICE [num_blocks, block_q, block_kv / 32]     */
   int64_t num_blocks;
 } splash_partial_masks;
 
@@ -238,10 +263,15 @@ typedef struct {
  * with grouped-query K/V (kv_heads, as splash_gqa_fwd) and optional dense-mask
  * blocks. With partial == NULL this is exactly those calls. With partial
  * given, `info` holds the block_mask / data_next of the same dense mask (its
- * meta_heads 1 or H, the head masks 1 or as many), segment ids are not
- * accepted (UNSUPPORTED), and on every block of class 1 the block's bits are
- * ANDed with the head band. mask_next entries outside [0, num_blocks) are
- * clamped, so no metadata content makes the kernel read outside the store. */
+ * meta_heads 1 or H, the head masks 1 or as many), and on every block of
+ * class 1 the block's bits are ANDed with the head band. Segment ids may be
+ * given with a dense mask: the metadata must then come from
+ * splash_dense_mask_info_host_ex with the same ids (meta_batch = B), which
+ * folds segment equality into the classes and bits, so the kernel does not
+ * read the device ids (METADATA_MISMATCH if meta_batch is not B; with B = 1
+ * the library cannot tell metadata built without the ids). mask_next entries
+ * outside [0, num_blocks) are clamped, so no metadata content makes the
+ * kernel read outside the store. */
 splash_status splash_masked_fwd(int pointwise, splash_dtype in_dtype, splash_dtype out_dtype, int B, int H,
                                 int kv_heads, int q_len, int kv_len, int head_dim,
                                 const void* q, const int64_t q_strides[3],
@@ -355,6 +385,47 @@ splash_status splash_softmax_bwd(splash_dtype in_dtype, splash_dtype out_dtype, 
                                  float scale, const splash_mask_desc* mask,
                                  const splash_mask_info* info, const splash_mask_info* info_dkv,
                                  hipStream_t stream);
+
+/* Softmax forward with the per-row log-sum-exp (as splash_fwd_lse) under a
+ * dense mask (as splash_masked_fwd with pointwise = 0): the residuals of the
+ * softmax backward for a dense-mask model. partial may be NULL. */
+splash_status splash_masked_fwd_lse(splash_dtype in_dtype, splash_dtype out_dtype, int B, int H, int kv_heads,
+                                    int q_len, int kv_len, int head_dim,
+                                    const void* q, const int64_t q_strides[3],
+                                    const void* k, const int64_t k_strides[3],
+                                    const void* v, const int64_t v_strides[3],
+                                    void* o, const int64_t o_strides[3],
+                                    float* lse, const int64_t lse_strides[2],
+                                    float scale, const splash_mask_desc* mask, const splash_mask_info* info,
+                                    const splash_partial_masks* partial, hipStream_t stream);
+
+/* General backward: softmax = 0 is splash_pointwise_bwd (lse, delta and
+ * stat_strides are ignored), 1 is splash_softmax_bwd, with optional dense
+ * masks ("hstu_ops.py", _pointwise_splash_attention_bwd: the dQ and dK/dV
+ * kernels fetch a partial block's mask through their own mask_next into
+ * their own store of mask blocks, built for their own block sizes). partial
+ * and partial_dkv are both NULL (exactly the calls above) or both given:
+ * `info` and `partial` from splash_dense_mask_info_host_ex with columns = 0,
+ * `info_dkv` and `partial_dkv` with columns = 1, both for the same mask and
+ * segment ids (as for splash_masked_fwd, the ids are then folded into the
+ * metadata and not read on the device) and the same metadata heads (1 or H);
+ * block_kv of both walks in {64, 128}. Errors as for the two calls above,
+ * plus INVALID_ARGUMENT for one of the two dense structs missing, null or
+ * misaligned arrays. */
+splash_status splash_masked_bwd(int softmax, splash_dtype in_dtype, splash_dtype out_dtype, int B, int H,
+                                int kv_heads, int q_len, int kv_len, int head_dim,
+                                const void* q, const int64_t q_strides[3],
+                                const void* k, const int64_t k_strides[3],
+                                const void* v, const int64_t v_strides[3],
+                                const void* d_o, const int64_t do_strides[3],
+                                const float* lse, const float* delta, const int64_t stat_strides[2],
+                                void* dq, const int64_t dq_strides[3],
+                                void* dk, const int64_t dk_strides[3],
+                                void* dv, const int64_t dv_strides[3],
+                                float scale, const splash_mask_desc* mask,
+                                const splash_mask_info* info, const splash_partial_masks* partial,
+                                const splash_mask_info* info_dkv, const splash_partial_masks* partial_dkv,
+                                hipStream_t stream);
 
 /* Static name of a status code. */
 const char* splash_status_string(splash_status s);

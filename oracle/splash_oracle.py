@@ -207,7 +207,7 @@ def mask_info(B: int, H: int, q_len: int, kv_len: int, bq: int, bkv: int, heads,
 
 
 def mask_info_dkv(B: int, H: int, q_len: int, kv_len: int, bq: int, bkv: int, heads,
-                  q_seg=None, kv_seg=None):
+                  q_seg=None, kv_seg=None, dense=None):
     """(block_mask, data_next) of the dK/dV pass, both [Bm, Hm, nq, nk].
 
     "hstu_ops.py", ``_pointwise_splash_attention_bwd_kernel``: the grid runs
@@ -219,7 +219,7 @@ def mask_info_dkv(B: int, H: int, q_len: int, kv_len: int, bq: int, bkv: int, he
     column j that is not empty, else nq (the sentinel read as for the
     forward's walk).
     """
-    bm, _ = mask_info(B, H, q_len, kv_len, bq, bkv, heads, q_seg, kv_seg)
+    bm, _ = mask_info(B, H, q_len, kv_len, bq, bkv, heads, q_seg, kv_seg, dense=dense)
     dn = np.empty(bm.shape, dtype=np.int32)
     for b in range(bm.shape[0]):
         for h in range(bm.shape[1]):
@@ -484,14 +484,15 @@ def pointwise_attention_bwd_rows(q_rows, k, v, do_rows, scale: float, mask_rows,
 
 
 def pointwise_attention_bwd(q, k, v, do, scale: float, heads, q_seg=None, kv_seg=None,
-                            row_chunk: int = 512):
+                            row_chunk: int = 512, dense=None):
     """Gradients (dq [B, H, Sq, D], dk, dv [B, Hk, Skv, D]) of
     ``pointwise_attention`` for the output gradient ``do``, fp64.
 
     Query rows are taken ``row_chunk`` at a time and their contributions to dk
     and dv summed (the kernel's sum over q blocks for each kv block). With
     fewer K/V heads than query heads (``kv_head_of``), a K/V head's dk and dv
-    sum over the query heads that read it.
+    sum over the query heads that read it. ``dense``: an optional boolean
+    [Sq, Skv] or [H, Sq, Skv] mask ANDed into every head's element mask.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -501,6 +502,7 @@ def pointwise_attention_bwd(q, k, v, do, scale: float, heads, q_seg=None, kv_seg
     Skv = k.shape[2]
     kv_heads = k.shape[1]
     heads = _heads_list(heads, H)
+    dh = _dense_heads(dense, H)
     dq = np.zeros(q.shape, dtype=np.float64)
     dk = np.zeros(k.shape, dtype=np.float64)
     dv = np.zeros(v.shape, dtype=np.float64)
@@ -512,7 +514,8 @@ def pointwise_attention_bwd(q, k, v, do, scale: float, heads, q_seg=None, kv_seg
             hk = kv_head_of(h, H, kv_heads)
             for r0 in range(0, Sq, row_chunk):
                 rows = np.arange(r0, min(Sq, r0 + row_chunk))
-                m = element_mask(Sq, Skv, hd, qs, ks, rows=rows)
+                dm = None if dh is None else dh[0 if len(dh) == 1 else h]
+                m = element_mask(Sq, Skv, hd, qs, ks, rows=rows, dense=dm)
                 a, bk, bv = pointwise_attention_bwd_rows(q[b, h, rows], k[b, hk], v[b, hk], do[b, h, rows],
                                                          scale, m, Sq)
                 dq[b, h, rows] = a
@@ -576,31 +579,35 @@ def softmax_attention_bwd_rows(q_rows, k, v, do_rows, scale: float, mask_rows):
     return dq, dk, dv
 
 
-def softmax_lse(q, k, scale: float, heads, q_seg=None, kv_seg=None) -> np.ndarray:
+def softmax_lse(q, k, scale: float, heads, q_seg=None, kv_seg=None, dense=None) -> np.ndarray:
     """Log-sum-exp [B, H, Sq] of every row (``softmax_lse_rows``); k may have
-    fewer heads than q (``kv_head_of``)."""
+    fewer heads than q (``kv_head_of``); ``dense`` as for
+    ``pointwise_attention_bwd``."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     B, H, Sq, _ = q.shape
     Skv = k.shape[2]
     heads = _heads_list(heads, H)
+    dh = _dense_heads(dense, H)
     out = np.zeros((B, H, Sq))
     for b in range(B):
         qs = None if q_seg is None else np.asarray(q_seg)[b]
         ks = None if kv_seg is None else np.asarray(kv_seg)[b]
         for h in range(H):
             hd = heads[0] if len(heads) == 1 else heads[h]
-            m = element_mask(Sq, Skv, hd, qs, ks)
+            dm = None if dh is None else dh[0 if len(dh) == 1 else h]
+            m = element_mask(Sq, Skv, hd, qs, ks, dense=dm)
             out[b, h] = softmax_lse_rows(q[b, h], k[b, kv_head_of(h, H, k.shape[1])], scale, m)
     return out
 
 
 def softmax_attention_bwd(q, k, v, do, scale: float, heads, q_seg=None, kv_seg=None,
-                          row_chunk: int = 512):
+                          row_chunk: int = 512, dense=None):
     """Gradients (dq [B, H, Sq, D], dk, dv [B, Hk, Skv, D]) of
     ``softmax_attention`` for the output gradient ``do``, fp64; rows are
     taken ``row_chunk`` at a time and their dk, dv contributions summed, and
-    a K/V head's gradients sum over the query heads that read it."""
+    a K/V head's gradients sum over the query heads that read it; ``dense``
+    as for ``pointwise_attention_bwd``."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -609,6 +616,7 @@ def softmax_attention_bwd(q, k, v, do, scale: float, heads, q_seg=None, kv_seg=N
     Skv = k.shape[2]
     kv_heads = k.shape[1]
     heads = _heads_list(heads, H)
+    dh = _dense_heads(dense, H)
     dq = np.zeros(q.shape)
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)
@@ -620,7 +628,8 @@ def softmax_attention_bwd(q, k, v, do, scale: float, heads, q_seg=None, kv_seg=N
             hk = kv_head_of(h, H, kv_heads)
             for r0 in range(0, Sq, row_chunk):
                 rows = np.arange(r0, min(Sq, r0 + row_chunk))
-                m = element_mask(Sq, Skv, hd, qs, ks, rows=rows)
+                dm = None if dh is None else dh[0 if len(dh) == 1 else h]
+                m = element_mask(Sq, Skv, hd, qs, ks, rows=rows, dense=dm)
                 a, bk, bv = softmax_attention_bwd_rows(q[b, h, rows], k[b, hk], v[b, hk], do[b, h, rows], scale, m)
                 dq[b, h, rows] = a
                 dk[b, hk] += bk

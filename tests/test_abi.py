@@ -319,3 +319,39 @@ def test_misaligned_metadata_and_statistics_are_refused():
                                      0x300000, stf[2], 0x400000, stf[3], 0.1, ctypes.byref(d),
                                      ctypes.byref(_info()), ctypes.byref(part), None) == E.SPLASH_ERR_INVALID_ARGUMENT
         assert b"dense mask arrays must be 4-byte aligned" in lib.splash_last_error()
+
+
+def test_masked_bwd_and_masked_fwd_lse_validation_errors():
+    """splash_masked_bwd takes the dense structs of both walks or neither;
+    its flag is 0 or 1; dense arrays must be non-null and aligned;
+    splash_masked_fwd_lse needs lse strides. Every call fails on the host."""
+    lib = bd.load_library()
+    d, keep = _desc()
+    row = _info(bq=64, bkv=64)
+    st = [bd._I64x3(4 * 256 * 128, 256 * 128, 128) for _ in range(7)]
+    ss = (ctypes.c_int64 * 2)(4 * 256, 256)
+    good = bd.PartialMasksC(0x30000, 0x40000, 2)
+
+    def bwd(softmax=0, p1=good, p2=good, info=row, info_dkv=row):
+        args = []
+        for n, s in enumerate(st):
+            args.append(0x100000 * (n + 1))
+            args.append(s)
+        return lib.splash_masked_bwd(softmax, 1, 1, 1, 4, 2, 256, 256, 128, *args[:8], 0x900000, 0xA00000, ss,
+                                     *args[8:], 0.1, ctypes.byref(d), ctypes.byref(info),
+                                     ctypes.byref(p1) if p1 is not None else None, ctypes.byref(info_dkv),
+                                     ctypes.byref(p2) if p2 is not None else None, None)
+
+    assert bwd(softmax=2) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert bwd(p2=None) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert b"both or neither" in lib.splash_last_error()
+    assert bwd(p1=bd.PartialMasksC(None, 0x40000, 2)) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert bwd(p2=bd.PartialMasksC(0x30002, 0x40000, 2)) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    assert b"aligned" in lib.splash_last_error()
+    assert bwd(p1=bd.PartialMasksC(0x30000, 0x40000, -1)) == bd.SPLASH_ERR_INVALID_ARGUMENT
+    # dense metadata heads must agree between the walks
+    assert bwd(info_dkv=_info(Hm=4, bq=64, bkv=64)) == bd.SPLASH_ERR_METADATA_MISMATCH
+    stf = [bd._I64x3(4 * 256 * 128, 256 * 128, 128) for _ in range(4)]
+    assert lib.splash_masked_fwd_lse(1, 1, 1, 4, 2, 256, 256, 128, 0x100000, stf[0], 0x200000, stf[1], 0x300000,
+                                     stf[2], 0x400000, stf[3], 0x900000, None, 0.1, ctypes.byref(d),
+                                     ctypes.byref(row), ctypes.byref(good), None) == bd.SPLASH_ERR_INVALID_ARGUMENT

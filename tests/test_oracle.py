@@ -876,3 +876,84 @@ def test_softmax_bwd_closed_forms_and_mutants(monkeypatch):
         err = max(np.abs(a - b).max() for a, b in zip(got, ref))
         # the real function is pinned to torch above; a mutant moves away from it
         assert err > 1e-3, old
+
+
+# ---------------------------------------------------------------------------
+# backward under dense masks
+# ---------------------------------------------------------------------------
+
+
+def _torch_mask(S, head, dense_h, qs_b, ks_b):
+    """Boolean [S, S] element mask built with torch from the definitions:
+    causal k <= q, window q - wl <= k <= q + wr, the dense array's bit, and
+    segment equality."""
+    causal, wl_, wr = head
+    qp = torch.arange(S)[:, None]
+    kp = torch.arange(S)[None, :]
+    m = torch.ones(S, S, dtype=torch.bool)
+    if causal:
+        m &= kp <= qp
+    if wl_ >= 0:
+        m &= kp >= qp - wl_
+    if wr >= 0:
+        m &= kp <= qp + wr
+    m &= torch.from_numpy(dense_h)
+    m &= torch.from_numpy(qs_b)[:, None] == torch.from_numpy(ks_b)[None, :]
+    return m
+
+
+@pytest.mark.parametrize("head", [FULL, CAUSAL, (0, 5, 3)])
+def test_dense_bwd_matches_torch_autograd(head):
+    """The backwards with a per-head dense mask (and segment ids) against
+    torch autograd in float64: softmax through scaled_dot_product_attention
+    with the boolean mask, pointwise through torch's SiLU masked to 0."""
+    B, H, S, D = 2, 2, 53, 16
+    q, k, v, qs, ks = _case(91, B, H, S, S, D, sigma=0.8, segments="docs")
+    rng = np.random.default_rng(92)
+    dense = rng.random((H, S, S)) < 0.6
+    dense[:, np.arange(S), np.arange(S)] = True  # every row keeps a key
+    do = rng.standard_normal(q.shape)
+    scale = 1 / math.sqrt(D)
+    for kind in ("softmax", "pointwise"):
+        fn = oracle.softmax_attention_bwd if kind == "softmax" else oracle.pointwise_attention_bwd
+        dq, dk, dv = fn(q, k, v, do, scale, [head], qs, ks, row_chunk=20, dense=dense)
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+        total = 0
+        for b in range(B):
+            for h in range(H):
+                m = _torch_mask(S, head, dense[h], qs[b], ks[b])
+                if kind == "softmax":
+                    o = torch.nn.functional.scaled_dot_product_attention(
+                        tq[b, h][None], tk[b, h][None], tv[b, h][None], attn_mask=m, scale=scale)[0]
+                else:
+                    x = scale * (tq[b, h] @ tk[b, h].T)
+                    p = torch.where(m, torch.nn.functional.silu(x), torch.zeros((), dtype=torch.float64)) / S
+                    o = p @ tv[b, h]
+                total = total + (o * torch.from_numpy(do[b, h])).sum()
+        total.backward()
+        for got, t in ((dq, tq), (dk, tk), (dv, tv)):
+            np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=kind)
+    # the log-sum-exp under the same mask against torch.logsumexp
+    lse = oracle.softmax_lse(q, k, scale, [head], qs, ks, dense=dense)
+    for b in range(B):
+        for h in range(H):
+            m = _torch_mask(S, head, dense[h], qs[b], ks[b])
+            x = scale * torch.from_numpy(q[b, h]) @ torch.from_numpy(k[b, h]).T
+            want = torch.logsumexp(x.masked_fill(~m, -math.inf), dim=-1).numpy()
+            np.testing.assert_allclose(lse[b, h], want, rtol=1e-12, atol=1e-12)
+
+
+def test_dense_bwd_lower_triangle_is_causal_and_dropped_mask_fails():
+    """A lower-triangular dense mask under the full head mask gives the causal
+    gradients; a dense mask that the backward ignored would not."""
+    B, H, S, D = 1, 2, 47, 8
+    q, k, v, _, _ = _case(93, B, H, S, S, D)
+    do = np.random.default_rng(94).standard_normal(q.shape)
+    tri = np.tri(S, S, dtype=bool)
+    for fn in (oracle.softmax_attention_bwd, oracle.pointwise_attention_bwd):
+        a = fn(q, k, v, do, 0.3, [FULL], dense=tri)
+        c = fn(q, k, v, do, 0.3, [CAUSAL])
+        f = fn(q, k, v, do, 0.3, [FULL])
+        for x, y, z in zip(a, c, f):
+            np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
+            assert not np.allclose(x, z)
