@@ -97,10 +97,18 @@ struct Tiling {
 // at D = 64 four fit, and the extra wavefronts hide the longer vector work
 // (per key, the pointwise variant spends two transcendentals on half as many
 // matrix FLOPs).
-template <int D, int NW, bool PW, typename OutT>
+// Kinds of element mask a kernel instance applies on partial blocks: the
+// head's band only, the band and segment ids, or the band and a dense mask's
+// stored bits (segment ids given with a dense mask are folded into its
+// metadata, so the kernels never see both).
+enum MaskKind { kBandOnly = 0, kSegments = 1, kDense = 2 };
+
+template <int D, int NW, bool PW, typename OutT, int MK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW>(),
                                                                       waves_per_simd<D, NW>())))
 void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int units_grouped) {
+  constexpr bool has_seg = MK == kSegments;
+  constexpr bool dense = MK == kDense;
   using T = Tiling<D, NW>;
   constexpr int KC = T::KC;
   constexpr int NS = T::NS;
@@ -159,7 +167,6 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
   OutT* og = reinterpret_cast<OutT*>(p.o) + b * p.o_sb + h * p.o_sh;
   const int64_t k_rs = p.k_ss * 2;  // bytes between key rows
   const int64_t v_rs = p.v_ss * 2;
-  const bool has_seg = p.q_seg != nullptr;
   const int32_t* kvseg_g = has_seg ? p.kv_seg + (int64_t)b * p.kv_len : nullptr;
 
   // ---- Q (B operand of Sᵀ = K Qᵀ), two 32-row column blocks per wave ----
@@ -199,7 +206,6 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
   const int64_t mrow = (((int64_t)bm * p.meta_heads + hm) * p.nq + i) * p.nk;
   const int8_t* bmask = p.block_mask + mrow;
   const int32_t* dnext = p.data_next + mrow;
-  const bool dense = p.mask_blocks != nullptr;
 
   // Copy of tile (block j, offset t): K and V rows, their segment ids, and for
   // a partial block of a dense mask the block's bits of this tile's keys.
@@ -212,12 +218,12 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
     const u32x4 vrs = buffer_rsrc(vg + key0 * v_rs, (uint32_t)(rows * v_rs));
     lds_copy_rows<T::LOADS, NW * 1024>(krs, kvsel, lds_addr(kdst + wave * T::RPI * T::ROWB));
     lds_copy_rows<T::LOADS, NW * 1024>(vrs, vvsel, lds_addr(vdst + wave * T::RPI * T::ROWB));
-    if (has_seg) {
+    if constexpr (has_seg) {
       const uint32_t sdst = lds_addr(reinterpret_cast<int32_t*>(smem + T::SEG_OFF) + stage * KC + wave * T::SEG_KEYS);
       const u32x4 srs = buffer_rsrc(kvseg_g + key0, (uint32_t)(rows * 4));
       if (lane < T::SEG_KEYS) lds_copy4(srs, (uint32_t)((wave * T::SEG_KEYS + lane) * 4), sdst);
     }
-    if (dense && j_partial) {
+    if constexpr (dense) if (j_partial) {
       int m = scalar_load_i32(p.mask_next + mrow + j);
       m = m < 0 ? 0 : (m >= p.num_mask_blocks ? (int)p.num_mask_blocks - 1 : m);  // any content stays in the store
       const int wpr = p.block_kv / 32;
@@ -309,8 +315,18 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
       // sacc[r] is the score of key k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4
       // against query qrow.
       // Element mask, only on blocks of class 1: the band and the sequence end
-      // leave row q one run of keys [a, e] of the tile (offsets from k0),
-      // tested per score as one unsigned compare; straight-line code.
+      // leave row q one run of keys [a, e] of the tile (offsets from k0).
+      constexpr float kMasked = PW ? 0.0f : kNegInf;
+      auto band_run = [&](int& a, int& e) {
+        a = qrow + band.lo - k0;
+        e = qrow + band.hi - k0;
+        a = a > 0 ? a : 0;
+        e = e < p.kv_len - 1 - k0 ? e : p.kv_len - 1 - k0;
+        e = e < KC - 1 ? e : KC - 1;
+        if (e < a) a = e = KC;  // no key of the tile
+      };
+      // The general form: every score tested against the run (one unsigned
+      // compare), the dense-mask bit and the key's segment id; straight-line code.
       auto apply_mask = [&](auto seg_tag, auto dense_tag) {
         constexpr bool kSeg = decltype(seg_tag)::value;
         constexpr bool kDense = decltype(dense_tag)::value;
@@ -321,12 +337,8 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
         }
         // dense mask: bit 8 (r / 4) + r % 4 of this word for score r
         const uint32_t dbits = kDense ? dmw[kb] >> (4 * hh) : 0u;
-        int a = qrow + band.lo - k0;
-        int e = qrow + band.hi - k0;
-        a = a > 0 ? a : 0;
-        e = e < p.kv_len - 1 - k0 ? e : p.kv_len - 1 - k0;
-        e = e < KC - 1 ? e : KC - 1;
-        if (e < a) a = e = KC;  // no key of the tile
+        int a, e;
+        band_run(a, e);
         const uint32_t width = (uint32_t)(e - a);
         const int base = 4 * hh - a;  // offset of element r minus a, up to a constant of r
 #pragma unroll
@@ -335,18 +347,54 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
           bool ok = (uint32_t)(base + kc) <= width;
           if constexpr (kDense) ok &= (bool)((dbits >> (8 * (r >> 2) + (r & 3))) & 1u);
           if constexpr (kSeg) ok &= kseg4[r >> 2][r & 3] == myseg;
-          sacc[r] = ok ? sacc[r] : (PW ? 0.0f : kNegInf);
+          sacc[r] = ok ? sacc[r] : kMasked;
         }
       };
-      // one straight-line variant per kind of mask (dense-mask metadata is
-      // never combined with segment ids)
+      // The run alone, for a row that keeps (row_ok) or drops every key of
+      // these 32. When each row's run covers all 32 keys or none of them
+      // (the usual case away from the diagonal: a block is partial because of
+      // a document edge or a sequence end elsewhere in it), a row is kept or
+      // dropped whole with one lane mask; only otherwise is every score
+      // compared.
+      auto apply_run = [&](bool row_ok) {
+        int a, e;
+        band_run(a, e);
+        if (!row_ok) a = e = KC;
+        const bool whole = a <= 32 * kb && e >= 32 * kb + 31;
+        const bool none = a == KC || a > 32 * kb + 31 || e < 32 * kb;
+        if (__builtin_amdgcn_ballot_w64(!(whole || none)) == 0) {
+          if (__builtin_amdgcn_ballot_w64(none) != 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] = none ? kMasked : sacc[r];
+          }
+        } else {
+          const uint32_t width = (uint32_t)(e - a);
+          const int base = 4 * hh - a;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kc = 32 * kb + 8 * (r >> 2) + (r & 3);
+            sacc[r] = (uint32_t)(base + kc) <= width ? sacc[r] : kMasked;
+          }
+        }
+      };
+      // one variant per kind of mask (dense-mask metadata is never combined
+      // with segment ids)
       if (partial) {
-        if (dense)
+        if constexpr (dense) {
           apply_mask(std::false_type{}, std::true_type{});
-        else if (has_seg)
-          apply_mask(std::true_type{}, std::false_type{});
-        else
-          apply_mask(std::false_type{}, std::false_type{});
+        } else if constexpr (has_seg) {
+          // segment ids of these 32 keys, one per lane (both half-waves read
+          // the same 32): when they are all equal, a row keeps them all or
+          // none, by its own id
+          const int kid = sseg[32 * kb + l32];
+          const int id0 = __builtin_amdgcn_readfirstlane(kid);
+          if (__builtin_amdgcn_ballot_w64(kid != id0) == 0)
+            apply_run(id0 == myseg);
+          else
+            apply_mask(std::true_type{}, std::false_type{});
+        } else {
+          apply_run(true);
+        }
       }
 
       bf16x8 pb[2];  // [g]: B operand of Oᵀ += Vᵀ Pᵀ for keys 32 kb + 16 g + ...
@@ -453,7 +501,7 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
   }
 }
 
-template <int D, int NW, bool PW, typename OutT>
+template <int D, int NW, bool PW, typename OutT, int MK>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   const int64_t total = (int64_t)p.nq * p.B * p.H;
   if (total == 0) return hipSuccess;
@@ -472,23 +520,30 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
     grouped = 1;
     while (grouped < 8 && 2 * grouped <= units / 8 && 2 * grouped * kv_unit <= 16.0 * 1024 * 1024) grouped *= 2;
   }
-  hipLaunchKernelGGL((splash_fwd_bf16_kernel<D, NW, PW, OutT>), dim3((unsigned)(per_xcd * 8)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((splash_fwd_bf16_kernel<D, NW, PW, OutT, MK>), dim3((unsigned)(per_xcd * 8)), dim3(NW * 64), 0,
                      stream, p, (int)total, (int)per_xcd, grouped);
   return hipGetLastError();
 }
 
 // Each wavefront owns 32 query rows: block_q / 32 wavefronts per workgroup.
-template <int D, bool PW, typename OutT>
+template <int D, bool PW, typename OutT, int MK>
 hipError_t launch_bq(const FwdParams& p, hipStream_t stream) {
-  if (p.block_q == 64) return launch_one<D, 2, PW, OutT>(p, stream);
-  if (p.block_q == 256) return launch_one<D, 8, PW, OutT>(p, stream);
-  return launch_one<D, 4, PW, OutT>(p, stream);
+  if (p.block_q == 64) return launch_one<D, 2, PW, OutT, MK>(p, stream);
+  if (p.block_q == 256) return launch_one<D, 8, PW, OutT, MK>(p, stream);
+  return launch_one<D, 4, PW, OutT, MK>(p, stream);
+}
+
+template <int D, bool PW, typename OutT>
+hipError_t launch_mk(const FwdParams& p, hipStream_t stream) {
+  if (p.mask_blocks != nullptr) return launch_bq<D, PW, OutT, kDense>(p, stream);
+  if (p.q_seg != nullptr) return launch_bq<D, PW, OutT, kSegments>(p, stream);
+  return launch_bq<D, PW, OutT, kBandOnly>(p, stream);
 }
 
 template <bool PW, typename OutT>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-  if (p.head_dim == 64) return launch_bq<64, PW, OutT>(p, stream);
-  return launch_bq<128, PW, OutT>(p, stream);
+  if (p.head_dim == 64) return launch_mk<64, PW, OutT>(p, stream);
+  return launch_mk<128, PW, OutT>(p, stream);
 }
 
 }  // namespace
