@@ -23,6 +23,13 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
 typedef __attribute__((address_space(1))) void* global_void_ptr;
 
+// Kinds of element mask a kernel instance applies on partial blocks: the
+// head's band only, the band and segment ids, or the band and a dense mask's
+// stored bits (segment ids given with a dense mask are folded into its
+// metadata, so the kernels never see both); kAnyMask decides at run time
+// from the parameters (one instance for every kind).
+enum MaskKind { kBandOnly = 0, kSegments = 1, kDense = 2, kAnyMask = 3 };
+
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 

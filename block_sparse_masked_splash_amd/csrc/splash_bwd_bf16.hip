@@ -125,7 +125,7 @@ constexpr int dkv_waves() {
   return D == 64 ? 2 : 1;
 }
 
-template <int D, int NW, bool SM, typename OutT>
+template <int D, int NW, bool SM, typename OutT, int MK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dkv_waves<D>(), dkv_waves<D>())))
 void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_grouped) {
   using T = DkvTiling<D, NW>;
@@ -150,7 +150,7 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
 
   const int key = j * p.c_block_kv + wave * 32 + l32;
   const bool kvalid = key < p.kv_len;
-  const bool has_seg = p.q_seg != nullptr;
+  const bool has_seg = MK == kAnyMask ? p.q_seg != nullptr : MK == kSegments;
 
   // ---- this lane's key: K and V rows as B operands (head-dim 16 s + 8 hh ..) ----
   bf16x8 kreg[NS], vreg[NS];
@@ -227,7 +227,7 @@ void bwd_dkv_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int unit
     }
   };
 
-  const bool dense = p.c_mask_blocks != nullptr;
+  const bool dense = MK == kAnyMask ? p.c_mask_blocks != nullptr : MK == kDense;
   // Copy of tile (q block i, offset t): Q and dO rows, their ids and
   // statistics, and for a partial block of a dense mask the block's words of
   // these rows, stored by key word ([NW][QC]).
@@ -510,7 +510,7 @@ struct PairTiling {
   static_assert(LOADS >= 1 && SEG_ROWS >= 1, "tile too small for the workgroup");
 };
 
-template <int D, int NG, bool SM, typename OutT>
+template <int D, int NG, bool SM, typename OutT, int MK>
 __global__ __launch_bounds__(2 * NG * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_grouped) {
   using T = PairTiling<D, NG>;
@@ -543,7 +543,7 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
 
   const int key = j * p.c_block_kv + part_of_block * T::KEYS + kg * 32 + l32;
   const bool kvalid = key < p.kv_len;
-  const bool has_seg = p.q_seg != nullptr;
+  const bool has_seg = MK == kAnyMask ? p.q_seg != nullptr : MK == kSegments;
 
   // ---- this lane's key row: K (role 0) or V (role 1) as the B operand ----
   bf16x8 breg[NS];
@@ -621,7 +621,7 @@ void bwd_dkv_pair_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int
     }
   };
 
-  const bool dense = p.c_mask_blocks != nullptr;
+  const bool dense = MK == kAnyMask ? p.c_mask_blocks != nullptr : MK == kDense;
   auto issue_tile = [&](int stage, int i, int t, bool i_partial) {
     const int q0 = i * p.c_block_q + t;
     // rows past the end of the sequence or of the q block read as 0 (no contribution)
@@ -894,7 +894,7 @@ constexpr int dq_waves() {
   return D == 64 ? 3 : 2;
 }
 
-template <int D, int NW, bool SM, typename OutT>
+template <int D, int NW, bool SM, typename OutT, int MK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_waves<D>(), dq_waves<D>())))
 void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units_grouped) {
   using T = DqTiling<D, NW>;
@@ -924,7 +924,7 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
   const char* kg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh);
   const char* vg = reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh);
   const int64_t k_rs = p.k_ss * 2, v_rs = p.v_ss * 2;
-  const bool has_seg = p.q_seg != nullptr;
+  const bool has_seg = MK == kAnyMask ? p.q_seg != nullptr : MK == kSegments;
   const int32_t* kvseg_g = has_seg ? p.kv_seg + (int64_t)b * p.kv_len : nullptr;
 
   // ---- this lane's query: Q and dO rows as B operands ----
@@ -966,7 +966,7 @@ void bwd_dq_bf16_kernel(BwdParams p, int total_work, int work_per_xcd, int units
   const int8_t* bmask = p.block_mask + mrow;
   const int32_t* dnext = p.data_next + mrow;
 
-  const bool dense = p.mask_blocks != nullptr;
+  const bool dense = MK == kAnyMask ? p.mask_blocks != nullptr : MK == kDense;
   // Copy of tile (block jj, offset t): K and V rows, their segment ids, and
   // for a partial block of a dense mask the block's bits of this tile's keys.
   auto issue_tile = [&](int stage, int jj, int t, bool j_partial) {
@@ -1173,53 +1173,87 @@ Order order_for(int64_t units, int64_t per_unit, double unit_bytes) {
   return {total, (total + 7) / 8, g};
 }
 
-template <int D, int NW, bool SM, typename OutT>
+template <int D, int NW, bool SM, typename OutT, int MK>
 hipError_t launch_dkv(const BwdParams& p, hipStream_t stream) {
   // a dK/dV unit streams Q and dO of its kv_group query heads
   const Order o = order_for((int64_t)p.B * p.kv_heads, p.c_nk, 4.0 * p.q_len * p.head_dim * p.kv_group);
   if (o.total == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkv_bf16_kernel<D, NW, SM, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((bwd_dkv_bf16_kernel<D, NW, SM, OutT, MK>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
                      stream, p, (int)o.total, (int)o.per_xcd, o.grouped);
   return hipGetLastError();
 }
 
-template <int D, int NW, bool SM, typename OutT>
+template <int D, int NW, bool SM, typename OutT, int MK>
 hipError_t launch_dq(const BwdParams& p, hipStream_t stream) {
   // a dQ unit streams K and V of its K/V head
   const Order o = order_for((int64_t)p.B * p.kv_heads, (int64_t)p.nq * p.kv_group, 4.0 * p.kv_len * p.head_dim);
   if (o.total == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NW, SM, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, NW, SM, OutT, MK>), dim3((unsigned)(o.per_xcd * 8)), dim3(NW * 64), 0,
                      stream, p, (int)o.total, (int)o.per_xcd, o.grouped);
   return hipGetLastError();
 }
 
-template <int D, int NG, bool SM, typename OutT>
+template <int D, int NG, bool SM, typename OutT, int MK>
 hipError_t launch_dkv_pair(const BwdParams& p, hipStream_t stream) {
   const Order o = order_for((int64_t)p.B * p.kv_heads, (int64_t)p.c_nk * (p.c_block_kv / (32 * NG)),
                             4.0 * p.q_len * p.head_dim * p.kv_group);
   if (o.total == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkv_pair_bf16_kernel<D, NG, SM, OutT>), dim3((unsigned)(o.per_xcd * 8)), dim3(2 * NG * 64),
+  hipLaunchKernelGGL((bwd_dkv_pair_bf16_kernel<D, NG, SM, OutT, MK>), dim3((unsigned)(o.per_xcd * 8)), dim3(2 * NG * 64),
                      0, stream, p, (int)o.total, (int)o.per_xcd, o.grouped);
   return hipGetLastError();
 }
 
-template <int D, bool SM, typename OutT>
-hipError_t launch_sm(const BwdParams& p, hipStream_t stream) {
-  hipError_t e;
+// The element-mask kind of each walk's instance: its own dense-mask store,
+// else segment ids, else the band alone.
+inline int dkv_mask_kind(const BwdParams& p) {
+  return p.c_mask_blocks != nullptr ? kDense : (p.q_seg != nullptr ? kSegments : kBandOnly);
+}
+inline int dq_mask_kind(const BwdParams& p) {
+  return p.mask_blocks != nullptr ? kDense : (p.q_seg != nullptr ? kSegments : kBandOnly);
+}
+
+template <int D, bool SM, typename OutT, int MK>
+hipError_t launch_dkv_mk(const BwdParams& p, hipStream_t stream) {
   if constexpr (D == 128) {
     // paired wavefronts: K, V, dK and dV do not fit one wavefront twice per
     // SIMD. 128-key blocks: one eight-wavefront workgroup per CU (each tile
     // copy serves 128 keys, and a SIMD's two wavefronts work in step);
     // 64-key blocks: two four-wavefront workgroups per CU.
-    e = p.c_block_kv % 128 == 0 ? launch_dkv_pair<D, 4, SM, OutT>(p, stream)
-                                : launch_dkv_pair<D, 2, SM, OutT>(p, stream);
+    return p.c_block_kv % 128 == 0 ? launch_dkv_pair<D, 4, SM, OutT, MK>(p, stream)
+                                   : launch_dkv_pair<D, 2, SM, OutT, MK>(p, stream);
   } else {
-    e = p.c_block_kv == 64 ? launch_dkv<D, 2, SM, OutT>(p, stream) : launch_dkv<D, 4, SM, OutT>(p, stream);
+    return p.c_block_kv == 64 ? launch_dkv<D, 2, SM, OutT, MK>(p, stream) : launch_dkv<D, 4, SM, OutT, MK>(p, stream);
   }
-  if (e != hipSuccess) return e;
-  if (p.block_q == 64) return launch_dq<D, 2, SM, OutT>(p, stream);
-  if (p.block_q == 256) return launch_dq<D, 8, SM, OutT>(p, stream);
-  return launch_dq<D, 4, SM, OutT>(p, stream);
+}
+
+template <int D, bool SM, typename OutT, int MK>
+hipError_t launch_dq_mk(const BwdParams& p, hipStream_t stream) {
+  if (p.block_q == 64) return launch_dq<D, 2, SM, OutT, MK>(p, stream);
+  if (p.block_q == 256) return launch_dq<D, 8, SM, OutT, MK>(p, stream);
+  return launch_dq<D, 4, SM, OutT, MK>(p, stream);
+}
+
+template <int D, bool SM, typename OutT>
+hipError_t launch_sm(const BwdParams& p, hipStream_t stream) {
+  if constexpr (D == 64) {
+    // One instance for every kind of mask at D = 64: the band-only instances
+    // measured slower there (pointwise 8 x 8 x 4096 x 64: dK/dV 355 -> 369 us,
+    // dQ 266 -> 269 us), while at D = 128 they shed the scalar spills of the
+    // paired dK/dV kernel (softmax 2 x 32 x 8192 x 128: 4.05 -> 3.77 ms).
+    const hipError_t e = launch_dkv_mk<D, SM, OutT, kAnyMask>(p, stream);
+    if (e != hipSuccess) return e;
+    return launch_dq_mk<D, SM, OutT, kAnyMask>(p, stream);
+  } else {
+    const int kd = dkv_mask_kind(p);
+    const hipError_t e = kd == kDense      ? launch_dkv_mk<D, SM, OutT, kDense>(p, stream)
+                         : kd == kSegments ? launch_dkv_mk<D, SM, OutT, kSegments>(p, stream)
+                                           : launch_dkv_mk<D, SM, OutT, kBandOnly>(p, stream);
+    if (e != hipSuccess) return e;
+    const int kq = dq_mask_kind(p);
+    return kq == kDense      ? launch_dq_mk<D, SM, OutT, kDense>(p, stream)
+           : kq == kSegments ? launch_dq_mk<D, SM, OutT, kSegments>(p, stream)
+                             : launch_dq_mk<D, SM, OutT, kBandOnly>(p, stream);
+  }
 }
 
 template <int D, typename OutT>

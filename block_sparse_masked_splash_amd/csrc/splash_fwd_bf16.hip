@@ -97,12 +97,6 @@ struct Tiling {
 // at D = 64 four fit, and the extra wavefronts hide the longer vector work
 // (per key, the pointwise variant spends two transcendentals on half as many
 // matrix FLOPs).
-// Kinds of element mask a kernel instance applies on partial blocks: the
-// head's band only, the band and segment ids, or the band and a dense mask's
-// stored bits (segment ids given with a dense mask are folded into its
-// metadata, so the kernels never see both).
-enum MaskKind { kBandOnly = 0, kSegments = 1, kDense = 2 };
-
 template <int D, int NW, bool PW, typename OutT, int MK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, NW>(),
                                                                       waves_per_simd<D, NW>())))
