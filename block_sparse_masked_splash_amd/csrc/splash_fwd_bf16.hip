@@ -174,12 +174,15 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
   bf16x8 qreg[NS];
   int32_t myseg = 0;
   {
+    // rows past the end read the last row (no branch around the loads, so
+    // they all issue at once) and are then zeroed
     const bool valid = qrow < p.q_len;
+    const __bf16* qrow_ptr = qg + (int64_t)(valid ? qrow : p.q_len - 1) * p.q_ss + 8 * hh;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (valid) v = *reinterpret_cast<const i16x8*>(qg + (int64_t)qrow * p.q_ss + 16 * s + 8 * hh);
+      i16x8 v = *reinterpret_cast<const i16x8*>(qrow_ptr + 16 * s);
       if (negate_q) v ^= (short)0x8000;
+      if (!valid) v = (i16x8){0, 0, 0, 0, 0, 0, 0, 0};
       qreg[s] = __builtin_bit_cast(bf16x8, v);
     }
     if (has_seg && valid) myseg = p.q_seg[(int64_t)b * p.q_len + qrow];
@@ -232,11 +235,20 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
     }
   };
 
+  // The first non-empty kv block and its class, read ahead of the LDS set-up.
+  int cur_j = p.nk > 0 ? scalar_load_i32(dnext) : p.nk;
+  if (cur_j < 0 || cur_j > p.nk) cur_j = p.nk;
+  int cur_t = 0;
+  // class of the block being walked, read once per block (off the tile's math)
+  bool cur_partial = cur_j < p.nk && block_class(bmask, cur_j) == 1;
+
   // The tiles start zeroed, so rows that a clipped copy leaves unwritten can
   // never hold NaN bit patterns (their probabilities are 0, and 0 * NaN is NaN).
+  // (The barrier waits for the LDS stores only: the Q loads stay in flight
+  // under the first tile copy.)
   for (int o = tid * 16; o < T::SEG_OFF; o += T::NT * 16)
     *reinterpret_cast<uint4*>(smem + o) = uint4{0u, 0u, 0u, 0u};
-  __syncthreads();
+  barrier_only();
 
   f32x16 oacc[ND];
 #pragma unroll
@@ -254,11 +266,6 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
     const int jn = (j + 1 < p.nk) ? scalar_load_i32(dnext + j + 1) : p.nk;
     return (jn > j && jn <= p.nk) ? jn : p.nk;
   };
-  int cur_j = p.nk > 0 ? scalar_load_i32(dnext) : p.nk;
-  if (cur_j < 0 || cur_j > p.nk) cur_j = p.nk;
-  int cur_t = 0;
-  // class of the block being walked, read once per block (off the tile's math)
-  bool cur_partial = cur_j < p.nk && block_class(bmask, cur_j) == 1;
   if (cur_j < p.nk) issue_tile(0, cur_j, 0, cur_partial);
 
   // One tile in LDS stage STAGE (a compile-time constant, so every tile

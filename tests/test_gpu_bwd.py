@@ -190,15 +190,15 @@ def test_pointwise_bwd_full_workload_sampled(gpu_device):
     rng = np.random.default_rng(1000 + w.seed)
     got = {"dq": [], "dk": [], "dv": []}
     ref = {"dq": [], "dk": [], "dv": []}
-    for _ in range(6):
+    for _ in range(16):
         b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
         q64, k64, v64, do64 = (to64(c[n][b, h]) for n in ("q", "k", "v", "d_o"))
-        rows = sorted({0, w.S - 1, 127, 128, *map(int, rng.integers(0, w.S, 5))})
+        rows = sorted({0, w.S - 1, 127, 128, *map(int, rng.integers(0, w.S, 24))})
         m = oracle.element_mask(w.S, w.S, w.head_masks[0], rows=rows)
         a, _, _ = oracle.pointwise_attention_bwd_rows(q64[rows], k64, v64, do64[rows], w.scale, m, w.S)
         got["dq"].append(to64(dq[b, h, rows]))
         ref["dq"].append(a)
-        keys = sorted({0, w.S - 1, 128, *map(int, rng.integers(0, w.S, 5))})
+        keys = sorted({0, w.S - 1, 127, 128, *map(int, rng.integers(0, w.S, 24))})
         m = oracle.element_mask(w.S, w.S, w.head_masks[0])[:, keys]
         _, bk, bv = oracle.pointwise_attention_bwd_rows(q64, k64[keys], v64[keys], do64, w.scale, m, w.S)
         got["dk"].append(to64(dk[b, h, keys]))
@@ -289,15 +289,15 @@ def test_softmax_bwd_full_workload_sampled(gpu_device):
     rng = np.random.default_rng(2000 + w.seed)
     got = {"dq": [], "dk": [], "dv": []}
     ref = {"dq": [], "dk": [], "dv": []}
-    for _ in range(2):
+    for _ in range(3):
         b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
         q64, k64, v64, do64 = (to64(c[n][b, h]) for n in ("q", "k", "v", "d_o"))
-        rows = sorted({0, w.S - 1, 127, 128, *map(int, rng.integers(0, w.S, 5))})
+        rows = sorted({0, w.S - 1, 127, 128, *map(int, rng.integers(0, w.S, 40))})
         m = oracle.element_mask(w.S, w.S, w.head_masks[0], rows=rows)
         a, _, _ = oracle.softmax_attention_bwd_rows(q64[rows], k64, v64, do64[rows], w.scale, m)
         got["dq"].append(to64(dq[b, h, rows]))
         ref["dq"].append(a)
-        keys = sorted({0, w.S - 1, 128, *map(int, rng.integers(0, w.S, 5))})
+        keys = sorted({0, w.S - 1, 127, 128, *map(int, rng.integers(0, w.S, 40))})
         dk_ref = np.zeros((len(keys), w.D))
         dv_ref = np.zeros((len(keys), w.D))
         for r0 in range(0, w.S, 1024):

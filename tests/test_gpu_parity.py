@@ -212,8 +212,12 @@ def test_full_workload_sampled_rows(gpu_device, name):
     torch.cuda.synchronize()
     rng = np.random.default_rng(1000 + w.seed)
     qs = _seg_np(c["q_segment_ids"])
-    extra = [w.block_q - 1, w.block_q, w.S // 2]
-    rows = sample_rows(rng, w.B, w.H, w.S, 60, extra)
+    # rows at query-block edges (where a block's diagonal kv block starts and
+    # ends) and at the sequence ends, besides 400 random rows
+    edges = [0, 1, w.block_q - 1, w.block_q, w.block_q + 1, w.S // 2 - 1, w.S // 2, w.S - 2, w.S - 1]
+    for i in rng.integers(1, w.S // w.block_q, size=8):
+        edges += [int(i) * w.block_q - 1, int(i) * w.block_q]
+    rows = sample_rows(rng, w.B, w.H, w.S, 400, sorted(set(edges)))
     if qs is not None:
         # document edges: in every batch row, the first token of each document
         # (it attends to itself alone), the token before it (the end of the
