@@ -269,10 +269,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # untimed warm-up steps: after the GPU has been idle, the first ~25 calls
-    # run about 5% slower while the clock settles; 30 steps reach the steady
-    # state (measured at c3h: 5 -> 1.123 ms per call, 30 -> 1.067, 100 -> 1.070)
-    ap.add_argument("--warmup", type=int, default=30)
+    # untimed warm-up steps: after the GPU has been idle its clock control
+    # overshoots for about fifteen calls (B=2 H=32 S=8192 D=128: 1.04 -> 1.40
+    # -> 1.04 ms per call); 100 steps also cover the shorter workloads, whose
+    # calls are ten times shorter
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c3h")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -347,16 +348,18 @@ def main():
         build_metadata()
         run_kernels()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    # no garbage-collection pass inside the timed steps (a full pass over the
-    # objects the setup left behind can stall one step's launches for tens of ms)
+    # No garbage-collection pass inside the timed steps (a full pass over the
+    # objects the setup left behind can stall one step's launches for tens of
+    # ms), and none between the warm-up and the timed steps either: after tens
+    # of ms of idle the GPU's clock control overshoots for about fifteen
+    # launches (kernel traces: 1.04 -> 1.40 -> 1.04 ms per call at B=2 H=32
+    # S=8192 D=128), so the warm-up runs straight into the timed steps.
     gc.collect()
     gc.disable()
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
