@@ -39,7 +39,7 @@ BWD_METRIC = "splash bwd TFLOP/s (unmasked FLOPs, 5 products per block) + % bf16
 # the sources each direction's kernels are built from: a counter summary stays
 # valid while these are unchanged
 KERNEL_SOURCES = {
-    False: ["splash_fwd_bf16.hip", "splash_fwd_f32.hip", "cdna4.h", "internal.h"],
+    False: ["splash_fwd_bf16.hip", "splash_fwd_rows64.hip", "splash_fwd_f32.hip", "cdna4.h", "internal.h"],
     True: ["splash_bwd_bf16.hip", "splash_bwd_f32.hip", "softmax_delta.hip", "cdna4.h", "internal.h"],
 }
 

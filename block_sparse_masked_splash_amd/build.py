@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsplash.so")
-SOURCES = ["api.cpp", "dense_mask.cpp", "mask_info.hip", "splash_fwd_bf16.hip", "splash_fwd_f32.hip",
+SOURCES = ["api.cpp", "dense_mask.cpp", "mask_info.hip", "splash_fwd_bf16.hip", "splash_fwd_rows64.hip", "splash_fwd_f32.hip",
            "splash_bwd_bf16.hip", "splash_bwd_f32.hip", "softmax_delta.hip"]
 ARCH = "gfx950"
 

@@ -144,6 +144,10 @@ hipError_t launch_mask_info(const MaskInfoParams& p, hipStream_t stream);
 hipError_t launch_mask_info_dkv(const MaskInfoParams& p, hipStream_t stream);
 // bf16 inputs, matrix-core path. out_f32 selects an fp32 output.
 hipError_t launch_fwd_bf16(const FwdParams& p, bool pointwise, bool out_f32, hipStream_t stream);
+// The softmax forward at head_dim 128 with 64 query rows per wavefront
+// (block_q 128 or 256, no dense-mask store): whether it applies, and its launch.
+bool fwd_rows64_applies(const FwdParams& p, bool pointwise);
+hipError_t launch_fwd_rows64(const FwdParams& p, bool out_f32, hipStream_t stream);
 // fp32 inputs and output.
 hipError_t launch_fwd_f32(const FwdParams& p, bool pointwise, hipStream_t stream);
 // Pointwise backward, bf16 inputs (gradients bf16 or fp32) and fp32 inputs.

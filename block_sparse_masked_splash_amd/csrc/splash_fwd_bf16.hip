@@ -550,6 +550,7 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, bool pointwise, bool out_f32, hipStream_t stream) {
+  if (fwd_rows64_applies(p, pointwise)) return launch_fwd_rows64(p, out_f32, stream);
   if (pointwise) {
     return out_f32 ? launch_d<true, float>(p, stream) : launch_d<true, __bf16>(p, stream);
   }

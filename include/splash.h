@@ -28,6 +28,13 @@
  *   - Positions: query q in [0, q_len), key k in [0, kv_len). Lengths need not
  *     be multiples of the block sizes: the last block of each axis is ragged
  *     and positions past the end are masked out.
+ *   - Kernel choice: the softmax forwards at head_dim 128 with a band-only
+ *     mask (no segment ids, no dense-mask store) and block_q 128 or 256 run a
+ *     kernel with 64 query rows per wavefront when the problem has at least
+ *     2048 of its 256-row workgroups, else the one-block kernel. The
+ *     environment variable SPLASH_FWD_ROWS64=1 (or 0), read at each call,
+ *     selects that kernel (or the other) whenever it applies. Both compute the
+ *     same function with the same arithmetic per row.
  */
 #ifndef SPLASH_H_
 #define SPLASH_H_
