@@ -108,3 +108,61 @@ def test_rows64_choice_by_size_gives_the_same_result(gpu_device, monkeypatch):
     monkeypatch.setenv("SPLASH_FWD_ROWS64", "1")
     out64, _ = _run(gpu_device, c, [CAUSAL], 128, 128, "bf16", "bhsd", H, S, S)
     assert torch.equal(out_default, out64)
+
+
+def _nan_padded(t, layout, dev, pad=96):
+    """``t`` ([B, H, S, D], CPU) at the start of a NaN-filled buffer with
+    ``pad`` more rows per sequence, as a view in ``layout``."""
+    B, H, S, D = t.shape
+    if layout == "bhsd":
+        buf = torch.full((B, H, S + pad, D), float("nan"), dtype=t.dtype, device=dev)
+        buf[:, :, :S] = t.to(dev)
+        return buf[:, :, :S]
+    buf = torch.full((B, S + pad, H, D), float("nan"), dtype=t.dtype, device=dev)
+    buf[:, :S] = t.transpose(1, 2).to(dev)
+    return buf[:, :S]
+
+
+@pytest.mark.parametrize("case", [
+    # B, H, kv_heads, Sq, Skv, heads, bq, bkv, layout
+    (2, 2, 2, 333, 290, [CAUSAL, FULL], 128, 128, "bhsd"),
+    (1, 4, 2, 301, 259, [FULL, CAUSAL, wl.local_causal(40), (0, 30, 60)], 256, 128, "bshd"),
+    (1, 2, 1, 270, 301, [FULL, CAUSAL], 128, 64, "bshd"),
+], ids=["n0", "n1", "n2"])
+def test_rows64_ignores_rows_past_the_end(gpu_device, monkeypatch, case):
+    """Ragged ends with NaN in every row past each sequence end (views into
+    larger buffers): a tile row read past the end would reach the output as
+    NaN through a zero weight."""
+    B, H, Hk, Sq, Skv, heads, bq, bkv, layout = case
+    D = 128
+    print(f"rows64 tail case {case}", flush=True)
+    c = wl.random_case(47, B, H, Sq, Skv, D, "bf16")
+    kv = wl.random_case(53, B, Hk, Sq, Skv, D, "bf16")
+    q, k, v = _nan_padded(c["q"], layout, gpu_device), _nan_padded(kv["k"], layout, gpu_device), \
+        _nan_padded(kv["v"], layout, gpu_device)
+    info = sp.mask_info_build(B, H, Sq, Skv, heads, bq, bkv, device=gpu_device)
+    monkeypatch.setenv("SPLASH_FWD_ROWS64", "1")
+    out, lse = sp.splash_fwd_lse(q, k, v, info, layout=layout)
+    torch.cuda.synchronize()
+    out = out if layout == "bhsd" else out.transpose(1, 2)
+    assert torch.isfinite(out.float()).all()
+    ref = oracle.softmax_attention(to64(c["q"]), to64(kv["k"]), to64(kv["v"]), 1 / math.sqrt(D), heads)
+    check_close(to64(out.cpu()), ref, "bf16", f"{case}")
+
+
+def test_rows64_no_keys_and_no_queries(gpu_device, monkeypatch):
+    """No keys: every row is empty, written as 0 with log-sum-exp -inf; no
+    query rows: nothing is launched."""
+    D = 128
+    monkeypatch.setenv("SPLASH_FWD_ROWS64", "1")
+    q = torch.randn(1, 2, 300, D, device=gpu_device).to(torch.bfloat16)
+    kv = torch.zeros(1, 2, 0, D, dtype=torch.bfloat16, device=gpu_device)
+    info = sp.mask_info_build(1, 2, 300, 0, [FULL, CAUSAL], 128, 128, device=gpu_device)
+    out = torch.full((1, 2, 300, D), 7.0, dtype=torch.bfloat16, device=gpu_device)
+    _, lse = sp.splash_fwd_lse(q, kv, kv, info, out=out)
+    torch.cuda.synchronize()
+    assert (out == 0).all()
+    assert torch.isneginf(lse).all()
+    q0 = torch.zeros(1, 2, 0, D, dtype=torch.bfloat16, device=gpu_device)
+    info0 = sp.mask_info_build(1, 2, 0, 0, [CAUSAL], 128, 128, device=gpu_device)
+    assert sp.splash_fwd(q0, q0, q0, info0).shape == (1, 2, 0, D)
