@@ -303,6 +303,36 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
     // The tile is processed in parts of 32 keys (kb), each: Sᵀ, softmax, Oᵀ += Vᵀ Pᵀ.
 #pragma unroll
     for (int kb = 0; kb < KC / 32; ++kb) {
+      // Element mask, only on blocks of class 1: the band and the sequence end
+      // leave row q one run of keys [a, e] of the tile (offsets from k0).
+      constexpr float kMasked = PW ? 0.0f : kNegInf;
+      auto band_run = [&](int& a, int& e) {
+        a = qrow + band.lo - k0;
+        e = qrow + band.hi - k0;
+        a = a > 0 ? a : 0;
+        e = e < p.kv_len - 1 - k0 ? e : p.kv_len - 1 - k0;
+        e = e < KC - 1 ? e : KC - 1;
+        if (e < a) a = e = KC;  // no key of the tile
+      };
+      // A part of 32 keys that no row of the wavefront may see (past the
+      // band, or all of one document none of its rows belongs to) adds
+      // nothing to O or L, so its products and probabilities are skipped
+      // (exactly: a masked score's probability is 0).
+      if (!dense && partial) {
+        int a, e;
+        band_run(a, e);
+        bool none = a == KC || a > 32 * kb + 31 || e < 32 * kb;
+        if constexpr (has_seg) {
+          // (the lane-crossing reads are made by every lane, outside any
+          // condition: each lane carries one key's id)
+          const int kid = sseg[32 * kb + l32];
+          const int id0 = __builtin_amdgcn_readfirstlane(kid);
+          const bool one_id = __builtin_amdgcn_ballot_w64(kid != id0) == 0;
+          none = none || (one_id && id0 != myseg);
+        }
+        if (__builtin_amdgcn_ballot_w64(!none) == 0) continue;
+      }
+
       // ---- Sᵀ = K Qᵀ: 32 keys x 32 queries ----
       f32x16 sacc;
 #pragma unroll
@@ -315,17 +345,6 @@ void splash_fwd_bf16_kernel(FwdParams p, int total_work, int work_per_xcd, int u
 
       // sacc[r] is the score of key k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4
       // against query qrow.
-      // Element mask, only on blocks of class 1: the band and the sequence end
-      // leave row q one run of keys [a, e] of the tile (offsets from k0).
-      constexpr float kMasked = PW ? 0.0f : kNegInf;
-      auto band_run = [&](int& a, int& e) {
-        a = qrow + band.lo - k0;
-        e = qrow + band.hi - k0;
-        a = a > 0 ? a : 0;
-        e = e < p.kv_len - 1 - k0 ? e : p.kv_len - 1 - k0;
-        e = e < KC - 1 ? e : KC - 1;
-        if (e < a) a = e = KC;  // no key of the tile
-      };
       // The general form: every score tested against the run (one unsigned
       // compare), the dense-mask bit and the key's segment id; straight-line code.
       auto apply_mask = [&](auto seg_tag, auto dense_tag) {
