@@ -179,3 +179,33 @@ def test_random_dense_mask_forward_matches_oracle(gpu_device, seed):
     ofn = oracle.pointwise_attention if pointwise else oracle.softmax_attention
     ref = ofn(to64(c["q"]), to64(kv["k"]), to64(kv["v"]), 1 / math.sqrt(D), heads, dense=dense)
     print(check_close(to64(out), ref, dt, f"fuzz dense {seed}"))
+
+
+N_ROWS64 = 16
+
+
+@pytest.mark.parametrize("seed", range(N_ROWS64))
+def test_random_rows64_forward_matches_one_block_and_oracle(gpu_device, monkeypatch, seed):
+    """The 64-rows-per-wavefront softmax forward (forced on for these small
+    cases) over random shapes, band masks, head counts, block sizes, output
+    dtypes and layouts: bit-equal to the one-block kernel (outputs and
+    log-sum-exp) and within the bf16 bound of the oracle."""
+    c = _draw(3000 + seed, backward=False)
+    rng = np.random.default_rng(7000 + seed)
+    c.update(D=128, seg=None, dt="bf16", bq=int(rng.choice([128, 256])))
+    out_dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+    print(f"fuzz rows64 seed {seed}: {c} out={out_dtype}", flush=True)
+    g = _inputs(17 * seed + 3, c, 1.0)
+    d = _dev(g, gpu_device)
+    info = sp.mask_info_build(c["B"], c["H"], c["Sq"], c["Skv"], c["heads"], c["bq"], c["bkv"], device=gpu_device)
+    q, k, v = (_to_layout(d[n], c["layout"]) for n in ("q", "k", "v"))
+    res = {}
+    for force in ("1", "0"):
+        monkeypatch.setenv("SPLASH_FWD_ROWS64", force)
+        out, lse = sp.splash_fwd_lse(q, k, v, info, layout=c["layout"], out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        res[force] = (_from_layout(out, c["layout"]).cpu(), lse.cpu())
+    assert torch.equal(res["1"][0], res["0"][0])
+    assert torch.equal(res["1"][1], res["0"][1])
+    ref = oracle.softmax_attention(to64(g["q"]), to64(g["k"]), to64(g["v"]), 1 / math.sqrt(c["D"]), c["heads"])
+    print(check_close(to64(res["1"][0]), ref, "bf16", f"fuzz rows64 {seed}"))
