@@ -159,22 +159,33 @@ __global__ __launch_bounds__(BKV*(D / 32)) void bwd_dkv_f32_kernel(BwdParams p) 
   }
 }
 
+// Rows of a q block per dQ workgroup: all of them, up to 512 threads (a q
+// block of 256 rows at D = 128 takes two workgroups: 1024 threads would
+// leave 128 registers per lane and spill).
+template <int D, int BQ>
+constexpr int dq_f32_rows() {
+  return BQ * (D / 32) > 512 ? 512 / (D / 32) : BQ;
+}
+
 template <int D, int BQ, bool SM>
-__global__ __launch_bounds__(BQ*(D / 32)) void bwd_dq_f32_kernel(BwdParams p) {
+__global__ __launch_bounds__((dq_f32_rows<D, BQ>() * (D / 32))) void bwd_dq_f32_kernel(BwdParams p) {
   constexpr int G = D / 32;
-  constexpr int NT = BQ * G;
+  constexpr int ROWS = dq_f32_rows<D, BQ>();
+  constexpr int SUB = BQ / ROWS;  // workgroups per q block
+  constexpr int NT = ROWS * G;
   constexpr int STRIDE = D + 4;
   __shared__ __attribute__((aligned(16))) float sK[TT * STRIDE];
   __shared__ __attribute__((aligned(16))) float sV[TT * STRIDE];
   __shared__ int32_t sKseg[TT];
 
   const int tid = threadIdx.x;
-  const int rl = tid / G;
   const int part = tid % G;
   const int BH = p.B * p.H;
   const int64_t lin = blockIdx.x;
   const int bh = (int)(lin % BH);
-  const int i = p.nq - 1 - (int)(lin / BH);
+  const int64_t rest = lin / BH;
+  const int i = p.nq - 1 - (int)(rest / SUB);
+  const int rl = tid / G + (int)(rest % SUB) * ROWS;  // row within the q block
   const int b = bh / p.H;
   const int h = bh % p.H;
   const int hk = h / p.kv_group;
@@ -283,9 +294,10 @@ hipError_t launch_dkv_f32(const BwdParams& p, hipStream_t stream) {
 
 template <int D, int BQ, bool SM>
 hipError_t launch_dq_f32(const BwdParams& p, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.nq * p.B * p.H;
+  constexpr int ROWS = dq_f32_rows<D, BQ>();
+  const int64_t grid = (int64_t)p.nq * p.B * p.H * (BQ / ROWS);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, BQ, SM>), dim3((unsigned)grid), dim3(BQ * (D / 32)), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, BQ, SM>), dim3((unsigned)grid), dim3(ROWS * (D / 32)), 0, stream, p);
   return hipGetLastError();
 }
 

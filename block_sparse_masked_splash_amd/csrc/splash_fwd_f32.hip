@@ -25,23 +25,35 @@ __device__ inline float group_sum(float x) {
   return x;
 }
 
+// Rows of a q block per workgroup: all of them, up to 512 threads (a q block
+// of 256 rows at D = 128 takes two workgroups: 1024 threads would leave 128
+// registers per lane and spill).
+template <int D, int BQ>
+constexpr int f32_rows() {
+  return BQ * (D / 32) > 512 ? 512 / (D / 32) : BQ;
+}
+
 template <int D, int BQ, bool PW>
-__global__ __launch_bounds__(BQ*(D / 32)) void splash_fwd_f32_kernel(FwdParams p) {
+__global__ __launch_bounds__((f32_rows<D, BQ>() * (D / 32))) void splash_fwd_f32_kernel(FwdParams p) {
   constexpr int G = D / 32;
-  constexpr int NT = BQ * G;
+  constexpr int ROWS = f32_rows<D, BQ>();
+  constexpr int SUB = BQ / ROWS;  // workgroups per q block
+  constexpr int NT = ROWS * G;
   constexpr int STRIDE = D + 4;
   __shared__ __attribute__((aligned(16))) float sK[KT * STRIDE];
   __shared__ __attribute__((aligned(16))) float sV[KT * STRIDE];
   __shared__ int32_t sKseg[KT];
 
   const int tid = threadIdx.x;
-  const int rl = tid / G;
+  const int rl0 = tid / G;
   const int part = tid % G;
 
   const int BH = p.B * p.H;
   const int64_t lin = blockIdx.x;
   const int bh = (int)(lin % BH);
-  const int i = p.nq - 1 - (int)(lin / BH);
+  const int64_t rest = lin / BH;
+  const int i = p.nq - 1 - (int)(rest / SUB);
+  const int rl = rl0 + (int)(rest % SUB) * ROWS;  // row within the q block
   const int b = bh / p.H;
   const int h = bh % p.H;
   const int hm = p.meta_heads == 1 ? 0 : h;
@@ -88,17 +100,26 @@ __global__ __launch_bounds__(BQ*(D / 32)) void splash_fwd_f32_kernel(FwdParams p
       const int k0 = j * p.block_kv + t;
       if (k0 >= p.kv_len) break;
       __syncthreads();
-      for (int c = tid; c < KT * (D / 4); c += NT) {
-        const int r = c / (D / 4);
-        const int cc = c % (D / 4);
-        const int kv = k0 + r;
-        float4 kval = {0.f, 0.f, 0.f, 0.f}, vval = {0.f, 0.f, 0.f, 0.f};
+      // the tile's K and V rows: every load of the thread is issued before
+      // the first LDS store, so their latencies overlap
+      constexpr int PER = KT * (D / 4) / NT;  // float4 of K (and of V) per thread
+      static_assert(PER * NT == KT * (D / 4), "tile not divisible over the threads");
+      float4 kval[PER], vval[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int c = tid + u * NT;
+        const int kv = k0 + c / (D / 4);
+        kval[u] = vval[u] = float4{0.f, 0.f, 0.f, 0.f};
         if (kv < p.kv_len) {
-          kval = *reinterpret_cast<const float4*>(kg + (int64_t)kv * p.k_ss + cc * 4);
-          vval = *reinterpret_cast<const float4*>(vg + (int64_t)kv * p.v_ss + cc * 4);
+          kval[u] = *reinterpret_cast<const float4*>(kg + (int64_t)kv * p.k_ss + (c % (D / 4)) * 4);
+          vval[u] = *reinterpret_cast<const float4*>(vg + (int64_t)kv * p.v_ss + (c % (D / 4)) * 4);
         }
-        *reinterpret_cast<float4*>(&sK[r * STRIDE + cc * 4]) = kval;
-        *reinterpret_cast<float4*>(&sV[r * STRIDE + cc * 4]) = vval;
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int c = tid + u * NT;
+        *reinterpret_cast<float4*>(&sK[(c / (D / 4)) * STRIDE + (c % (D / 4)) * 4]) = kval[u];
+        *reinterpret_cast<float4*>(&sV[(c / (D / 4)) * STRIDE + (c % (D / 4)) * 4]) = vval[u];
       }
       if (partial && has_seg && tid < KT) {
         const int kv = k0 + tid;
@@ -112,32 +133,37 @@ __global__ __launch_bounds__(BQ*(D / 32)) void splash_fwd_f32_kernel(FwdParams p
         for (int d = 0; d < 32; ++d) acc = fmaf(qv[d], sK[kk * STRIDE + part * 32 + d], acc);
         s[kk] = group_sum<G>(acc) * p.scale;
       }
-      bool ok[KT];
-      for (int kk = 0; kk < KT; ++kk) {
-        ok[kk] = true;
-        if (partial) {
-          const int kv = k0 + kk;
-          const int dlt = kv - qrow;
-          ok[kk] = kv < p.kv_len && dlt >= band.lo && dlt <= band.hi && (!has_seg || sKseg[kk] == my_qseg);
-          if (drow != nullptr) ok[kk] = ok[kk] && ((drow[(t + kk) >> 5] >> ((t + kk) & 31)) & 1u);
-        }
-      }
+      // whether this row may see key k0 + kk (every key of a full block)
+      auto allowed = [&](int kk) -> bool {
+        if (!partial) return true;
+        const int kv = k0 + kk;
+        const int dlt = kv - qrow;
+        bool ok = kv < p.kv_len && dlt >= band.lo && dlt <= band.hi && (!has_seg || sKseg[kk] == my_qseg);
+        if (drow != nullptr) ok = ok && ((drow[(t + kk) >> 5] >> ((t + kk) & 31)) & 1u);
+        return ok;
+      };
       if constexpr (PW) {
+#pragma unroll
         for (int kk = 0; kk < KT; ++kk) {
-          const float pr = ok[kk] ? s[kk] / (1.0f + expf(-s[kk])) * p.inv_q_len : 0.0f;
+          // (a key a row may not see is passed over, as in the softmax below;
+          // the branch also keeps the compiler from loading the V rows of
+          // many keys ahead, which ran it out of registers)
+          if (!allowed(kk)) continue;
+          // silu(s) / q_len; the reciprocal instruction is within 1 ulp
+          const float pr = s[kk] * __builtin_amdgcn_rcpf(1.0f + expf(-s[kk])) * p.inv_q_len;
           for (int d = 0; d < 32; ++d) o[d] = fmaf(pr, sV[kk * STRIDE + part * 32 + d], o[d]);
         }
       } else {
         float mx = kNegInf;
         for (int kk = 0; kk < KT; ++kk)
-          if (ok[kk]) mx = fmaxf(mx, s[kk]);
+          if (allowed(kk)) mx = fmaxf(mx, s[kk]);
         const float m_new = fmaxf(m_run, mx);
         if (m_new != kNegInf) {
           const float alpha = expf(m_run - m_new);
           l_run *= alpha;
           for (int d = 0; d < 32; ++d) o[d] *= alpha;
           for (int kk = 0; kk < KT; ++kk) {
-            if (!ok[kk]) continue;
+            if (!allowed(kk)) continue;
             const float e = expf(s[kk] - m_new);
             l_run += e;
             for (int d = 0; d < 32; ++d) o[d] = fmaf(e, sV[kk * STRIDE + part * 32 + d], o[d]);
@@ -164,9 +190,10 @@ __global__ __launch_bounds__(BQ*(D / 32)) void splash_fwd_f32_kernel(FwdParams p
 
 template <int D, int BQ, bool PW>
 hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.nq * p.B * p.H;
+  constexpr int ROWS = f32_rows<D, BQ>();
+  const int64_t grid = (int64_t)p.nq * p.B * p.H * (BQ / ROWS);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((splash_fwd_f32_kernel<D, BQ, PW>), dim3((unsigned)grid), dim3(BQ * (D / 32)), 0,
+  hipLaunchKernelGGL((splash_fwd_f32_kernel<D, BQ, PW>), dim3((unsigned)grid), dim3(ROWS * (D / 32)), 0,
                      stream, p);
   return hipGetLastError();
 }

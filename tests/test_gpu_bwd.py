@@ -86,6 +86,8 @@ BWD_CASES = [
     (1, 2, 2, 200, 200, 64, [CAUSAL], (64, 64), (64, 64), "docs", "f32", "f32", "bhsd"),
     (1, 2, 1, 130, 190, 128, [CAUSAL, (0, 20, 20)], (128, 128), (64, 64), "random", "f32", "f32", "bhsd"),
     (1, 1, 1, 300, 300, 64, [FULL], (256, 128), (128, 64), None, "f32", "f32", "bhsd"),
+    # fp32 at D = 128 with 256-row q blocks: each q block takes two dQ workgroups
+    (1, 2, 1, 300, 270, 128, [CAUSAL, wl.local_causal(90)], (256, 64), (64, 128), "docs", "f32", "f32", "bshd"),
     (1, 2, 2, 300, 300, 128, [CAUSAL, FULL], (64, 64), (32, 128), "docs", "bf16", "bf16", "bhsd"),
     # units a multiple of 8 (three or five per XCD): both passes deal them in
     # groups of 2 or 4 with a smaller last group
@@ -222,6 +224,7 @@ SM_CASES = [
     (1, 4, 1, 517, 517, 64, [CAUSAL], (256, 64), (256, 128), "docs", "bf16", "bf16", "bshd"),
     (1, 2, 2, 200, 200, 64, [CAUSAL], (64, 64), (64, 64), "docs", "f32", "f32", "bhsd"),
     (1, 2, 1, 130, 190, 128, [CAUSAL, (0, 20, 20)], (128, 128), (64, 64), "random", "f32", "f32", "bhsd"),
+    (1, 2, 2, 300, 300, 128, [FULL, CAUSAL], (256, 128), (128, 64), "random", "f32", "f32", "bhsd"),
     (1, 2, 2, 250, 250, 128, [CAUSAL, wl.local_causal(60)], (64, 64), (96, 64), "docs", "bf16", "bf16", "bhsd"),
     (1, 48, 24, 130, 200, 128, [CAUSAL], (128, 128), (128, 128), None, "bf16", "bf16", "bhsd"),
 ]

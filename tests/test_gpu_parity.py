@@ -143,6 +143,9 @@ FWD_CASES = [
     (2, 2, 600, 600, 128, [CAUSAL, wl.local_causal(100)], 256, 128, "docs", "bf16"),
     (1, 2, 300, 333, 64, [FULL, CAUSAL], 256, 64, None, "bf16"),
     (1, 2, 280, 280, 64, [CAUSAL, (0, 50, 20)], 256, 64, "random", "f32"),
+    # fp32 at D = 128 with 256-row q blocks: each q block takes two workgroups
+    (2, 2, 300, 270, 128, [CAUSAL, wl.local_causal(90)], 256, 64, "docs", "f32"),
+    (1, 2, 517, 517, 128, [FULL, CAUSAL], 256, 128, None, "f32"),
 ]
 
 
