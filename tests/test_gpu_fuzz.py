@@ -21,8 +21,8 @@ from parity_util import check_close, check_close_grad, to64
 
 pytestmark = pytest.mark.gpu
 
-N_FWD = 24
-N_BWD = 10
+N_FWD = 64
+N_BWD = 24
 
 
 def _head_mask(rng):
@@ -135,7 +135,7 @@ def test_random_backward_matches_oracle(gpu_device, seed):
         print(name, check_close_grad(to64(got), want, f"fuzz backward {seed} {name}"))
 
 
-N_DENSE = 8
+N_DENSE = 16
 
 
 @pytest.mark.parametrize("seed", range(N_DENSE))
@@ -181,7 +181,7 @@ def test_random_dense_mask_forward_matches_oracle(gpu_device, seed):
     print(check_close(to64(out), ref, dt, f"fuzz dense {seed}"))
 
 
-N_ROWS64 = 16
+N_ROWS64 = 32
 
 
 @pytest.mark.parametrize("seed", range(N_ROWS64))
