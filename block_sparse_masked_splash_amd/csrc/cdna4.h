@@ -61,7 +61,12 @@ __device__ inline void wait_vmcnt() {
 // part of a lane's offset travels in voff and the SGPR offset is 0. Issued
 // through asm so that the compiler does not treat the tile being filled as a
 // pending write to every LDS read that follows; completion is awaited
-// explicitly with wait_vmcnt.
+// explicitly with wait_vmcnt. The copies set m0 (the LDS destination) and
+// name it as clobbered; the compiler warns that it does not preserve a
+// reserved register across such a statement. That is safe here because
+// nothing of the compiler's lives in m0 in these kernels: on this target LDS
+// instructions do not read it, and the kernels use none of the instructions
+// that do (no builtin LDS-direct loads, no indexed register moves, no GWS).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // 32-bit data format, no swizzle, no stride
 

@@ -119,7 +119,8 @@ struct DkvTiling {
 
 // D = 64: about 170 VGPRs, two wavefronts per SIMD. D = 128: K, V and the
 // two accumulators alone take 192 VGPRs, and the whole step about 270, more
-// than two wavefronts per SIMD can hold without spilling: one.
+// than two wavefronts per SIMD can hold without spilling, so D = 128 runs the
+// paired kernel below instead (the value here only keeps the template whole).
 template <int D>
 constexpr int dkv_waves() {
   return D == 64 ? 2 : 1;
