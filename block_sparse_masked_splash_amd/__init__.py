@@ -2,7 +2,8 @@
 
 The computation lives in libsplash.so (hand-written HIP kernels behind a C
 ABI, declared in include/splash.h); ``binding`` marshals torch tensors into
-it. ``workloads`` holds the seeded synthetic inputs.
+it, and ``autograd`` chains the forward and backward calls into one
+differentiable function. ``workloads`` holds the seeded synthetic inputs.
 """
 
 from .binding import (  # noqa: F401
@@ -20,4 +21,5 @@ from .binding import (  # noqa: F401
     splash_fwd,
     splash_fwd_lse,
 )
+from .autograd import splash_attention  # noqa: F401
 from .workloads import CAUSAL, FULL, local_causal  # noqa: F401
